@@ -1,0 +1,226 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused MoE layer forward pass on one MI355X.
+
+One step = the whole hot path on one batch of resident synthetic input:
+gate scores (GEMM) -> softmax top-k -> moe_align_block_size -> up/gate GEMM
+with SwiGLU -> down GEMM with the router-weighted combine -> output cast,
+all enqueued on one stream through the C ABI.
+
+Default workload: the balanced prefill layer (S=16384 tokens, H=2048,
+D=2048, E=64 experts, top-2, capacity factor 1.0, bf16 with fp32
+accumulation), seeded synthetic inputs.
+
+Prints one JSON line: whole-job tokens/s, the roofline of the dominant kernel
+(the up/gate grouped GEMM, timed live with HIP events on its stream) and the
+CPU oracle's tokens/s on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_F32_TFLOPS = 157.3     # MI355X fp32 (MFMA / vector)
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=32)
+    ap.add_argument("--warmup", type=int, default=32)
+    ap.add_argument("--workload", default="prefill_bal")
+    ap.add_argument("--block-size", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="target CPU work of the oracle baseline sample")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run only a plain 1 GiB device copy (HBM counter calibration)")
+    return ap.parse_args()
+
+
+def layer_counts(wl, counts_e, bm):
+    """Algorithmic flops and bytes of one layer pass given the kept per-expert
+    counts (routing-dependent)."""
+    kept = int(counts_e.sum())
+    touched = int((counts_e > 0).sum())
+    b = wl.elem_bytes
+    f_gate = 2.0 * wl.S * wl.H * wl.E
+    f_up = 4.0 * wl.H * wl.D * kept + 4.0 * wl.H * wl.D_shared * wl.S
+    f_down = 2.0 * wl.D * wl.H * kept + 2.0 * wl.D_shared * wl.H * wl.S
+    w_expert = 3.0 * wl.H * wl.D * b
+    bytes_w = touched * w_expert + 3.0 * wl.H * wl.D_shared * b
+    bytes_up = touched * 2.0 * wl.H * wl.D * b + 2.0 * wl.H * wl.D_shared * b + wl.S * wl.H * b
+    bytes_io = 2.0 * wl.S * wl.H * b + wl.H * wl.E * b
+    return {"kept": kept, "touched": touched, "flops_gate": f_gate, "flops_up": f_up,
+            "flops_down": f_down, "flops": f_gate + f_up + f_down,
+            "bytes": bytes_w + bytes_io, "bytes_up": bytes_up}
+
+
+def copy_calibration():
+    import torch
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device="cuda")
+    b = torch.empty(n, dtype=torch.uint8, device="cuda")
+    a.fill_(1)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": n, "copies": 3}))
+
+
+def cpu_baseline(wl, target_s):
+    """The oracle as it stands, on a bounded sample of the same workload
+    (first S' tokens' worth: the same layer at S' tokens), whole layer."""
+    import oracle
+    from sparse_expert_ffn_amd import workloads as wk
+    orc = oracle.default()
+
+    def one(S):
+        w = wl.with_tokens(S)
+        li = wk.draw_layer(w)
+        t0 = time.perf_counter()
+        orc.layer(li.A, li.Wr, li.bias, li.W_up, li.W_gate, li.W_down, w.k,
+                  renormalize=w.renormalize, capacity=w.capacity, Ws_up=li.Ws_up,
+                  Ws_gate=li.Ws_gate, Ws_down=li.Ws_down)
+        return time.perf_counter() - t0
+
+    S0 = min(wl.S, 64)
+    t0 = one(S0)
+    S1 = int(min(wl.S, max(S0, S0 * target_s / max(t0, 1e-3))))
+    t1 = one(S1) if S1 != S0 else t0
+    return {"value": S1 / t1, "unit": "tokens/s", "cores": orc.num_threads(), "kind": "oracle",
+            "sample": f"{wl.name} layer at S={S1} tokens (same H, D, E, k, distributions; "
+                      f"capacity recomputed for S), gate+top-k+capacity+experts+combine, "
+                      f"{t1:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the multi-GPU expert-parallel path is not built)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if args.copy_calibration:
+        copy_calibration()
+        return
+
+    import sparse_expert_ffn_amd as moe
+    from sparse_expert_ffn_amd import workloads as wk
+    from sparse_expert_ffn_amd.layer import MoEBuffers, suggest_block_size
+
+    moe.load_library()
+    wl = wk.WORKLOADS[args.workload]
+    bm = args.block_size or suggest_block_size(wl.S, wl.k, wl.E)
+    dev = "cuda"
+
+    def td(a):
+        if a is None:
+            return None
+        a = np.ascontiguousarray(a)
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(a).to(dev)
+
+    A, Wr, bias = wk.draw_routing_inputs(wl)
+    su, sd, ssu, ssd = wk.expert_sigmas(wl)
+    tdt = torch.bfloat16 if wl.dtype == wk.BF16 else torch.float32
+
+    def experts(tid, shape, sigma):
+        t = torch.empty((wl.E,) + shape, dtype=tdt, device=dev)
+
+        def sink(e, slab):
+            t[e].copy_(td(slab))
+        wk.draw_experts(wl, tid, wl.E, shape, sigma, sink=sink)
+        return t
+
+    A_d, Wr_d, b_d = td(A), td(Wr), td(bias)
+    Wu = experts(wk.T_WUP, (wl.H, wl.D), su)
+    Wg = experts(wk.T_WGATE, (wl.H, wl.D), su)
+    Wd = experts(wk.T_WDOWN, (wl.D, wl.H), sd)
+    Wsu = Wsg = Wsd = None
+    if wl.D_shared:
+        Wsu = td(wk.draw_tensor(wl, wk.T_WSUP, (wl.H, wl.D_shared), ssu))
+        Wsg = td(wk.draw_tensor(wl, wk.T_WSGATE, (wl.H, wl.D_shared), ssu))
+        Wsd = td(wk.draw_tensor(wl, wk.T_WSDOWN, (wl.D_shared, wl.H), ssd))
+    buf = MoEBuffers(wl.S, wl.H, wl.D, wl.E, wl.k, wl.D_shared, wl.capacity, bm,
+                     wl.renormalize, wl.dtype, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        buf.run(A_d, Wr_d, Wu, Wg, Wd, Wsu, Wsg, Wsd, router_bias=b_d, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    counts = buf.expert_counts.cpu().numpy()
+    cnt = layer_counts(wl, counts, bm)
+
+    moe.moe_profile_enable(True)
+    moe.moe_profile_collect()  # drop anything recorded before the timed region
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    moe.moe_profile_enable(False)
+    stage_ms, n_calls = moe.moe_profile_collect(4)
+    ms = ev0.elapsed_time(ev1) / args.steps
+    up_ms = stage_ms[1] / max(n_calls, 1)
+    down_ms = stage_ms[2] / max(n_calls, 1)
+
+    peak = PEAK_BF16_TFLOPS if wl.dtype == wk.BF16 else PEAK_F32_TFLOPS
+    up_tflops = cnt["flops_up"] / (up_ms * 1e-3) / 1e12
+    layer_tflops = cnt["flops"] / (ms * 1e-3) / 1e12
+    floor_s = max(cnt["flops"] / (peak * 1e12), cnt["bytes"] / (PEAK_HBM_GBS * 1e9))
+    out = {
+        "metric": "MoE layer tokens/s (one GPU, forward)",
+        "value": wl.S / (ms * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if wl.dtype == wk.BF16 else "f32",
+        "data": "synthetic (seeded PCG64 normals, pages' distributions)",
+        "config": {"workload": wl.name, "S": wl.S, "H": wl.H, "D": wl.D, "E": wl.E, "k": wl.k,
+                   "D_shared": wl.D_shared, "capacity": wl.capacity, "block_size": bm,
+                   "parallelism": "single GPU"},
+        "roofline": {"bound": "mfma", "achieved": up_tflops, "peak": peak, "unit": "TFLOP/s",
+                     "frac": up_tflops / peak, "traffic": None,
+                     "kernel": "up/gate grouped GEMM + SwiGLU",
+                     "avg_launch_ms": up_ms, "flops_per_launch": cnt["flops_up"]},
+        "layer": {"tflops": layer_tflops, "mfma_frac": layer_tflops / peak,
+                  "floor_ms": floor_s * 1e3, "roofline_frac": floor_s / (ms * 1e-3),
+                  "gbs": cnt["bytes"] / (ms * 1e-3) / 1e9, "kept": cnt["kept"],
+                  "touched_experts": cnt["touched"], "down_ms": down_ms,
+                  "down_tflops": cnt["flops_down"] / (down_ms * 1e-3) / 1e12,
+                  "setup_ms": stage_ms[0] / max(n_calls, 1),
+                  "finalize_ms": stage_ms[3] / max(n_calls, 1),
+                  "wall_s": wall},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,220 @@
+/*
+ * sparse_expert_ffn_amd — C ABI of the fused Mixture-of-Experts layer forward
+ * pass on one MI355X (gfx950) GPU.
+ *
+ * The layer (Mixture-of-Kittens page, "Overlapping compute and communication
+ * in MoE", the layer equation and the SwiGLU definition under it):
+ *
+ *     x' = W_shared(x) + sum_{e in top-k(x)} w_e * W_down^e SwiGLU(W_up^e x, W_gate^e x),
+ *     SwiGLU(u, g) = SiLU(u) * g,   SiLU(u) = u / (1 + exp(-u)).
+ *
+ * Notation follows the FlashMoE review ("Core formulas"): A, O in R^{S x H}
+ * are the input and output token matrices, X in R^{E x H x D} the expert
+ * weights, G_phi in R^{S x E} the gate scores, T_phi(e, c) = (token i,
+ * weight w) the routing table with C slots per expert. The pass is split into
+ * the three calls the vLLM fused_moe note lists as separate launches
+ * (topk_softmax, moe_align_block_size, the two fused_moe GEMMs with SiLU-and-
+ * mul and the expert merge in between), here as:
+ *
+ *   moe_gate_topk         gate scores and softmax top-k routing
+ *   moe_align_block_size  per-expert counts, capacity, block padding,
+ *                         exclusive cumsum, sorted ids and per-block expert ids
+ *   moe_forward           up/gate GEMM + SwiGLU, down GEMM + router-weighted
+ *                         combine, shared expert, output cast
+ *
+ * Conventions for every call:
+ *  - Every array argument is a DEVICE pointer (hipMalloc'd or equivalent
+ *    device memory), except the shape struct, which is a host pointer read
+ *    before the call returns. All arrays are dense and row-major.
+ *  - `stream` is a hipStream_t (NULL = the default stream). A call validates
+ *    its arguments on the host, enqueues kernels on `stream` and returns; it
+ *    never synchronises, never allocates or frees device memory, and never
+ *    retains a pointer after it returns. The caller owns every buffer and
+ *    must keep them alive until the enqueued work has finished.
+ *  - Errors are returned as a moe_status; nothing aborts or throws across the
+ *    ABI. Argument errors are found before anything is enqueued. A failure of
+ *    the HIP runtime while enqueuing is MOE_ERR_HIP. Faults inside kernels
+ *    surface at the caller's next synchronisation.
+ *  - Device-side preconditions (topk_ids in [0, E), sorted_ids / expert_ids
+ *    / num_tokens_post_padded produced by moe_align_block_size with the same
+ *    shape) are not checked on the device.
+ *  - Element offsets are computed in 64-bit (size_t) arithmetic; indices
+ *    stored in arrays are int32 (vLLM PR 53280 summary, "Implementation"
+ *    step 3, widens its offsets for the same reason).
+ *  - Calls on different streams need distinct workspaces and outputs.
+ */
+#ifndef SPARSE_EXPERT_FFN_AMD_MOE_H
+#define SPARSE_EXPERT_FFN_AMD_MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARGUMENT = 1,   /* null pointer, bad dimension, k > E, ... */
+  MOE_ERR_UNSUPPORTED = 2,        /* valid layer the kernels do not cover      */
+  MOE_ERR_WORKSPACE_TOO_SMALL = 3,
+  MOE_ERR_HIP = 4                 /* HIP runtime error while enqueuing         */
+} moe_status;
+
+typedef enum {
+  MOE_F32 = 0,   /* activations, weights and output are fp32                */
+  MOE_BF16 = 1   /* bf16 activations/weights/output; accumulation is fp32  */
+} moe_dtype;
+
+/* Shape of one MoE layer call. */
+typedef struct {
+  int64_t S;           /* tokens (rows of A and O); 0 is a valid empty call    */
+  int64_t H;           /* hidden size (columns of A and O)                      */
+  int64_t D;           /* routed expert intermediate size                       */
+  int64_t E;           /* routed experts, 1..1024                               */
+  int64_t k;           /* experts per token, 1..min(E, 32)                      */
+  int64_t D_shared;    /* shared expert intermediate size; 0 = no shared expert */
+  int64_t capacity;    /* C slots per expert (T_phi in (N x R)^{E x C});
+                          0 = dropless. An expert keeps its assignments in
+                          ascending token order; those past slot C are dropped
+                          and contribute nothing (weights are not rescaled).  */
+  int32_t block_size;  /* BM rows per sorted block. moe_align_block_size
+                          accepts any value >= 1; moe_forward takes 16, 32, 64
+                          or 128 and must see the value the align call used.  */
+  int32_t renormalize; /* 1: router weights = softmax over the k chosen scores
+                          (the full softmax restricted and rescaled to sum 1);
+                          0: the full softmax over all E scores at the chosen ids */
+  int32_t dtype;       /* moe_dtype                                             */
+  int32_t flags;       /* 0, or MOE_OUTPUT_F32                                  */
+} moe_shape;
+
+/* flags: in bf16 mode, write O as fp32 (the fp32 accumulator itself, no final
+ * rounding to bf16). Ignored in fp32 mode, where O is fp32 anyway. */
+#define MOE_OUTPUT_F32 1
+
+/*
+ * Gate scores and softmax top-k routing.
+ *
+ * Computes G = A . W_router (+ router_bias), the S x E affinity matrix G_phi
+ * (FlashMoE review, "Core formulas", and Algorithm 1's FusedGate step), then
+ * per token the k largest scores (vLLM fused_moe note, "topk_softmax"): slot
+ * j holds the j-th largest score's expert; equal scores go to the lower
+ * expert index; NaN scores rank as -inf. Router weights are computed in
+ * double from the fp32 scores and rounded once to fp32:
+ *   renormalize=1: w_j = exp(G_j - G_0) / sum_{j'<k} exp(G_j' - G_0)
+ *   renormalize=0: w_j = exp(G_j - G_0) / sum_{e<E} exp(G_e - G_0)
+ *
+ *   A            [S][H]   dtype                      (read if logits_in NULL)
+ *   W_router     [H][E]   dtype                      (read if logits_in NULL)
+ *   router_bias  [E]      fp32, or NULL; added (fp32 add) to each score row
+ *   logits_in    [S][E]   fp32, or NULL. When given, these are the scores
+ *                         (no GEMM, no bias): A and W_router may be NULL.
+ *   logits_out   [S][E]   fp32: receives the scores used. Required when
+ *                         logits_in is NULL (it is the GEMM's output buffer);
+ *                         optional (a copy of logits_in) otherwise.
+ * The GEMM path requires H a multiple of 8 and 16-byte aligned A and
+ * W_router (else MOE_ERR_UNSUPPORTED).
+ *   topk_ids     [S][k]   int32 out
+ *   topk_weights [S][k]   fp32 out
+ */
+moe_status moe_gate_topk(const moe_shape* shape, const void* A, const void* W_router,
+                         const float* router_bias, const float* logits_in, float* logits_out,
+                         int32_t* topk_ids, float* topk_weights, void* stream);
+
+/* Bytes of device workspace moe_align_block_size needs for this shape
+ * (depends on S, k, E only). 0 on invalid shape. */
+size_t moe_align_workspace_bytes(const moe_shape* shape);
+
+/*
+ * moe_align_block_size (vLLM fused_moe note, op table; vLLM PR 53280 summary,
+ * "Implementation" steps 2-3; the routing table with C slots per expert from
+ * the FlashMoE review, "Core formulas"). Over the F = S*k flat assignments
+ * f = token*k + slot:
+ *   cnt_e   = #{f : topk_ids[f] = e}
+ *   kept_e  = min(cnt_e, capacity) (cnt_e when dropless)
+ *   pad_e   = ceil(kept_e / BM) * BM
+ *   off_e   = sum_{e' < e} pad_e'                      (exclusive cumsum)
+ *   sorted_ids[off_e + c] = the c-th (ascending f) assignment of expert e,
+ *                           for c < kept_e; sorted_ids[off_e + c] = F (the
+ *                           sentinel) for kept_e <= c < pad_e
+ *   expert_ids[b]          = e for every block b of expert e
+ *   *num_tokens_post_padded = sum_e pad_e
+ *   expert_counts[e]        = kept_e
+ * The result is a pure integer function of topk_ids (bit-reproducible).
+ * Entries past num_tokens_post_padded (and blocks past it) are unspecified.
+ *
+ *   topk_ids       [S*k]                     int32 in, values in [0, E)
+ *   sorted_ids     [S*k + E*(BM-1)]          int32 out
+ *   expert_ids     [(S*k + E*(BM-1)) / BM]   int32 out (at least 1 entry)
+ *   num_tokens_post_padded [1]               int32 out
+ *   expert_counts  [E]                       int32 out
+ *   workspace      >= moe_align_workspace_bytes(shape) bytes, any contents
+ */
+moe_status moe_align_block_size(const moe_shape* shape, const int32_t* topk_ids,
+                                int32_t* sorted_ids, int32_t* expert_ids,
+                                int32_t* num_tokens_post_padded, int32_t* expert_counts,
+                                void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of device workspace moe_forward needs for this shape. 0 on invalid
+ * shape. Holds the fp32 combine accumulator (bf16 mode), the SwiGLU rows of
+ * the routed and shared experts, and the task counters. */
+size_t moe_forward_workspace_bytes(const moe_shape* shape);
+
+/*
+ * The expert computation and combine for routed tokens (Mixture-of-Kittens
+ * layer equation; FlashMoE review, "Model components": GEMM_0 / GEMM_1 with
+ * elementwise work in between; vLLM fused_moe note, fused_moe_kernel(w1),
+ * silu_and_mul, fused_moe_kernel(w2) and the torch.sum expert merge, fused
+ * here into two GEMM launches):
+ *   for every kept assignment f = t*k + j of expert e (from sorted_ids):
+ *     h_f  = SiLU(A_t . W_up^e) * (A_t . W_gate^e)              [D]
+ *     O_t += topk_weights[f] * h_f . W_down^e                   [H]
+ *   plus, when D_shared > 0, for every token t:
+ *     O_t += SiLU(A_t . Ws_up) * (A_t . Ws_gate) . Ws_down      (weight 1)
+ * O is fully overwritten. Tokens with no kept assignment (and no shared
+ * expert) get O_t = 0. Accumulation is fp32; in bf16 mode h is stored as
+ * bf16 and O is rounded once from fp32 to bf16, unless flags has
+ * MOE_OUTPUT_F32 (then O is fp32).
+ *
+ *   A         [S][H]              dtype
+ *   W_up      [E][H][D]           dtype   (X in R^{E x H x D})
+ *   W_gate    [E][H][D]           dtype
+ *   W_down    [E][D][H]           dtype
+ *   Ws_up     [H][D_shared]       dtype, NULL iff D_shared = 0
+ *   Ws_gate   [H][D_shared]       dtype, NULL iff D_shared = 0
+ *   Ws_down   [D_shared][H]       dtype, NULL iff D_shared = 0
+ *   topk_weights [S*k]            fp32 (from moe_gate_topk)
+ *   sorted_ids, expert_ids, num_tokens_post_padded: moe_align_block_size
+ *                                 outputs for this shape
+ *   O         [S][H]              dtype out (fp32 with MOE_OUTPUT_F32)
+ *   workspace >= moe_forward_workspace_bytes(shape) bytes, any contents
+ * Requires H, D, D_shared multiples of 8 and block_size in {16,32,64,128}
+ * (else MOE_ERR_UNSUPPORTED).
+ */
+moe_status moe_forward(const moe_shape* shape, const void* A, const void* W_up,
+                       const void* W_gate, const void* W_down, const void* Ws_up,
+                       const void* Ws_gate, const void* Ws_down, const float* topk_weights,
+                       const int32_t* sorted_ids, const int32_t* expert_ids,
+                       const int32_t* num_tokens_post_padded, void* O, void* workspace,
+                       size_t workspace_bytes, void* stream);
+
+/* Static, never-NULL text for a status code. */
+const char* moe_status_string(moe_status status);
+
+/*
+ * Per-stage timing of moe_forward (measurement aid, not part of the layer).
+ * After moe_profile_enable(1), each moe_forward call records a pair of HIP
+ * events on its stream around each kernel it enqueues. moe_profile_collect
+ * waits for those events, adds each stage's elapsed milliseconds to
+ * stage_ms[stage] (stage_ms has room for max_stages floats; stages are
+ * 0 = setup, 1 = up/gate GEMM, 2 = down GEMM, 3 = finalize), stores the
+ * number of calls recorded in *n_calls, and forgets them. Not thread-safe.
+ */
+moe_status moe_profile_enable(int enable);
+moe_status moe_profile_collect(float* stage_ms, int max_stages, int* n_calls);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPARSE_EXPERT_FFN_AMD_MOE_H */

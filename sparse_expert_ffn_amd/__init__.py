@@ -1,0 +1,202 @@
+"""Fused Mixture-of-Experts layer forward pass on one MI355X (gfx950).
+
+Thin ctypes binding of the C ABI in include/moe.h, with the same names.
+It only marshals arguments: every step of the layer runs in the HIP kernels
+of libmoe.so. Array arguments are device tensors (torch, on the GPU) or raw
+device addresses (int); ``stream`` is a torch stream, a raw hipStream_t
+(int), or None for torch's current stream.
+
+Loading fails loudly when libmoe.so has not been built (``build()``); there
+is no CPU fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = ["MOE_F32", "MOE_BF16", "MoeError", "moe_shape", "make_shape", "load_library",
+           "moe_gate_topk", "moe_align_workspace_bytes", "moe_align_block_size",
+           "moe_forward_workspace_bytes", "moe_forward", "moe_status_string",
+           "moe_profile_enable", "moe_profile_collect", "build", "LIB_PATH", "STATUS"]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe.so")
+
+MOE_F32 = 0
+MOE_BF16 = 1
+MOE_OUTPUT_F32 = 1
+
+STATUS = {0: "MOE_OK", 1: "MOE_ERR_INVALID_ARGUMENT", 2: "MOE_ERR_UNSUPPORTED",
+          3: "MOE_ERR_WORKSPACE_TOO_SMALL", 4: "MOE_ERR_HIP"}
+
+# names of the entry points declared in include/moe.h
+EXPORTS = ("moe_gate_topk", "moe_align_workspace_bytes", "moe_align_block_size",
+           "moe_forward_workspace_bytes", "moe_forward", "moe_status_string",
+           "moe_profile_enable", "moe_profile_collect")
+
+
+class MoeError(RuntimeError):
+    def __init__(self, call: str, code: int):
+        self.code = code
+        super().__init__(f"{call} failed: {STATUS.get(code, code)}")
+
+
+class moe_shape(ctypes.Structure):
+    _fields_ = [("S", ctypes.c_int64), ("H", ctypes.c_int64), ("D", ctypes.c_int64),
+                ("E", ctypes.c_int64), ("k", ctypes.c_int64), ("D_shared", ctypes.c_int64),
+                ("capacity", ctypes.c_int64), ("block_size", ctypes.c_int32),
+                ("renormalize", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("flags", ctypes.c_int32)]
+
+    def __repr__(self):
+        return ("moe_shape(" + ", ".join(f"{n}={getattr(self, n)}" for n, _ in self._fields_)
+                + ")")
+
+
+def make_shape(S, H, D, E, k, D_shared=0, capacity=0, block_size=128, renormalize=1,
+               dtype=MOE_BF16, out_f32=False) -> moe_shape:
+    return moe_shape(S, H, D, E, k, D_shared, capacity, block_size, renormalize, dtype,
+                     MOE_OUTPUT_F32 if out_f32 else 0)
+
+
+_LIB = None
+
+
+def build(verbose: bool = False) -> str:
+    """Compile libmoe.so for gfx950 in-tree (hipcc)."""
+    from . import buildlib as _b
+    global _LIB
+    _LIB = None
+    return _b.build(verbose=verbose)
+
+
+def load_library(path: str | None = None) -> ctypes.CDLL:
+    global _LIB
+    if _LIB is not None and path is None:
+        return _LIB
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise ImportError(f"{p} is missing: the HIP library must be built first "
+                          "(sparse_expert_ffn_amd.build())")
+    lib = ctypes.CDLL(p)
+    vp, i64, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t
+    sp = ctypes.POINTER(moe_shape)
+    lib.moe_gate_topk.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.moe_align_workspace_bytes.argtypes = [sp]
+    lib.moe_align_workspace_bytes.restype = sz
+    lib.moe_align_block_size.argtypes = [sp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.moe_forward_workspace_bytes.argtypes = [sp]
+    lib.moe_forward_workspace_bytes.restype = sz
+    lib.moe_forward.argtypes = [sp] + [vp] * 13 + [sz, vp]
+    lib.moe_status_string.argtypes = [ctypes.c_int]
+    lib.moe_status_string.restype = ctypes.c_char_p
+    lib.moe_profile_enable.argtypes = [ctypes.c_int]
+    lib.moe_profile_collect.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_int,
+                                        ctypes.POINTER(ctypes.c_int)]
+    for name in ("moe_gate_topk", "moe_align_block_size", "moe_forward", "moe_profile_enable",
+                 "moe_profile_collect"):
+        getattr(lib, name).restype = ctypes.c_int
+    del i64
+    if path is None:
+        _LIB = lib
+    return lib
+
+
+def _addr(x):
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    if hasattr(x, "data_ptr"):
+        if hasattr(x, "is_contiguous") and not x.is_contiguous():
+            raise ValueError("tensor arguments must be contiguous")
+        if getattr(x, "device", None) is not None and x.device.type != "cuda":
+            raise ValueError(f"tensor on {x.device}: the library takes device memory")
+        return x.data_ptr() if x.numel() else None
+    raise TypeError(f"cannot pass {type(x)} as a device pointer")
+
+
+def _nbytes(x):
+    if x is None:
+        return 0
+    if isinstance(x, int):
+        raise TypeError("pass the workspace as a tensor, or (address, nbytes)")
+    return x.numel() * x.element_size()
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _ws(workspace):
+    if isinstance(workspace, tuple):
+        return workspace[0], workspace[1]
+    return _addr(workspace), _nbytes(workspace)
+
+
+def _check(call, code):
+    if code != 0:
+        raise MoeError(call, code)
+
+
+def moe_status_string(code: int) -> str:
+    return load_library().moe_status_string(code).decode()
+
+
+def moe_gate_topk(shape, A, W_router, router_bias, logits_in, logits_out, topk_ids,
+                  topk_weights, stream=None, check=True) -> int:
+    code = load_library().moe_gate_topk(
+        ctypes.byref(shape), _addr(A), _addr(W_router), _addr(router_bias), _addr(logits_in),
+        _addr(logits_out), _addr(topk_ids), _addr(topk_weights), _stream(stream))
+    if check:
+        _check("moe_gate_topk", code)
+    return code
+
+
+def moe_align_workspace_bytes(shape) -> int:
+    return int(load_library().moe_align_workspace_bytes(ctypes.byref(shape)))
+
+
+def moe_align_block_size(shape, topk_ids, sorted_ids, expert_ids, num_tokens_post_padded,
+                         expert_counts, workspace, stream=None, check=True) -> int:
+    wa, wn = _ws(workspace)
+    code = load_library().moe_align_block_size(
+        ctypes.byref(shape), _addr(topk_ids), _addr(sorted_ids), _addr(expert_ids),
+        _addr(num_tokens_post_padded), _addr(expert_counts), wa, wn, _stream(stream))
+    if check:
+        _check("moe_align_block_size", code)
+    return code
+
+
+def moe_forward_workspace_bytes(shape) -> int:
+    return int(load_library().moe_forward_workspace_bytes(ctypes.byref(shape)))
+
+
+def moe_forward(shape, A, W_up, W_gate, W_down, Ws_up, Ws_gate, Ws_down, topk_weights,
+                sorted_ids, expert_ids, num_tokens_post_padded, O, workspace, stream=None,
+                check=True) -> int:
+    wa, wn = _ws(workspace)
+    code = load_library().moe_forward(
+        ctypes.byref(shape), _addr(A), _addr(W_up), _addr(W_gate), _addr(W_down), _addr(Ws_up),
+        _addr(Ws_gate), _addr(Ws_down), _addr(topk_weights), _addr(sorted_ids),
+        _addr(expert_ids), _addr(num_tokens_post_padded), _addr(O), wa, wn, _stream(stream))
+    if check:
+        _check("moe_forward", code)
+    return code
+
+
+def moe_profile_enable(enable: bool) -> None:
+    _check("moe_profile_enable", load_library().moe_profile_enable(1 if enable else 0))
+
+
+def moe_profile_collect(n_stages: int = 4):
+    """(per-stage milliseconds summed over recorded calls, number of calls)."""
+    buf = (ctypes.c_float * n_stages)()
+    n = ctypes.c_int(0)
+    _check("moe_profile_collect", load_library().moe_profile_collect(buf, n_stages,
+                                                                     ctypes.byref(n)))
+    return [float(x) for x in buf], int(n.value)

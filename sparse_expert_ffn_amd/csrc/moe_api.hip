@@ -1,0 +1,311 @@
+// Host side of the C ABI declared in include/moe.h: argument validation,
+// workspace layout, kernel launches and the optional per-stage timing.
+#include <mutex>
+#include <vector>
+
+#include "moe.h"
+#include "moe_common.h"
+
+using namespace moe;
+
+namespace {
+
+constexpr int64_t kMaxE = 1024;
+constexpr int64_t kMaxK = 32;
+constexpr size_t kAlignUp = 256;
+
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
+moe_status check_routing_dims(const moe_shape* s) {
+  if (s == nullptr) return MOE_ERR_INVALID_ARGUMENT;
+  if (s->flags != 0 && s->flags != MOE_OUTPUT_F32) return MOE_ERR_INVALID_ARGUMENT;
+  if (s->dtype != MOE_F32 && s->dtype != MOE_BF16) return MOE_ERR_INVALID_ARGUMENT;
+  if (s->S < 0 || s->E < 1 || s->k < 1 || s->k > s->E) return MOE_ERR_INVALID_ARGUMENT;
+  if (s->E > kMaxE || s->k > kMaxK) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+moe_status check_align_dims(const moe_shape* s) {
+  moe_status st = check_routing_dims(s);
+  if (st != MOE_OK) return st;
+  if (s->block_size < 1 || s->capacity < 0) return MOE_ERR_INVALID_ARGUMENT;
+  // every stored index (flat ids, the sentinel S*k, padded positions) is int32
+  if (s->S > (int64_t)INT32_MAX / s->k) return MOE_ERR_UNSUPPORTED;
+  const int64_t cap = s->S * s->k + s->E * ((int64_t)s->block_size - 1);
+  if (cap > (int64_t)INT32_MAX) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+moe_status check_forward_dims(const moe_shape* s) {
+  moe_status st = check_align_dims(s);
+  if (st != MOE_OK) return st;
+  if (s->H < 1 || s->D < 1 || s->D_shared < 0) return MOE_ERR_INVALID_ARGUMENT;
+  if (s->H % 8 || s->D % 8 || s->D_shared % 8) return MOE_ERR_UNSUPPORTED;
+  if (!forward_lds_ok(s->dtype, s->block_size)) return MOE_ERR_UNSUPPORTED;
+  if (s->S > (int64_t)INT32_MAX) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+int64_t align_nseg(const moe_shape* s) { return (s->S * s->k + kAlignSeg - 1) / kAlignSeg; }
+
+struct AlignLayout {
+  size_t seg_counts, offsets, kept, total;
+};
+
+AlignLayout align_layout(const moe_shape* s) {
+  AlignLayout L;
+  L.seg_counts = 0;
+  L.offsets = round_up((size_t)align_nseg(s) * s->E * sizeof(int32_t), kAlignUp);
+  L.kept = L.offsets + round_up((size_t)s->E * sizeof(int64_t), kAlignUp);
+  L.total = L.kept + round_up((size_t)s->E * sizeof(int32_t), kAlignUp);
+  return L;
+}
+
+// bf16 output: accumulate in an fp32 workspace buffer, then cast into O.
+bool needs_cast(const moe_shape* s) {
+  return s->dtype == MOE_BF16 && (s->flags & MOE_OUTPUT_F32) == 0;
+}
+
+struct ForwardLayout {
+  size_t counters, oacc, h, hs, total;
+};
+
+ForwardLayout forward_layout(const moe_shape* s) {
+  const size_t es = s->dtype == MOE_BF16 ? 2 : 4;
+  const int64_t BM = s->block_size;
+  const int64_t cap_rows = (s->S * s->k + s->E * (BM - 1) + BM - 1) / BM * BM;
+  const int64_t s_rows = (s->S + BM - 1) / BM * BM;
+  ForwardLayout L;
+  L.counters = 0;
+  L.oacc = round_up(kCounterInts * sizeof(int), kAlignUp);
+  const size_t oacc_bytes = needs_cast(s) ? (size_t)s->S * s->H * sizeof(float) : 0;
+  L.h = L.oacc + round_up(oacc_bytes, kAlignUp);
+  L.hs = L.h + round_up((size_t)cap_rows * s->D * es, kAlignUp);
+  L.total = L.hs + round_up((size_t)s_rows * s->D_shared * es, kAlignUp);
+  return L;
+}
+
+// ------------------------------------------------------------ stage timing
+struct ProfileRecord {
+  int stage;
+  hipEvent_t start, stop;
+};
+
+std::mutex g_prof_mu;
+bool g_prof_on = false;
+int g_prof_calls = 0;
+std::vector<ProfileRecord> g_prof;
+std::vector<hipEvent_t> g_event_pool;
+
+hipEvent_t take_event() {
+  if (!g_event_pool.empty()) {
+    hipEvent_t e = g_event_pool.back();
+    g_event_pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+// Launch one stage, bracketed by events when timing is on.
+template <typename F>
+hipError_t run_stage(int stage, hipStream_t st, F launch) {
+  if (!g_prof_on) return launch();
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  ProfileRecord r{stage, take_event(), take_event()};
+  if (r.start == nullptr || r.stop == nullptr) return hipErrorOutOfMemory;
+  hipError_t e = hipEventRecord(r.start, st);
+  if (e != hipSuccess) return e;
+  e = launch();
+  if (e != hipSuccess) return e;
+  e = hipEventRecord(r.stop, st);
+  if (e != hipSuccess) return e;
+  g_prof.push_back(r);
+  return hipSuccess;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_string(moe_status status) {
+  switch (status) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_ERR_INVALID_ARGUMENT: return "MOE_ERR_INVALID_ARGUMENT";
+    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED";
+    case MOE_ERR_WORKSPACE_TOO_SMALL: return "MOE_ERR_WORKSPACE_TOO_SMALL";
+    case MOE_ERR_HIP: return "MOE_ERR_HIP";
+  }
+  return "MOE_ERR_UNKNOWN";
+}
+
+moe_status moe_gate_topk(const moe_shape* shape, const void* A, const void* W_router,
+                         const float* router_bias, const float* logits_in, float* logits_out,
+                         int32_t* topk_ids, float* topk_weights, void* stream) {
+  moe_status st = check_routing_dims(shape);
+  if (st != MOE_OK) return st;
+  if (shape->renormalize != 0 && shape->renormalize != 1) return MOE_ERR_INVALID_ARGUMENT;
+  if (shape->S == 0) return MOE_OK;
+  if (topk_ids == nullptr || topk_weights == nullptr) return MOE_ERR_INVALID_ARGUMENT;
+  const float* G = logits_in;
+  if (logits_in == nullptr) {
+    if (A == nullptr || W_router == nullptr || logits_out == nullptr) return MOE_ERR_INVALID_ARGUMENT;
+    if (shape->H < 1) return MOE_ERR_INVALID_ARGUMENT;
+    if (shape->H % 8 || !aligned16(A) || !aligned16(W_router)) return MOE_ERR_UNSUPPORTED;
+    G = logits_out;
+  }
+  hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+  if (logits_in == nullptr) {
+    GateParams gp{A, W_router, router_bias, logits_out, shape->S, shape->H, shape->E};
+    if (launch_gate(gp, shape->dtype, hs) != hipSuccess) return MOE_ERR_HIP;
+  } else if (logits_out != nullptr && logits_out != logits_in) {
+    if (hipMemcpyAsync(logits_out, logits_in, (size_t)shape->S * shape->E * sizeof(float),
+                       hipMemcpyDeviceToDevice, hs) != hipSuccess)
+      return MOE_ERR_HIP;
+  }
+  TopkParams tp{G, topk_ids, topk_weights, shape->S, shape->E, shape->k, shape->renormalize};
+  if (launch_topk(tp, hs) != hipSuccess) return MOE_ERR_HIP;
+  return MOE_OK;
+}
+
+size_t moe_align_workspace_bytes(const moe_shape* shape) {
+  if (check_align_dims(shape) != MOE_OK) return 0;
+  return align_layout(shape).total;
+}
+
+moe_status moe_align_block_size(const moe_shape* shape, const int32_t* topk_ids,
+                                int32_t* sorted_ids, int32_t* expert_ids,
+                                int32_t* num_tokens_post_padded, int32_t* expert_counts,
+                                void* workspace, size_t workspace_bytes, void* stream) {
+  moe_status st = check_align_dims(shape);
+  if (st != MOE_OK) return st;
+  if ((topk_ids == nullptr && shape->S > 0) || sorted_ids == nullptr || expert_ids == nullptr ||
+      num_tokens_post_padded == nullptr || expert_counts == nullptr || workspace == nullptr)
+    return MOE_ERR_INVALID_ARGUMENT;
+  const AlignLayout L = align_layout(shape);
+  if (workspace_bytes < L.total) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  char* ws = static_cast<char*>(workspace);
+  AlignParams p;
+  p.ids = topk_ids;
+  p.sorted_ids = sorted_ids;
+  p.expert_ids = expert_ids;
+  p.ntpp = num_tokens_post_padded;
+  p.counts = expert_counts;
+  p.seg_counts = reinterpret_cast<int32_t*>(ws + L.seg_counts);
+  p.offsets = reinterpret_cast<int64_t*>(ws + L.offsets);
+  p.kept = reinterpret_cast<int32_t*>(ws + L.kept);
+  p.F = shape->S * shape->k;
+  p.E = shape->E;
+  p.BM = shape->block_size;
+  p.C = shape->capacity;
+  p.nseg = align_nseg(shape);
+  if (launch_align(p, reinterpret_cast<hipStream_t>(stream)) != hipSuccess) return MOE_ERR_HIP;
+  return MOE_OK;
+}
+
+size_t moe_forward_workspace_bytes(const moe_shape* shape) {
+  if (check_forward_dims(shape) != MOE_OK) return 0;
+  return forward_layout(shape).total;
+}
+
+moe_status moe_forward(const moe_shape* shape, const void* A, const void* W_up,
+                       const void* W_gate, const void* W_down, const void* Ws_up,
+                       const void* Ws_gate, const void* Ws_down, const float* topk_weights,
+                       const int32_t* sorted_ids, const int32_t* expert_ids,
+                       const int32_t* num_tokens_post_padded, void* O, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+  moe_status st = check_forward_dims(shape);
+  if (st != MOE_OK) return st;
+  const bool has_shared = shape->D_shared > 0;
+  if ((Ws_up != nullptr) != has_shared || (Ws_gate != nullptr) != has_shared ||
+      (Ws_down != nullptr) != has_shared)
+    return MOE_ERR_INVALID_ARGUMENT;
+  if (shape->S == 0) return MOE_OK;
+  if (A == nullptr || W_up == nullptr || W_gate == nullptr || W_down == nullptr ||
+      topk_weights == nullptr || sorted_ids == nullptr || expert_ids == nullptr ||
+      num_tokens_post_padded == nullptr || O == nullptr || workspace == nullptr)
+    return MOE_ERR_INVALID_ARGUMENT;
+  const void* vec_ptrs[] = {A, W_up, W_gate, W_down, O, workspace};
+  for (const void* q : vec_ptrs)
+    if (!aligned16(q)) return MOE_ERR_UNSUPPORTED;
+  if (has_shared && (!aligned16(Ws_up) || !aligned16(Ws_gate) || !aligned16(Ws_down)))
+    return MOE_ERR_UNSUPPORTED;
+  const ForwardLayout L = forward_layout(shape);
+  if (workspace_bytes < L.total) return MOE_ERR_WORKSPACE_TOO_SMALL;
+
+  char* ws = static_cast<char*>(workspace);
+  ForwardParams p;
+  p.A = A;
+  p.Wu = W_up;
+  p.Wg = W_gate;
+  p.Wd = W_down;
+  p.Wsu = Ws_up;
+  p.Wsg = Ws_gate;
+  p.Wsd = Ws_down;
+  p.topk_w = topk_weights;
+  p.sorted_ids = sorted_ids;
+  p.expert_ids = expert_ids;
+  p.ntpp = num_tokens_post_padded;
+  p.O = O;
+  const bool cast = needs_cast(shape);
+  p.Oacc = cast ? reinterpret_cast<float*>(ws + L.oacc) : reinterpret_cast<float*>(O);
+  p.h = ws + L.h;
+  p.hs = ws + L.hs;
+  p.counters = reinterpret_cast<int*>(ws + L.counters);
+  p.S = shape->S;
+  p.H = shape->H;
+  p.D = shape->D;
+  p.E = shape->E;
+  p.k = shape->k;
+  p.Ds = shape->D_shared;
+  p.F = shape->S * shape->k;
+  p.grid = 0;
+  const int dt = shape->dtype;
+  const int BM = shape->block_size;
+  hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+  if (g_prof_on) {
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    ++g_prof_calls;
+  }
+  if (run_stage(0, hs, [&] { return launch_forward_setup(p, dt, hs); }) != hipSuccess)
+    return MOE_ERR_HIP;
+  if (run_stage(1, hs, [&] { return launch_forward_upgate(p, dt, BM, hs); }) != hipSuccess)
+    return MOE_ERR_HIP;
+  if (run_stage(2, hs, [&] { return launch_forward_down(p, dt, BM, hs); }) != hipSuccess)
+    return MOE_ERR_HIP;
+  if (cast && run_stage(3, hs, [&] { return launch_forward_finalize(p, hs); }) != hipSuccess)
+    return MOE_ERR_HIP;
+  return MOE_OK;
+}
+
+moe_status moe_profile_enable(int enable) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  g_prof_on = enable != 0;
+  return MOE_OK;
+}
+
+moe_status moe_profile_collect(float* stage_ms, int max_stages, int* n_calls) {
+  if (max_stages < 0 || (max_stages > 0 && stage_ms == nullptr)) return MOE_ERR_INVALID_ARGUMENT;
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  moe_status st = MOE_OK;
+  for (const ProfileRecord& r : g_prof) {
+    float ms = 0.f;
+    if (hipEventSynchronize(r.stop) != hipSuccess ||
+        hipEventElapsedTime(&ms, r.start, r.stop) != hipSuccess) {
+      st = MOE_ERR_HIP;
+    } else if (r.stage < max_stages) {
+      stage_ms[r.stage] += ms;
+    }
+    g_event_pool.push_back(r.start);
+    g_event_pool.push_back(r.stop);
+  }
+  g_prof.clear();
+  if (n_calls) *n_calls = g_prof_calls;
+  g_prof_calls = 0;
+  return st;
+}
+
+}  // extern "C"

@@ -1,0 +1,108 @@
+// Internal definitions shared by the HIP sources of the MoE library.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+typedef uint16_t bf16_t;
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kXcds = 8;          // MI355X: 8 XCDs, workgroups dispatched round-robin
+constexpr int kCounterInts = 64;  // task counters at the head of the forward workspace
+
+__device__ __forceinline__ float bf16_to_f32(bf16_t x) {
+  return __uint_as_float(((uint32_t)x) << 16);
+}
+
+__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
+  // round to nearest even (v_cvt_pk_bf16_f32 on gfx950)
+  __bf16 b = (__bf16)f;
+  return __builtin_bit_cast(bf16_t, b);
+}
+
+template <typename T>
+__device__ __forceinline__ float to_f32(T x);
+template <>
+__device__ __forceinline__ float to_f32<float>(float x) { return x; }
+template <>
+__device__ __forceinline__ float to_f32<bf16_t>(bf16_t x) { return bf16_to_f32(x); }
+
+template <typename T>
+__device__ __forceinline__ T from_f32(float x);
+template <>
+__device__ __forceinline__ float from_f32<float>(float x) { return x; }
+template <>
+__device__ __forceinline__ bf16_t from_f32<bf16_t>(float x) { return f32_to_bf16(x); }
+
+__device__ __forceinline__ float silu_f32(float u) { return u / (1.0f + __expf(-u)); }
+
+// ---------------------------------------------------------------- launchers
+// Host-side launch helpers implemented in the .hip sources; each returns the
+// hipError_t of its launch.
+
+struct GateParams {
+  const void* A;          // [S][H]
+  const void* Wr;         // [H][E]
+  const float* bias;      // [E] or null
+  float* G;               // [S][E]
+  int64_t S, H, E;
+};
+
+struct TopkParams {
+  const float* G;         // [S][E]
+  int32_t* ids;           // [S][k]
+  float* w;               // [S][k]
+  int64_t S, E, k;
+  int renormalize;
+};
+
+struct AlignParams {
+  const int32_t* ids;     // [F]
+  int32_t* sorted_ids;
+  int32_t* expert_ids;
+  int32_t* ntpp;
+  int32_t* counts;
+  int32_t* seg_counts;    // workspace [nseg][E]
+  int64_t* offsets;       // workspace [E]
+  int32_t* kept;          // workspace [E]
+  int64_t F, E, BM, C;
+  int64_t nseg;
+};
+
+struct ForwardParams {
+  const void* A;
+  const void* Wu;
+  const void* Wg;
+  const void* Wd;
+  const void* Wsu;
+  const void* Wsg;
+  const void* Wsd;
+  const float* topk_w;
+  const int32_t* sorted_ids;
+  const int32_t* expert_ids;
+  const int32_t* ntpp;
+  void* O;                // [S][H] dtype
+  float* Oacc;            // [S][H] fp32 accumulator (== O in fp32 mode)
+  void* h;                // [cap_rows][D]
+  void* hs;               // [round_up(S, BM)][Ds]
+  int* counters;          // kCounterInts ints
+  int64_t S, H, D, E, k, Ds, F;
+  int grid;               // persistent workgroups
+};
+
+constexpr int kAlignSeg = 512;   // assignments per wave segment in the align kernels
+
+hipError_t launch_gate(const GateParams& p, int dtype, hipStream_t st);
+hipError_t launch_topk(const TopkParams& p, hipStream_t st);
+hipError_t launch_align(const AlignParams& p, hipStream_t st);
+hipError_t launch_forward_setup(const ForwardParams& p, int dtype, hipStream_t st);
+hipError_t launch_forward_upgate(const ForwardParams& p, int dtype, int BM, hipStream_t st);
+hipError_t launch_forward_down(const ForwardParams& p, int dtype, int BM, hipStream_t st);
+hipError_t launch_forward_finalize(const ForwardParams& p, hipStream_t st);
+int forward_lds_ok(int dtype, int BM);
+
+}  // namespace moe

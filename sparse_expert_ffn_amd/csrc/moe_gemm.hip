@@ -1,0 +1,382 @@
+// GEMM kernels of the MoE layer: gate scores, and the two persistent grouped
+// GEMMs of the expert FFN (up/gate with a SwiGLU epilogue, down with the
+// router-weighted combine epilogue), plus the accumulator setup and the
+// final output cast.
+//
+// Persistent scheduling (Weave review, sections 2.1-2.2 and 5.1): the work of
+// a grouped GEMM is cut into tile tasks (m-block of BM sorted rows, n-tile of
+// BN output columns); a grid of about one workgroup per CU claims tasks with
+// an atomic counter until none are left, instead of a fixed share of CUs per
+// expert. Task count depends on the routing and is read on the device (no
+// host synchronisation). On MI355X the task list is cut into 8 contiguous
+// ranges, one per XCD (workgroup i runs on XCD i % 8); a workgroup claims from
+// its own XCD's range first, so tasks that share weight and activation tiles
+// run on CUs that share one L2, and moves on to the other ranges when its
+// own is empty (work stealing keeps the tail balanced).
+//
+// Inside a range the tasks of a group of kGroupBlocks consecutive m-blocks are
+// ordered n-tile-major: tasks running side by side share both the A rows of
+// a few m-blocks and the weight strips of a few n-tiles.
+#include "gemm_tile.h"
+
+namespace moe {
+
+constexpr int kGroupBlocks = 4;
+constexpr int kGateBM = 64;
+constexpr int kGateBN = 64;
+
+// ------------------------------------------------------------------ gate GEMM
+// G[s][e] = sum_h A[s][h] * Wr[h][e] (+ bias[e]), fp32 out. One tile per
+// workgroup (not persistent: the gate has no routing-dependent imbalance).
+template <typename T>
+__global__ __launch_bounds__(256) void gate_gemm_kernel(GateParams p) {
+  using TG = TileGemm<T, kGateBM, kGateBN, 1>;
+  __shared__ __align__(16) char smem[TG::LDS_BYTES];
+  const int64_t n_tiles = (p.E + kGateBN - 1) / kGateBN;
+  const int64_t m0 = (int64_t)(blockIdx.x / n_tiles) * kGateBM;
+  const int64_t n0 = (int64_t)(blockIdx.x % n_tiles) * kGateBN;
+  TG g;
+  const char* Ab = reinterpret_cast<const char*>(p.A);
+  const char* Bm[1] = {reinterpret_cast<const char*>(p.Wr) + (size_t)n0 * sizeof(T)};
+  const int64_t S = p.S, H = p.H;
+  g.setup([&](int r) -> const char* {
+    const int64_t s = m0 + r;
+    return s < S ? Ab + (size_t)s * H * sizeof(T) : nullptr;
+  }, Bm, p.E, p.E - n0);
+  g.mainloop(smem, p.H, p.E, p.E - n0);
+  g.for_each([&](int, int row, int col, float v) {
+    const int64_t s = m0 + row, e = n0 + col;
+    if (s < p.S && e < p.E) {
+      float out = v;
+      if (p.bias) out = out + p.bias[e];
+      p.G[(size_t)s * p.E + e] = out;
+    }
+  });
+}
+
+hipError_t launch_gate(const GateParams& p, int dtype, hipStream_t st) {
+  if (p.S == 0) return hipSuccess;
+  const int64_t tiles = ((p.S + kGateBM - 1) / kGateBM) * ((p.E + kGateBN - 1) / kGateBN);
+  if (dtype == 1)
+    hipLaunchKernelGGL(gate_gemm_kernel<bf16_t>, dim3((unsigned)tiles), dim3(256), 0, st, p);
+  else
+    hipLaunchKernelGGL(gate_gemm_kernel<float>, dim3((unsigned)tiles), dim3(256), 0, st, p);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------ task scheduling
+
+// Task t of a space of nb m-blocks x nn n-tiles -> (m-block b, n-tile j),
+// n-tile-major inside each group of kGroupBlocks consecutive m-blocks.
+__device__ __forceinline__ void decode_task(int64_t t, int64_t nb, int64_t nn, int64_t& b,
+                                            int64_t& j) {
+  const int64_t per = (int64_t)kGroupBlocks * nn;
+  const int64_t grp = t / per;
+  const int64_t b0 = grp * kGroupBlocks;
+  const int64_t gsz = min((int64_t)kGroupBlocks, nb - b0);
+  const int64_t w = t - grp * per;
+  j = w / gsz;
+  b = b0 + w % gsz;
+}
+
+// Claim the next task of [0, total): own XCD's range first, then the others.
+// q / tried persist across calls of one workgroup (thread 0 only).
+__device__ __forceinline__ int64_t claim_task(int* counters, int64_t total, int& q, int& tried) {
+  while (tried < kXcds) {
+    const int64_t lo = total * q / kXcds;
+    const int64_t hi = total * (q + 1) / kXcds;
+    if (lo < hi) {
+      const int c = atomicAdd(&counters[q], 1);
+      if (lo + c < hi) return lo + c;
+    }
+    q = (q + 1) % kXcds;
+    ++tried;
+  }
+  return -1;
+}
+
+struct TaskSpace {
+  int64_t nb_r, nn_r, nb_s, nn_s, t_r, total;
+};
+
+__device__ __forceinline__ TaskSpace task_space(const ForwardParams& p, int BM, int BN,
+                                                int64_t n_routed_cols, int64_t n_shared_cols) {
+  TaskSpace ts;
+  ts.nb_r = (int64_t)(*p.ntpp) / BM;
+  ts.nn_r = (n_routed_cols + BN - 1) / BN;
+  ts.nb_s = p.Ds > 0 ? (p.S + BM - 1) / BM : 0;
+  ts.nn_s = (n_shared_cols + BN - 1) / BN;
+  ts.t_r = ts.nb_r * ts.nn_r;
+  ts.total = ts.t_r + ts.nb_s * ts.nn_s;
+  return ts;
+}
+
+// ---------------------------------------------------- up/gate GEMM + SwiGLU
+// Routed task (m-block b of expert e = expert_ids[b], n-tile j):
+//   h[b*BM + r][n] = SiLU(A_t . W_up^e[:, n]) * (A_t . W_gate^e[:, n]),
+//   t = sorted_ids[b*BM + r] / k; sentinel rows are skipped.
+// Shared task (m-block b over tokens b*BM + r < S): the same with Ws_up,
+// Ws_gate into hs.
+template <typename T, int BM, int BN>
+__global__ __launch_bounds__(256, 1) void upgate_kernel(ForwardParams p) {
+  using TG = TileGemm<T, BM, BN, 2>;
+  extern __shared__ __align__(16) char smem[];
+  __shared__ int64_t s_task;
+  __shared__ int s_tok[BM];
+  const TaskSpace ts = task_space(p, BM, BN, p.D, p.Ds);
+  int q = blockIdx.x % kXcds, tried = 0;
+  TG g;
+  for (;;) {
+    if (threadIdx.x == 0) s_task = claim_task(p.counters, ts.total, q, tried);
+    __syncthreads();
+    const int64_t t = s_task;
+    if (t < 0) break;
+    const bool shared = t >= ts.t_r;
+    int64_t b, j;
+    if (!shared)
+      decode_task(t, ts.nb_r, ts.nn_r, b, j);
+    else
+      decode_task(t - ts.t_r, ts.nb_s, ts.nn_s, b, j);
+    if (threadIdx.x < BM) {
+      const int r = threadIdx.x;
+      int tok;
+      if (!shared) {
+        const int f = p.sorted_ids[b * BM + r];
+        tok = f < p.F ? (int)(f / p.k) : -1;
+      } else {
+        const int64_t s = b * BM + r;
+        tok = s < p.S ? (int)s : -1;
+      }
+      s_tok[r] = tok;
+    }
+    __syncthreads();
+    const int64_t N = shared ? p.Ds : p.D;
+    const int64_t n0 = j * BN;
+    const char* Bm[2];
+    if (!shared) {
+      const int64_t e = p.expert_ids[b];
+      const size_t off = ((size_t)e * p.H * p.D + n0) * sizeof(T);
+      Bm[0] = reinterpret_cast<const char*>(p.Wu) + off;
+      Bm[1] = reinterpret_cast<const char*>(p.Wg) + off;
+    } else {
+      Bm[0] = reinterpret_cast<const char*>(p.Wsu) + n0 * sizeof(T);
+      Bm[1] = reinterpret_cast<const char*>(p.Wsg) + n0 * sizeof(T);
+    }
+    const char* Ab = reinterpret_cast<const char*>(p.A);
+    const int64_t H = p.H;
+    g.setup([&](int r) -> const char* {
+      const int tok = s_tok[r];
+      return tok >= 0 ? Ab + (size_t)tok * H * sizeof(T) : nullptr;
+    }, Bm, N, N - n0);
+    g.mainloop(smem, p.H, N, N - n0);
+    T* out = reinterpret_cast<T*>(shared ? p.hs : p.h);
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int wm0 = (wave / TG::WN) * (BM / TG::WM);
+    const int wn0 = (wave % TG::WN) * (BN / TG::WN);
+#pragma unroll
+    for (int i = 0; i < TG::MI; ++i)
+#pragma unroll
+      for (int jj = 0; jj < TG::NI; ++jj)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int row = wm0 + i * 16 + (lane >> 4) * 4 + r;
+          const int64_t col = n0 + wn0 + jj * 16 + (lane & 15);
+          if (s_tok[row] >= 0 && col < N) {
+            const float u = g.acc[0][i][jj][r];
+            const float gv = g.acc[1][i][jj][r];
+            out[(size_t)(b * BM + row) * N + col] = from_f32<T>(silu_f32(u) * gv);
+          }
+        }
+  }
+}
+
+// ---------------------------------------------------- down GEMM + combine
+// Routed task: y = h[b*BM + r] . W_down^e[:, n-tile];
+//   O_acc[t][n] += topk_weights[f] * y for f = sorted_ids[b*BM + r] != F.
+// Shared task: y = hs[b*BM + r] . Ws_down[:, n-tile]; O_acc[s][n] += y.
+template <typename T, int BM, int BN>
+__global__ __launch_bounds__(256, 1) void down_kernel(ForwardParams p) {
+  using TG = TileGemm<T, BM, BN, 1>;
+  extern __shared__ __align__(16) char smem[];
+  __shared__ int64_t s_task;
+  __shared__ int s_tok[BM];
+  __shared__ float s_w[BM];
+  const TaskSpace ts = task_space(p, BM, BN, p.H, p.H);
+  int q = blockIdx.x % kXcds, tried = 0;
+  int* counters = p.counters + kXcds;
+  TG g;
+  for (;;) {
+    if (threadIdx.x == 0) s_task = claim_task(counters, ts.total, q, tried);
+    __syncthreads();
+    const int64_t t = s_task;
+    if (t < 0) break;
+    const bool shared = t >= ts.t_r;
+    int64_t b, j;
+    if (!shared)
+      decode_task(t, ts.nb_r, ts.nn_r, b, j);
+    else
+      decode_task(t - ts.t_r, ts.nb_s, ts.nn_s, b, j);
+    if (threadIdx.x < BM) {
+      const int r = threadIdx.x;
+      if (!shared) {
+        const int f = p.sorted_ids[b * BM + r];
+        if (f < p.F) {
+          s_tok[r] = (int)(f / p.k);
+          s_w[r] = p.topk_w[f];
+        } else {
+          s_tok[r] = -1;
+          s_w[r] = 0.f;
+        }
+      } else {
+        const int64_t s = b * BM + r;
+        s_tok[r] = s < p.S ? (int)s : -1;
+        s_w[r] = 1.f;
+      }
+    }
+    __syncthreads();
+    const int64_t K = shared ? p.Ds : p.D;
+    const int64_t n0 = j * BN;
+    const char* Bm[1];
+    if (!shared) {
+      const int64_t e = p.expert_ids[b];
+      Bm[0] = reinterpret_cast<const char*>(p.Wd) + ((size_t)e * p.D * p.H + n0) * sizeof(T);
+    } else {
+      Bm[0] = reinterpret_cast<const char*>(p.Wsd) + n0 * sizeof(T);
+    }
+    const char* Ab = reinterpret_cast<const char*>(shared ? p.hs : p.h) +
+                     (size_t)b * BM * K * sizeof(T);
+    g.setup([&](int r) -> const char* {
+      return s_tok[r] >= 0 ? Ab + (size_t)r * K * sizeof(T) : nullptr;
+    }, Bm, p.H, p.H - n0);
+    g.mainloop(smem, K, p.H, p.H - n0);
+    float* O = p.Oacc;
+    const int64_t H = p.H;
+    g.for_each([&](int, int row, int col, float v) {
+      const int tok = s_tok[row];
+      const int64_t n = n0 + col;
+      if (tok >= 0 && n < H) atomicAdd(O + (size_t)tok * H + n, s_w[row] * v);
+    });
+  }
+}
+
+template <typename T, int BM, int BN, int NB>
+static int lds_bytes() {
+  return TileGemm<T, BM, BN, NB>::LDS_BYTES;
+}
+
+static int num_cus() {
+  static int cus[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cus[dev] == 0) {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0)
+      v = 256;
+    cus[dev] = v;
+  }
+  return cus[dev];
+}
+
+template <typename K>
+static hipError_t launch_persistent(K kernel, int lds, const ForwardParams& p, hipStream_t st) {
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+  if (e != hipSuccess) return e;
+  int per_cu = 0;
+  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, 256, lds);
+  if (e != hipSuccess) return e;
+  if (per_cu < 1) per_cu = 1;
+  const int grid = num_cus() * per_cu;
+  hipLaunchKernelGGL(kernel, dim3(grid), dim3(256), lds, st, p);
+  return hipGetLastError();
+}
+
+template <typename T, int BM>
+static hipError_t launch_upgate_t(const ForwardParams& p, hipStream_t st) {
+  constexpr int BN = 128;
+  return launch_persistent(upgate_kernel<T, BM, BN>, lds_bytes<T, BM, BN, 2>(), p, st);
+}
+
+template <typename T, int BM>
+static hipError_t launch_down_t(const ForwardParams& p, hipStream_t st) {
+  constexpr int BN = 128;
+  return launch_persistent(down_kernel<T, BM, BN>, lds_bytes<T, BM, BN, 1>(), p, st);
+}
+
+template <typename T>
+static hipError_t dispatch_bm(const ForwardParams& p, int BM, bool up, hipStream_t st) {
+  switch (BM) {
+    case 16: return up ? launch_upgate_t<T, 16>(p, st) : launch_down_t<T, 16>(p, st);
+    case 32: return up ? launch_upgate_t<T, 32>(p, st) : launch_down_t<T, 32>(p, st);
+    case 64: return up ? launch_upgate_t<T, 64>(p, st) : launch_down_t<T, 64>(p, st);
+    case 128: return up ? launch_upgate_t<T, 128>(p, st) : launch_down_t<T, 128>(p, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_forward_upgate(const ForwardParams& p, int dtype, int BM, hipStream_t st) {
+  return dtype == 1 ? dispatch_bm<bf16_t>(p, BM, true, st) : dispatch_bm<float>(p, BM, true, st);
+}
+
+hipError_t launch_forward_down(const ForwardParams& p, int dtype, int BM, hipStream_t st) {
+  return dtype == 1 ? dispatch_bm<bf16_t>(p, BM, false, st) : dispatch_bm<float>(p, BM, false, st);
+}
+
+int forward_lds_ok(int dtype, int BM) {
+  (void)dtype;
+  return BM == 16 || BM == 32 || BM == 64 || BM == 128;
+}
+
+// ------------------------------------------------------- setup and finalize
+// Zero the fp32 accumulator and the task counters (a fill kernel rather than
+// a memset node, so the whole call can be captured in a HIP graph).
+__global__ __launch_bounds__(256) void setup_kernel(float* acc, int64_t n, int* counters) {
+  const int64_t n4 = n / 4;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  const int64_t i0 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  float4* a4 = reinterpret_cast<float4*>(acc);
+  for (int64_t i = i0; i < n4; i += stride) a4[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int64_t i = n4 * 4 + i0; i < n; i += stride) acc[i] = 0.f;
+  if (i0 < kCounterInts) counters[i0] = 0;
+}
+
+hipError_t launch_forward_setup(const ForwardParams& p, int dtype, hipStream_t st) {
+  (void)dtype;
+  const int64_t n = p.S * p.H;
+  int64_t blocks = (n / 4 + 255) / 256;
+  if (blocks < 1) blocks = 1;
+  if (blocks > 4096) blocks = 4096;
+  hipLaunchKernelGGL(setup_kernel, dim3((unsigned)blocks), dim3(256), 0, st, p.Oacc, n, p.counters);
+  return hipGetLastError();
+}
+
+// O = bf16_rne(O_acc), 8 elements per thread step.
+__global__ __launch_bounds__(256) void finalize_kernel(const float* acc, bf16_t* out, int64_t n) {
+  const int64_t n8 = n / 8;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  const int64_t i0 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  for (int64_t i = i0; i < n8; i += stride) {
+    const float4 a = reinterpret_cast<const float4*>(acc)[2 * i];
+    const float4 b = reinterpret_cast<const float4*>(acc)[2 * i + 1];
+    const uint32_t w0 = f32_to_bf16(a.x) | ((uint32_t)f32_to_bf16(a.y) << 16);
+    const uint32_t w1 = f32_to_bf16(a.z) | ((uint32_t)f32_to_bf16(a.w) << 16);
+    const uint32_t w2 = f32_to_bf16(b.x) | ((uint32_t)f32_to_bf16(b.y) << 16);
+    const uint32_t w3 = f32_to_bf16(b.z) | ((uint32_t)f32_to_bf16(b.w) << 16);
+    reinterpret_cast<uint4*>(out)[i] = make_uint4(w0, w1, w2, w3);
+  }
+  for (int64_t i = n8 * 8 + i0; i < n; i += stride) out[i] = f32_to_bf16(acc[i]);
+}
+
+hipError_t launch_forward_finalize(const ForwardParams& p, hipStream_t st) {
+  const int64_t n = p.S * p.H;
+  if (n == 0) return hipSuccess;
+  int64_t blocks = (n / 8 + 255) / 256;
+  if (blocks < 1) blocks = 1;
+  if (blocks > 4096) blocks = 4096;
+  hipLaunchKernelGGL(finalize_kernel, dim3((unsigned)blocks), dim3(256), 0, st, p.Oacc,
+                     reinterpret_cast<bf16_t*>(p.O), n);
+  return hipGetLastError();
+}
+
+}  // namespace moe

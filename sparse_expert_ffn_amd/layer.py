@@ -1,0 +1,67 @@
+"""Device buffers for one MoE layer shape, and the three C-ABI calls in order.
+
+Allocation (torch, device memory) happens once in the constructor; ``run``
+only enqueues moe_gate_topk, moe_align_block_size and moe_forward on the
+stream, so repeated calls allocate nothing.
+"""
+from __future__ import annotations
+
+import torch
+
+from . import (MOE_BF16, make_shape, moe_align_block_size, moe_align_workspace_bytes,
+               moe_forward, moe_forward_workspace_bytes, moe_gate_topk)
+
+
+class MoEBuffers:
+    def __init__(self, S, H, D, E, k, D_shared=0, capacity=0, block_size=128, renormalize=1,
+                 dtype=MOE_BF16, out_f32=False, device="cuda"):
+        self.shape = make_shape(S, H, D, E, k, D_shared, capacity, block_size, renormalize,
+                                dtype, out_f32)
+        self.tdtype = torch.bfloat16 if dtype == MOE_BF16 and not out_f32 else torch.float32
+        dev = torch.device(device)
+        cap = S * k + E * (block_size - 1)
+        i32, f32 = torch.int32, torch.float32
+        self.logits = torch.empty((S, E), dtype=f32, device=dev)
+        self.topk_ids = torch.empty((S, k), dtype=i32, device=dev)
+        self.topk_weights = torch.empty((S, k), dtype=f32, device=dev)
+        self.sorted_ids = torch.empty(max(cap, 1), dtype=i32, device=dev)
+        self.expert_ids = torch.empty(max(cap // block_size, 1), dtype=i32, device=dev)
+        self.ntpp = torch.empty(1, dtype=i32, device=dev)
+        self.expert_counts = torch.empty(E, dtype=i32, device=dev)
+        self.align_ws = torch.empty(max(moe_align_workspace_bytes(self.shape), 1),
+                                    dtype=torch.uint8, device=dev)
+        self.forward_ws = torch.empty(max(moe_forward_workspace_bytes(self.shape), 1),
+                                      dtype=torch.uint8, device=dev)
+        self.O = torch.empty((S, H), dtype=self.tdtype, device=dev)
+
+    def route(self, A=None, W_router=None, router_bias=None, logits_in=None, stream=None):
+        moe_gate_topk(self.shape, A, W_router, router_bias, logits_in, self.logits,
+                      self.topk_ids, self.topk_weights, stream)
+        moe_align_block_size(self.shape, self.topk_ids, self.sorted_ids, self.expert_ids,
+                             self.ntpp, self.expert_counts, self.align_ws, stream)
+
+    def forward(self, A, W_up, W_gate, W_down, Ws_up=None, Ws_gate=None, Ws_down=None,
+                stream=None):
+        moe_forward(self.shape, A, W_up, W_gate, W_down, Ws_up, Ws_gate, Ws_down,
+                    self.topk_weights, self.sorted_ids, self.expert_ids, self.ntpp, self.O,
+                    self.forward_ws, stream)
+        return self.O
+
+    def run(self, A, W_router, W_up, W_gate, W_down, Ws_up=None, Ws_gate=None, Ws_down=None,
+            router_bias=None, logits_in=None, stream=None):
+        """One pass of the whole layer: gate, top-k, align, experts, combine."""
+        self.route(A, W_router, router_bias, logits_in, stream)
+        return self.forward(A, W_up, W_gate, W_down, Ws_up, Ws_gate, Ws_down, stream)
+
+
+def suggest_block_size(S: int, k: int, E: int) -> int:
+    """Rows per sorted block from the mean rows per expert (vLLM's fused_moe
+    note uses 16 / 32 / 64 as the token count grows; 128 for prefill)."""
+    mean = S * k / max(E, 1)
+    if mean <= 16:
+        return 16
+    if mean <= 48:
+        return 32
+    if mean <= 96:
+        return 64
+    return 128

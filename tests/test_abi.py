@@ -1,0 +1,135 @@
+"""The C-ABI library: it loads, exports every entry point include/moe.h
+declares, and rejects bad arguments on the host (no GPU needed: each call
+here returns from argument validation before anything is enqueued)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import sparse_expert_ffn_amd as moe
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+FAKE = 0x100000  # 16-byte aligned address, never dereferenced by these calls
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(moe.LIB_PATH):
+        moe.build()
+    return moe.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert set(names) == set(moe.EXPORTS), names
+    out = subprocess.run(["nm", "-D", "--defined-only", moe.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(line.split()[-1] for line in out.splitlines() if " T " in line)
+    for n in names:
+        assert n in exported, f"{n} not exported"
+        assert hasattr(lib, n)
+
+
+def test_shape_struct_layout():
+    # int64 x 7, int32 x 4 -> 72 bytes, no padding surprises
+    assert ctypes.sizeof(moe.moe_shape) == 72
+
+
+def test_status_strings(lib):
+    for code, name in moe.STATUS.items():
+        assert moe.moe_status_string(code) == name
+    assert moe.moe_status_string(99) == "MOE_ERR_UNKNOWN"
+
+
+def shape(**kw):
+    base = dict(S=64, H=128, D=256, E=8, k=2, D_shared=0, capacity=0, block_size=16,
+                renormalize=1, dtype=moe.MOE_BF16)
+    base.update(kw)
+    return moe.make_shape(**base)
+
+
+def gate(lib, s, **kw):
+    args = dict(A=FAKE, Wr=FAKE, bias=None, lin=None, lout=FAKE, ids=FAKE, w=FAKE)
+    args.update(kw)
+    return lib.moe_gate_topk(ctypes.byref(s) if s is not None else None, args["A"], args["Wr"],
+                             args["bias"], args["lin"], args["lout"], args["ids"], args["w"],
+                             None)
+
+
+def test_gate_topk_validation(lib):
+    assert gate(lib, None) == 1
+    assert gate(lib, shape(k=9)) == 1                   # k > E
+    assert gate(lib, shape(k=0)) == 1
+    assert gate(lib, shape(E=2000, k=2)) == 2           # E > 1024
+    assert gate(lib, shape(E=64, k=33)) == 2            # k > 32
+    assert gate(lib, shape(dtype=7)) == 1
+    assert gate(lib, shape(renormalize=2)) == 1
+    assert gate(lib, shape(), ids=None) == 1
+    assert gate(lib, shape(), lout=None) == 1           # scores need a buffer
+    assert gate(lib, shape(H=100)) == 2                 # H not a multiple of 8
+    assert gate(lib, shape(), A=FAKE + 4) == 2          # misaligned
+    assert gate(lib, shape(S=0), ids=None, w=None) == 0  # empty call
+    s = shape()
+    s.flags = 2
+    assert gate(lib, s) == 1
+
+
+def align(lib, s, ws_bytes=1 << 20, **kw):
+    args = dict(ids=FAKE, si=FAKE, ei=FAKE, n=FAKE, c=FAKE, ws=FAKE)
+    args.update(kw)
+    return lib.moe_align_block_size(ctypes.byref(s), args["ids"], args["si"], args["ei"],
+                                    args["n"], args["c"], args["ws"], ws_bytes, None)
+
+
+def test_align_validation(lib):
+    assert align(lib, shape(block_size=0)) == 1
+    assert align(lib, shape(capacity=-1)) == 1
+    assert align(lib, shape(), si=None) == 1
+    assert align(lib, shape(), ws=None) == 1
+    assert align(lib, shape(), ws_bytes=8) == 3
+    big = shape(S=2**30, k=8, E=256)
+    assert align(lib, big) == 2                         # indices would overflow int32
+
+
+def test_workspace_sizes(lib):
+    for bm in (1, 16, 48, 128):
+        s = shape(block_size=bm)
+        assert moe.moe_align_workspace_bytes(s) > 0
+    assert moe.moe_align_workspace_bytes(shape(k=9)) == 0
+    s = shape(block_size=128, S=16384, H=2048, D=2048, E=64, k=2)
+    f = moe.moe_forward_workspace_bytes(s)
+    # O_acc (fp32) + h rows (bf16), at least
+    assert f >= 16384 * 2048 * 4 + (16384 * 2 + 64 * 127) * 2048 * 2
+    assert moe.moe_forward_workspace_bytes(shape(block_size=48)) == 0  # forward BM set
+    sh = moe.moe_forward_workspace_bytes(shape(D_shared=64))
+    assert sh > moe.moe_forward_workspace_bytes(shape())
+
+
+def fwd(lib, s, ws_bytes=1 << 30, **kw):
+    a = dict(A=FAKE, Wu=FAKE, Wg=FAKE, Wd=FAKE, Su=None, Sg=None, Sd=None, w=FAKE, si=FAKE,
+             ei=FAKE, n=FAKE, O=FAKE, ws=FAKE)
+    a.update(kw)
+    return lib.moe_forward(ctypes.byref(s), a["A"], a["Wu"], a["Wg"], a["Wd"], a["Su"], a["Sg"],
+                           a["Sd"], a["w"], a["si"], a["ei"], a["n"], a["O"], a["ws"], ws_bytes,
+                           None)
+
+
+def test_forward_validation(lib):
+    assert fwd(lib, shape(block_size=48)) == 2
+    assert fwd(lib, shape(D=100)) == 2
+    assert fwd(lib, shape(H=0)) == 1
+    assert fwd(lib, shape(D_shared=64)) == 1            # shared weights missing
+    assert fwd(lib, shape(), Su=FAKE, Sg=FAKE, Sd=FAKE) == 1  # shared weights without D_shared
+    assert fwd(lib, shape(), O=None) == 1
+    assert fwd(lib, shape(), A=FAKE + 2) == 2
+    assert fwd(lib, shape(), ws_bytes=100) == 3
+    assert fwd(lib, shape(S=0), A=None, O=None) == 0    # empty call, nothing enqueued

@@ -1,0 +1,71 @@
+"""GPU moe_align_block_size is bit-exact with the oracle's, for the token
+distributions of the vLLM align-kernel PR (random, alternating empty,
+skewed, mostly empty) and all-to-one, non-power-of-two expert counts and
+block sizes, 16k+ tokens, capacity drops and empty inputs."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import sparse_expert_ffn_amd as moe
+from sparse_expert_ffn_amd import workloads as wk
+from tests.gpu_util import DEV, dev
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def orc():
+    return oracle.default()
+
+
+def align_gpu(ids, E, BM, C):
+    S, k = ids.shape
+    shape = moe.make_shape(S, 8, 8, E, k, capacity=C, block_size=BM)
+    cap = S * k + E * (BM - 1)
+    sorted_ids = torch.full((max(cap, 1),), -7, dtype=torch.int32, device=DEV)
+    expert_ids = torch.full((max(cap // BM, 1),), -7, dtype=torch.int32, device=DEV)
+    ntpp = torch.full((1,), -7, dtype=torch.int32, device=DEV)
+    counts = torch.full((E,), -7, dtype=torch.int32, device=DEV)
+    ws = torch.full((moe.moe_align_workspace_bytes(shape),), 0xAB, dtype=torch.uint8, device=DEV)
+    moe.moe_align_block_size(shape, dev(ids) if ids.size else None, sorted_ids, expert_ids,
+                             ntpp, counts, ws)
+    torch.cuda.synchronize()
+    return (sorted_ids.cpu().numpy(), expert_ids.cpu().numpy(), int(ntpp.item()),
+            counts.cpu().numpy())
+
+
+def check(orc, ids, E, BM, C, tag):
+    si, ei, n, c = align_gpu(ids, E, BM, C)
+    osi, oei, on, oc = orc.align(ids, E, BM, C)
+    assert n == on, f"{tag}: ntpp {n} != {on}"
+    assert np.array_equal(si[:n], osi[:n]), f"{tag}: sorted_ids"
+    assert np.array_equal(ei[: n // BM], oei[: n // BM]), f"{tag}: expert_ids"
+    assert np.array_equal(c, oc), f"{tag}: counts"
+
+
+GRID = [  # (S, k, E, BM, C)
+    (64, 2, 8, 16, 0), (700, 2, 64, 128, 0), (700, 2, 64, 128, 22), (300, 4, 64, 32, 0),
+    (64, 8, 256, 16, 0), (1000, 3, 24, 48, 0), (513, 5, 100, 64, 40), (16384, 2, 64, 128, 512),
+    (16384, 8, 256, 128, 0), (8192, 4, 64, 128, 0), (4097, 8, 1024, 16, 0), (1, 1, 1, 1, 0),
+    (1, 8, 1024, 128, 0), (2000, 1, 7, 1, 0), (3000, 2, 33, 256, 0), (333, 6, 6, 5, 3)]
+
+
+@pytest.mark.parametrize("dist", wk.ID_DISTS)
+@pytest.mark.parametrize("S,k,E,BM,C", GRID)
+def test_align_bitexact(orc, dist, S, k, E, BM, C):
+    ids = wk.draw_topk_ids(S, k, E, dist, seed=S + E)
+    check(orc, ids, E, BM, C, f"{dist} S={S} k={k} E={E} BM={BM} C={C}")
+
+
+def test_align_empty_input(orc):
+    si, ei, n, c = align_gpu(np.zeros((0, 2), np.int32), 8, 16, 0)
+    assert n == 0 and np.all(c == 0)
+
+
+def test_align_repeatable():
+    ids = wk.draw_topk_ids(5000, 4, 100, "skewed", seed=3)
+    a = align_gpu(ids, 100, 64, 0)
+    b = align_gpu(ids, 100, 64, 0)
+    for x, y in zip(a, b):
+        assert np.array_equal(np.asarray(x), np.asarray(y))

@@ -1,0 +1,135 @@
+"""GPU layer forward vs the CPU oracle, element by element, on one shared
+routing (the GPU is fed the oracle's gate scores), at token counts the oracle
+finishes in seconds: every workload, several block sizes, ragged tiles,
+capacity drops, a hot expert, k = E, shared experts, fp32 and bf16, poisoned
+workspaces and outputs."""
+import dataclasses
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from sparse_expert_ffn_amd import workloads as wk
+from tests.gpu_util import DeviceLayer, bf16_output_excess, buffers, dev, host, parity
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def orc():
+    return oracle.default()
+
+
+def run_case(orc, wl, bm=None, li=None, logits=None, poison=True):
+    """Oracle and GPU on one routing. bf16 layers run twice: with an fp32
+    output (the parity bar applies to the fp32-accumulated result) and with a
+    bf16 output (the bar plus that output's own rounding)."""
+    li = li if li is not None else wk.draw_layer(wl)
+    G_o = orc.gate_logits(li.A, li.Wr, li.bias) if logits is None else logits
+    ref = orc.layer(li.A, li.Wr, li.bias, li.W_up, li.W_gate, li.W_down, wl.k,
+                    renormalize=wl.renormalize, capacity=wl.capacity, Ws_up=li.Ws_up,
+                    Ws_gate=li.Ws_gate, Ws_down=li.Ws_down, logits=G_o)
+    L = DeviceLayer(wl, li)
+    outs = {}
+    for out_f32 in ((False,) if wl.dtype == wk.F32 else (True, False)):
+        buf = buffers(wl, bm, out_f32)
+        if poison:
+            buf.forward_ws.fill_(0xFF)   # NaN patterns: any unwritten read shows up
+            buf.align_ws.fill_(0xFF)
+            buf.O.fill_(float("nan"))
+        buf.route(logits_in=dev(G_o))
+        O = L.forward(buf)
+        torch.cuda.synchronize()
+        assert np.array_equal(buf.topk_ids.cpu().numpy(), ref["ids"]), "routing differs"
+        outs[out_f32] = host(O)
+        assert np.all(np.isfinite(outs[out_f32])), "non-finite output"
+    if wl.dtype == wk.F32:
+        err, tol = parity(wl, outs[False], ref["O"])
+        return err, tol, ref, outs[False]
+    err, tol = parity(wl, outs[True], ref["O"])
+    ex = bf16_output_excess(outs[False], ref["O"])
+    assert ex <= 1.0, f"bf16 output beyond bar + own rounding: {ex:.3f}"
+    return err, tol, ref, outs[True]
+
+
+CASES = [("tiny_fp32", 64, 16), ("tiny_fp32", 64, 128), ("prefill_bal", 700, 128),
+         ("prefill_bal", 700, 16), ("prefill_bal", 333, 64), ("prefill_skew", 300, 128),
+         ("prefill_skew", 300, 32), ("decode", 64, 16), ("decode", 64, 128), ("decode", 1, 16)]
+
+
+@pytest.mark.parametrize("name,S,bm", CASES)
+def test_layer_parity(orc, name, S, bm):
+    wl = wk.WORKLOADS[name].with_tokens(S)
+    err, tol, ref, _ = run_case(orc, wl, bm)
+    print(f"{name} S={S} BM={bm}: err {err:.3e} (tol {tol:.0e})")
+    assert err <= tol
+
+
+def _small(dtype, **kw):
+    base = dict(name="small", S=200, H=136, D=200, E=12, k=3, dtype=dtype,
+                router_std=0.5)
+    base.update(kw)
+    return wk.Workload(**base)
+
+
+@pytest.mark.parametrize("dtype", [wk.F32, wk.BF16])
+def test_ragged_tiles_and_shared(orc, dtype):
+    """H, D, D_shared not multiples of the 128-wide tiles; K tails; shared expert."""
+    wl = _small(dtype, D_shared=72)
+    for bm in (16, 64):
+        err, tol, _, _ = run_case(orc, wl, bm)
+        assert err <= tol, f"BM={bm}: {err:.3e}"
+
+
+@pytest.mark.parametrize("dtype", [wk.F32, wk.BF16])
+def test_capacity_drops(orc, dtype):
+    wl = _small(dtype, capacity_factor=0.25)
+    assert 0 < wl.capacity < 50
+    err, tol, ref, _ = run_case(orc, wl, 32)
+    assert ref["kept"] is not None and ref["kept"].sum() < wl.S * wl.k
+    assert err <= tol
+
+
+def test_hot_expert_and_empty_experts(orc):
+    """Every token picks expert 5 first: one expert holds S rows (many m-blocks),
+    most experts are empty."""
+    wl = _small(wk.BF16, S=1500, E=40, k=2)
+    li = wk.draw_layer(wl)
+    rng = np.random.default_rng(0)
+    G = rng.standard_normal((wl.S, wl.E)).astype(np.float32)
+    G[:, 5] += 50.0
+    G[:, 9] += 10.0 * (rng.random(wl.S) > 0.5)
+    err, tol, ref, _ = run_case(orc, wl, 128, li=li, logits=G)
+    assert err <= tol
+
+
+def test_k_equals_E(orc):
+    wl = _small(wk.BF16, S=130, E=4, k=4)
+    err, tol, _, _ = run_case(orc, wl, 64)
+    assert err <= tol
+
+
+def test_all_dropped_but_shared(orc):
+    """Capacity 1 on a tiny layer: most tokens get only the shared expert."""
+    wl = _small(wk.F32, S=64, E=2, k=1, D_shared=16, capacity_factor=1.0 / 32)
+    assert wl.capacity == 1
+    err, tol, _, _ = run_case(orc, wl, 16)
+    assert err <= tol
+
+
+def test_repeat_calls_same_buffers(orc):
+    """Two forward passes on the same buffers give the same routing and an
+    output within the bar (fp32 atomics may reorder the combine's sums)."""
+    wl = wk.WORKLOADS["prefill_skew"].with_tokens(200)
+    li = wk.draw_layer(wl)
+    L = DeviceLayer(wl, li)
+    buf = buffers(wl, 64)
+    G = orc.gate_logits(li.A, li.Wr, li.bias)
+    outs = []
+    for _ in range(2):
+        buf.route(logits_in=dev(G))
+        outs.append(host(L.forward(buf)).copy())
+    torch.cuda.synchronize()
+    assert np.max(np.abs(outs[0] - outs[1])) <= 1e-2 * np.sqrt(np.mean(outs[0] ** 2))

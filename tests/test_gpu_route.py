@@ -1,0 +1,92 @@
+"""GPU parity of the routing steps: gate scores (tolerance), softmax top-k
+(bit-exact when fed the oracle's scores) and their edge cases."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import sparse_expert_ffn_amd as moe
+from sparse_expert_ffn_amd import workloads as wk
+from tests.gpu_util import DEV, buffers, dev, rms
+
+pytestmark = pytest.mark.gpu
+
+# each workload at a token count the oracle finishes in seconds (ragged sizes)
+CASES = [("tiny_fp32", 64), ("prefill_bal", 700), ("prefill_skew", 300), ("decode", 64),
+         ("dsv3", 100)]
+
+
+@pytest.fixture(scope="module")
+def orc():
+    return oracle.default()
+
+
+@pytest.mark.parametrize("name,S", CASES)
+def test_gate_scores(orc, name, S):
+    wl = wk.WORKLOADS[name].with_tokens(S)
+    A, Wr, bias = wk.draw_routing_inputs(wl)
+    G_o = orc.gate_logits(A, Wr, bias)
+    buf = buffers(wl)
+    moe.moe_gate_topk(buf.shape, dev(A), dev(Wr), dev(bias), None, buf.logits, buf.topk_ids,
+                      buf.topk_weights)
+    torch.cuda.synchronize()
+    G = buf.logits.cpu().numpy()
+    err = float(np.max(np.abs(G.astype(np.float64) - G_o)) / rms(G_o))
+    assert err <= 1e-4, f"{name}: gate scores max err / RMS = {err:.3e}"
+
+
+def _topk_gpu(G, k, renormalize, dtype=wk.BF16):
+    S, E = G.shape
+    shape = moe.make_shape(S, 8, 8, E, k, renormalize=renormalize, block_size=16, dtype=dtype)
+    ids = torch.empty((S, k), dtype=torch.int32, device=DEV)
+    w = torch.empty((S, k), dtype=torch.float32, device=DEV)
+    out = torch.empty((S, E), dtype=torch.float32, device=DEV)
+    moe.moe_gate_topk(shape, None, None, None, dev(G), out, ids, w)
+    torch.cuda.synchronize()
+    assert np.array_equal(out.cpu().numpy(), G), "logits_out must copy logits_in"
+    return ids.cpu().numpy(), w.cpu().numpy()
+
+
+@pytest.mark.parametrize("name,S", CASES)
+def test_topk_bitexact_on_oracle_scores(orc, name, S):
+    wl = wk.WORKLOADS[name].with_tokens(S)
+    A, Wr, bias = wk.draw_routing_inputs(wl)
+    G_o = orc.gate_logits(A, Wr, bias)
+    ids_o, w_o = orc.topk_softmax(G_o, wl.k, wl.renormalize)
+    ids, w = _topk_gpu(G_o, wl.k, wl.renormalize)
+    assert np.array_equal(ids, ids_o), f"{name}: top-k ids differ"
+    assert np.array_equal(w.view(np.uint32), w_o.view(np.uint32)), f"{name}: weights differ"
+
+
+@pytest.mark.parametrize("E,k", [(1, 1), (3, 3), (8, 2), (100, 7), (256, 8), (1024, 32),
+                                 (1000, 1), (65, 32)])
+@pytest.mark.parametrize("renorm", [0, 1])
+def test_topk_edge_shapes(orc, E, k, renorm):
+    rng = np.random.default_rng(E * 100 + k)
+    G = (rng.standard_normal((37, E)) * 2).astype(np.float32)
+    ids_o, w_o = orc.topk_softmax(G, k, renorm)
+    ids, w = _topk_gpu(G, k, renorm)
+    assert np.array_equal(ids, ids_o)
+    assert np.array_equal(w.view(np.uint32), w_o.view(np.uint32))
+
+
+def test_topk_ties(orc):
+    rng = np.random.default_rng(5)
+    G = rng.integers(-2, 3, size=(200, 64)).astype(np.float32)  # many exact ties
+    G[:5] = 0.0                                                  # all equal
+    G[5, :] = -0.0
+    G[5, 7] = 0.0                                                # -0 and +0 compare equal
+    for k in (1, 4, 17, 32):
+        ids_o, w_o = orc.topk_softmax(G, k, 1)
+        ids, w = _topk_gpu(G, k, 1)
+        assert np.array_equal(ids, ids_o), f"k={k}"
+        assert np.array_equal(w.view(np.uint32), w_o.view(np.uint32))
+
+
+def test_topk_fp32_mode_and_empty(orc):
+    G = np.random.default_rng(1).standard_normal((5, 8)).astype(np.float32)
+    ids_o, w_o = orc.topk_softmax(G, 2, 1)
+    ids, w = _topk_gpu(G, 2, 1, dtype=wk.F32)
+    assert np.array_equal(ids, ids_o)
+    shape = moe.make_shape(0, 8, 8, 8, 2)
+    assert moe.moe_gate_topk(shape, None, None, None, None, None, None, None) == 0
