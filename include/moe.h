@@ -112,8 +112,8 @@ typedef struct {
  *   logits_out   [S][E]   fp32: receives the scores used. Required when
  *                         logits_in is NULL (it is the GEMM's output buffer);
  *                         optional (a copy of logits_in) otherwise.
- * The GEMM path requires H a multiple of 8 and 16-byte aligned A and
- * W_router (else MOE_ERR_UNSUPPORTED).
+ * The GEMM path requires H a multiple of 8, 16-byte aligned A and W_router,
+ * and each of them under 2 GiB (else MOE_ERR_UNSUPPORTED).
  *   topk_ids     [S][k]   int32 out
  *   topk_weights [S][k]   fp32 out
  */
@@ -188,8 +188,9 @@ size_t moe_forward_workspace_bytes(const moe_shape* shape);
  *                                 outputs for this shape
  *   O         [S][H]              dtype out (fp32 with MOE_OUTPUT_F32)
  *   workspace >= moe_forward_workspace_bytes(shape) bytes, any contents
- * Requires H, D, D_shared multiples of 8 and block_size in {16,32,64,128}
- * (else MOE_ERR_UNSUPPORTED).
+ * Requires H, D, D_shared multiples of 8, block_size in {16,32,64,128}, 16-byte
+ * aligned arrays, and each of A, one expert's weight matrix and the workspace's
+ * SwiGLU rows under 2 GiB (else MOE_ERR_UNSUPPORTED).
  */
 moe_status moe_forward(const moe_shape* shape, const void* A, const void* W_up,
                        const void* W_gate, const void* W_down, const void* Ws_up,

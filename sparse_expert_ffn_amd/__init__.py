@@ -19,7 +19,10 @@ __all__ = ["MOE_F32", "MOE_BF16", "MoeError", "moe_shape", "make_shape", "load_l
            "moe_forward_workspace_bytes", "moe_forward", "moe_status_string",
            "moe_profile_enable", "moe_profile_collect", "build", "LIB_PATH", "STATUS"]
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe.so")
+# SPARSE_EXPERT_FFN_LIB: load the library from another path (e.g. a build
+# with different compile-time tile settings)
+LIB_PATH = os.environ.get("SPARSE_EXPERT_FFN_LIB") or os.path.join(
+    os.path.dirname(os.path.abspath(__file__)), "libmoe.so")
 
 MOE_F32 = 0
 MOE_BF16 = 1

@@ -8,7 +8,7 @@ import sys
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
-LIB = os.path.join(PKG, "libmoe.so")
+LIB = os.path.join(PKG, "libmoe.so")  # the build() target (not SPARSE_EXPERT_FFN_LIB)
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [

@@ -18,6 +18,9 @@ size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
+// below 2 GiB: addressable by one raw buffer resource
+bool fits_buffer(int64_t bytes) { return bytes >= 0 && bytes < ((int64_t)1 << 31); }
+
 moe_status check_routing_dims(const moe_shape* s) {
   if (s == nullptr) return MOE_ERR_INVALID_ARGUMENT;
   if (s->flags != 0 && s->flags != MOE_OUTPUT_F32) return MOE_ERR_INVALID_ARGUMENT;
@@ -44,7 +47,15 @@ moe_status check_forward_dims(const moe_shape* s) {
   if (s->H < 1 || s->D < 1 || s->D_shared < 0) return MOE_ERR_INVALID_ARGUMENT;
   if (s->H % 8 || s->D % 8 || s->D_shared % 8) return MOE_ERR_UNSUPPORTED;
   if (!forward_lds_ok(s->dtype, s->block_size)) return MOE_ERR_UNSUPPORTED;
-  if (s->S > (int64_t)INT32_MAX) return MOE_ERR_UNSUPPORTED;
+  // the kernels address A, each expert's weight matrices and the SwiGLU rows
+  // through 32-bit buffer offsets: each must stay below 2 GiB
+  const int64_t es = s->dtype == MOE_BF16 ? 2 : 4;
+  const int64_t BM = s->block_size;
+  const int64_t cap_rows = (s->S * s->k + s->E * (BM - 1) + BM - 1) / BM * BM;
+  if (!fits_buffer(s->S * s->H * es) || !fits_buffer(s->H * s->D * es) ||
+      !fits_buffer(s->H * s->D_shared * es) || !fits_buffer(cap_rows * s->D * es) ||
+      !fits_buffer(((s->S + BM - 1) / BM * BM) * s->D_shared * es))
+    return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
 }
 
@@ -155,6 +166,9 @@ moe_status moe_gate_topk(const moe_shape* shape, const void* A, const void* W_ro
     if (A == nullptr || W_router == nullptr || logits_out == nullptr) return MOE_ERR_INVALID_ARGUMENT;
     if (shape->H < 1) return MOE_ERR_INVALID_ARGUMENT;
     if (shape->H % 8 || !aligned16(A) || !aligned16(W_router)) return MOE_ERR_UNSUPPORTED;
+    const int64_t es = shape->dtype == MOE_BF16 ? 2 : 4;
+    if (!fits_buffer(shape->S * shape->H * es) || !fits_buffer(shape->H * shape->E * es))
+      return MOE_ERR_UNSUPPORTED;
     G = logits_out;
   }
   hipStream_t hs = reinterpret_cast<hipStream_t>(stream);

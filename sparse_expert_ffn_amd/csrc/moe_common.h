@@ -38,7 +38,11 @@ __device__ __forceinline__ float from_f32<float>(float x) { return x; }
 template <>
 __device__ __forceinline__ bf16_t from_f32<bf16_t>(float x) { return f32_to_bf16(x); }
 
-__device__ __forceinline__ float silu_f32(float u) { return u / (1.0f + __expf(-u)); }
+// SiLU(u) = u / (1 + exp(-u)); v_exp_f32 and v_rcp_f32 (about 1 ulp each).
+// exp overflows to +inf for u < -88, where rcp(inf) = 0 gives the -0 limit.
+__device__ __forceinline__ float silu_f32(float u) {
+  return u * __builtin_amdgcn_rcpf(1.0f + __expf(-u));
+}
 
 // ---------------------------------------------------------------- launchers
 // Host-side launch helpers implemented in the .hip sources; each returns the

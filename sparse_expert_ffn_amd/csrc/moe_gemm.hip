@@ -28,22 +28,21 @@ constexpr int kGateBN = 64;
 // ------------------------------------------------------------------ gate GEMM
 // G[s][e] = sum_h A[s][h] * Wr[h][e] (+ bias[e]), fp32 out. One tile per
 // workgroup (not persistent: the gate has no routing-dependent imbalance).
-template <typename T>
+template <typename T, bool RAGGED>
 __global__ __launch_bounds__(256) void gate_gemm_kernel(GateParams p) {
-  using TG = TileGemm<T, kGateBM, kGateBN, 1>;
+  using TG = TileGemm<T, kGateBM, kGateBN, 1, RAGGED>;
   __shared__ __align__(16) char smem[TG::LDS_BYTES];
   const int64_t n_tiles = (p.E + kGateBN - 1) / kGateBN;
   const int64_t m0 = (int64_t)(blockIdx.x / n_tiles) * kGateBM;
   const int64_t n0 = (int64_t)(blockIdx.x % n_tiles) * kGateBN;
   TG g;
-  const char* Ab = reinterpret_cast<const char*>(p.A);
-  const char* Bm[1] = {reinterpret_cast<const char*>(p.Wr) + (size_t)n0 * sizeof(T)};
+  const char* Bm[1] = {reinterpret_cast<const char*>(p.Wr)};
   const int64_t S = p.S, H = p.H;
-  g.setup([&](int r) -> const char* {
+  g.setup(p.A, (uint32_t)(S * H * sizeof(T)), [&](int r) -> uint32_t {
     const int64_t s = m0 + r;
-    return s < S ? Ab + (size_t)s * H * sizeof(T) : nullptr;
-  }, Bm, p.E, p.E - n0);
-  g.mainloop(smem, p.H, p.E, p.E - n0);
+    return s < S ? (uint32_t)(s * H * sizeof(T)) : kOob;
+  }, Bm, (uint32_t)(H * p.E * sizeof(T)), p.E, n0, p.E - n0);
+  g.mainloop(smem, p.H);
   g.for_each([&](int, int row, int col, float v) {
     const int64_t s = m0 + row, e = n0 + col;
     if (s < p.S && e < p.E) {
@@ -57,10 +56,18 @@ __global__ __launch_bounds__(256) void gate_gemm_kernel(GateParams p) {
 hipError_t launch_gate(const GateParams& p, int dtype, hipStream_t st) {
   if (p.S == 0) return hipSuccess;
   const int64_t tiles = ((p.S + kGateBM - 1) / kGateBM) * ((p.E + kGateBN - 1) / kGateBN);
-  if (dtype == 1)
-    hipLaunchKernelGGL(gate_gemm_kernel<bf16_t>, dim3((unsigned)tiles), dim3(256), 0, st, p);
-  else
-    hipLaunchKernelGGL(gate_gemm_kernel<float>, dim3((unsigned)tiles), dim3(256), 0, st, p);
+  const bool ragged = (p.E % 8) != 0;
+  if (dtype == 1) {
+    if (ragged)
+      hipLaunchKernelGGL((gate_gemm_kernel<bf16_t, true>), dim3((unsigned)tiles), dim3(256), 0, st, p);
+    else
+      hipLaunchKernelGGL((gate_gemm_kernel<bf16_t, false>), dim3((unsigned)tiles), dim3(256), 0, st, p);
+  } else {
+    if (ragged)
+      hipLaunchKernelGGL((gate_gemm_kernel<float, true>), dim3((unsigned)tiles), dim3(256), 0, st, p);
+    else
+      hipLaunchKernelGGL((gate_gemm_kernel<float, false>), dim3((unsigned)tiles), dim3(256), 0, st, p);
+  }
   return hipGetLastError();
 }
 
@@ -119,7 +126,7 @@ __device__ __forceinline__ TaskSpace task_space(const ForwardParams& p, int BM, 
 // Ws_gate into hs.
 template <typename T, int BM, int BN>
 __global__ __launch_bounds__(256, 1) void upgate_kernel(ForwardParams p) {
-  using TG = TileGemm<T, BM, BN, 2>;
+  using TG = TileGemm<T, BM, BN, 2, false, 2>;
   extern __shared__ __align__(16) char smem[];
   __shared__ int64_t s_task;
   __shared__ int s_tok[BM];
@@ -155,27 +162,29 @@ __global__ __launch_bounds__(256, 1) void upgate_kernel(ForwardParams p) {
     const char* Bm[2];
     if (!shared) {
       const int64_t e = p.expert_ids[b];
-      const size_t off = ((size_t)e * p.H * p.D + n0) * sizeof(T);
+      const size_t off = (size_t)e * p.H * p.D * sizeof(T);
       Bm[0] = reinterpret_cast<const char*>(p.Wu) + off;
       Bm[1] = reinterpret_cast<const char*>(p.Wg) + off;
     } else {
-      Bm[0] = reinterpret_cast<const char*>(p.Wsu) + n0 * sizeof(T);
-      Bm[1] = reinterpret_cast<const char*>(p.Wsg) + n0 * sizeof(T);
+      Bm[0] = reinterpret_cast<const char*>(p.Wsu);
+      Bm[1] = reinterpret_cast<const char*>(p.Wsg);
     }
-    const char* Ab = reinterpret_cast<const char*>(p.A);
     const int64_t H = p.H;
-    g.setup([&](int r) -> const char* {
+    g.setup(p.A, (uint32_t)(p.S * H * sizeof(T)), [&](int r) -> uint32_t {
       const int tok = s_tok[r];
-      return tok >= 0 ? Ab + (size_t)tok * H * sizeof(T) : nullptr;
-    }, Bm, N, N - n0);
-    g.mainloop(smem, p.H, N, N - n0);
+      return tok >= 0 ? (uint32_t)((int64_t)tok * H * sizeof(T)) : kOob;
+    }, Bm, (uint32_t)(H * N * sizeof(T)), N, n0, N - n0);
+    g.mainloop(smem, p.H);
     T* out = reinterpret_cast<T*>(shared ? p.hs : p.h);
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int wm0 = (wave / TG::WN) * (BM / TG::WM);
     const int wn0 = (wave % TG::WN) * (BN / TG::WN);
 #pragma unroll
-    for (int i = 0; i < TG::MI; ++i)
+    for (int i = 0; i < TG::MI; ++i) {
+      // one 16-row block at a time: keeps the accumulator reads from being
+      // hoisted into VGPRs all at once
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int jj = 0; jj < TG::NI; ++jj)
 #pragma unroll
@@ -188,6 +197,7 @@ __global__ __launch_bounds__(256, 1) void upgate_kernel(ForwardParams p) {
             out[(size_t)(b * BM + row) * N + col] = from_f32<T>(silu_f32(u) * gv);
           }
         }
+    }
   }
 }
 
@@ -240,16 +250,17 @@ __global__ __launch_bounds__(256, 1) void down_kernel(ForwardParams p) {
     const char* Bm[1];
     if (!shared) {
       const int64_t e = p.expert_ids[b];
-      Bm[0] = reinterpret_cast<const char*>(p.Wd) + ((size_t)e * p.D * p.H + n0) * sizeof(T);
+      Bm[0] = reinterpret_cast<const char*>(p.Wd) + (size_t)e * p.D * p.H * sizeof(T);
     } else {
-      Bm[0] = reinterpret_cast<const char*>(p.Wsd) + n0 * sizeof(T);
+      Bm[0] = reinterpret_cast<const char*>(p.Wsd);
     }
+    // this m-block's BM rows of h (or hs), K-contiguous
     const char* Ab = reinterpret_cast<const char*>(shared ? p.hs : p.h) +
                      (size_t)b * BM * K * sizeof(T);
-    g.setup([&](int r) -> const char* {
-      return s_tok[r] >= 0 ? Ab + (size_t)r * K * sizeof(T) : nullptr;
-    }, Bm, p.H, p.H - n0);
-    g.mainloop(smem, K, p.H, p.H - n0);
+    g.setup(Ab, (uint32_t)(BM * K * sizeof(T)), [&](int r) -> uint32_t {
+      return s_tok[r] >= 0 ? (uint32_t)(r * K * sizeof(T)) : kOob;
+    }, Bm, (uint32_t)(K * p.H * sizeof(T)), p.H, n0, p.H - n0);
+    g.mainloop(smem, K);
     float* O = p.Oacc;
     const int64_t H = p.H;
     g.for_each([&](int, int row, int col, float v) {
@@ -292,15 +303,21 @@ static hipError_t launch_persistent(K kernel, int lds, const ForwardParams& p, h
   return hipGetLastError();
 }
 
+// Output tile width per weight matrix (up/gate: 2 matrices share the A tile).
+template <int BM>
+constexpr int upgate_bn() { return 128; }
+template <int BM>
+constexpr int down_bn() { return 128; }
+
 template <typename T, int BM>
 static hipError_t launch_upgate_t(const ForwardParams& p, hipStream_t st) {
-  constexpr int BN = 128;
+  constexpr int BN = upgate_bn<BM>();
   return launch_persistent(upgate_kernel<T, BM, BN>, lds_bytes<T, BM, BN, 2>(), p, st);
 }
 
 template <typename T, int BM>
 static hipError_t launch_down_t(const ForwardParams& p, hipStream_t st) {
-  constexpr int BN = 128;
+  constexpr int BN = down_bn<BM>();
   return launch_persistent(down_kernel<T, BM, BN>, lds_bytes<T, BM, BN, 1>(), p, st);
 }
 
