@@ -1,0 +1,282 @@
+// One workgroup's bf16 output tile of C_m = A . B_m (m < NB) on gfx950, with
+// both operands loaded straight from global memory into LDS.
+//
+// 256 threads (4 wave64s), tile BM rows x BN (= 128) columns per weight
+// matrix, K stages of 64 elements, NSTAGE = 3 LDS stages.
+//
+//  - global -> LDS: buffer_load_dwordx4 with the lds bit (16 bytes per lane;
+//    lane l's bytes land at the LDS base in M0 + 16 l). No staging registers,
+//    no register transpose, no LDS store instructions.
+//    Zero rows, rows past K and columns past N use out-of-range offsets: the
+//    hardware writes zeros.
+//  - A in LDS: BM rows of 128 bytes, 16-byte chunk c of row r stored in slot
+//    c ^ key(r), key(r) = (r & 7) ^ ((r >> 3) & 1): the 16 rows one operand
+//    read touches land in 16 different 16-byte bank windows.
+//  - B in LDS: each matrix as [64 k-rows][BN columns], N-contiguous as in
+//    memory (256 bytes per row); its 32-byte column pairs are XOR-swizzled by
+//    g(k) = (k & 3) | ((k >> 3) & 1) << 2 so the 16 k-rows one transposed read
+//    touches fall in 8 different pair slots.
+//  - A operand: one ds_read_b128 per 16x32 block (lane l: row l % 16, K
+//    elements 8 (l / 16) .. +7).
+//  - B operand: two ds_read_b64_tr_b16 per 32x16 block. Within each 16-lane
+//    group, lane i receives element i % 4 of the 8-byte chunks addressed by
+//    lanes i/4, i/4 + 4, i/4 + 8, i/4 + 12 of its group. With lane i of group
+//    g addressing k-row k0 + 8g + i/4 and columns n0 + 4 (i % 4) .. +3, lane i
+//    receives column n0 + i at k-rows k0 + 8g .. +3: the MFMA B operand layout
+//    (column l % 16, K elements 8 (l / 16) .. +7) after the second read at
+//    k-rows + 4.
+//  - v_mfma_f32_16x16x32_bf16, fp32 accumulators (lane l: column l % 16, rows
+//    4 (l / 16) .. +3 of each 16x16 block).
+//  - Pipeline: stage kt+2's loads are issued right after the barrier that
+//    makes stage kt visible; each wave waits (vmcnt) only for its own stage-kt
+//    loads, then one barrier per stage.
+#pragma once
+
+#include "gemm_tile.h"
+
+namespace moe {
+
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+
+// Raw buffer descriptor (gfx9): base[47:0], stride 0, num_records = bytes,
+// dword3 0x00020000. Built from wave-uniform values so it lives in SGPRs.
+__device__ __forceinline__ i32x4_t make_srd(const void* base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  i32x4_t r;
+  r.x = (int)(uint32_t)a;
+  r.y = (int)((a >> 32) & 0xFFFFu);
+  r.z = (int)bytes;
+  r.w = 0x00020000;
+  return r;
+}
+
+// 16 bytes per lane from buffer `srd` at byte offset voff into LDS at
+// lds_dst + 16 * lane (lds_dst wave-uniform, set through M0). Written as a
+// one-instruction asm block so that the compiler does not add a wait for it in
+// front of later LDS reads of other stage buffers: the K loop orders these
+// loads itself (vmcnt wait on the issuing wave, then a workgroup barrier).
+// The instruction has no register result.
+__device__ __forceinline__ void dma16(i32x4_t srd, uint32_t voff, const void* lds_dst) {
+  const uint32_t m0v = (uint32_t)reinterpret_cast<uintptr_t>(
+      (const __attribute__((address_space(3))) char*)lds_dst);
+  asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(srd), "{m0}"(m0v)
+               : "memory");
+}
+
+// s_waitcnt with vmcnt <= n, expcnt and lgkmcnt unconstrained (gfx9 encoding:
+// vmcnt[3:0], expcnt[6:4], lgkmcnt[11:8], vmcnt[5:4] in bits [15:14]).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+template <int BM_, int NB_>
+struct TileGemmDirect {
+  static constexpr int BM = BM_, BN = 128, NB = NB_;
+  static constexpr int ES = 2;
+  static constexpr int BK = 64;
+  static constexpr int NSTAGE = 3;
+  static constexpr int A_ROWB = 128;
+  static constexpr int B_ROWB = BN * ES;          // 256
+  static constexpr int A_LDS = BM * A_ROWB;
+  static constexpr int B_MAT = BK * B_ROWB;        // 16 KB per matrix per stage
+  static constexpr int B_LDS = NB * B_MAT;
+  static constexpr int STAGE = A_LDS + B_LDS;
+  static constexpr int LDS_BYTES = NSTAGE * STAGE;  // three __shared__ arrays of STAGE bytes
+  static constexpr int WM = BM >= 32 ? 2 : 1;
+  static constexpr int WN = 4 / WM;
+  static constexpr int MI = BM / WM / 16;
+  static constexpr int NI = BN / WN / 16;
+  static constexpr int KSTEPS = BK / 32;
+  // 1 KB (one wave instruction) units per stage
+  static constexpr int A_INSTR = A_LDS / 1024;
+  static constexpr int B_INSTR = B_LDS / 1024;
+  static constexpr int A_PW = (A_INSTR + 3) / 4;   // per wave (upper bound)
+  static constexpr int B_PW = B_INSTR / 4;
+  // loads every wave issues per stage (waves with fewer A units wait for less)
+  static constexpr int MIN_PW = A_INSTR / 4 + B_PW;
+  static_assert(B_INSTR % 4 == 0, "B loads split evenly over the waves");
+  static_assert(MI >= 1 && NI >= 1, "tile too small for four waves");
+  static_assert(LDS_BYTES <= 160 * 1024, "LDS");
+
+  f32x4_t acc[NB][MI][NI];
+  uint32_t aoff[A_PW];   // per-lane A row byte offset + logical chunk (kOob = zero)
+  uint32_t boff[B_PW];   // per-lane B offset at k-stage 0 (kOob = zero column strip)
+  i32x4_t rsrc_a;
+  i32x4_t rsrc_b[NB];
+  uint32_t b_stage_bytes;  // BK * ldb * ES
+  int64_t K_;
+
+  __device__ __forceinline__ static int bswz(int k) { return (k & 3) | (((k >> 3) & 1) << 2); }
+  __device__ __forceinline__ static int aswz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+
+  __device__ __forceinline__ void zero_acc() {
+#pragma unroll
+    for (int m = 0; m < NB; ++m)
+#pragma unroll
+      for (int i = 0; i < MI; ++i)
+#pragma unroll
+        for (int j = 0; j < NI; ++j) acc[m][i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
+
+  template <typename RowOff>
+  __device__ __forceinline__ void setup(const void* a_base, uint32_t a_bytes, RowOff row_off,
+                                        const char* const* B, uint32_t b_bytes, int64_t ldb,
+                                        int64_t n0, int64_t ncols) {
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    rsrc_a = make_srd(a_base, a_bytes);
+#pragma unroll
+    for (int m = 0; m < NB; ++m) rsrc_b[m] = make_srd(B[m], b_bytes);
+    b_stage_bytes = (uint32_t)(BK * ldb * ES);
+#pragma unroll
+    for (int t = 0; t < A_PW; ++t) {
+      const int q = wave + 4 * t;  // A instruction index: rows 8q .. 8q + 7
+      uint32_t o = kOob;
+      if (q < A_INSTR) {
+        const int r = 8 * q + (lane >> 3);
+        const int c = (lane & 7) ^ aswz(r);  // logical chunk stored in this lane's slot
+        const uint32_t ro = row_off(r);
+        if (ro != kOob) o = ro + c * 16;
+      }
+      aoff[t] = o;
+    }
+#pragma unroll
+    for (int t = 0; t < B_PW; ++t) {
+      const int q = wave + 4 * t;                 // B instruction index
+      const int kr = (q % (B_MAT / 1024)) * 4 + (lane >> 4);  // k-row in the stage
+      const int pc = lane & 15;                   // physical 16-byte chunk in the row
+      const int c = (((pc >> 1) ^ bswz(kr)) << 1) | (pc & 1);  // logical chunk
+      const bool ok = (int64_t)c * 8 + 8 <= ncols;
+      boff[t] = ok ? (uint32_t)(((int64_t)kr * ldb + n0 + c * 8) * ES) : kOob;
+    }
+  }
+
+  // Issue the LDS-direct loads of K stage kt into the stage buffer `base`.
+  __device__ __forceinline__ void issue_stage(char* base, int kt) {
+    // wave-uniform (scalar) so the buffer resources stay in SGPRs
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t k0 = (int64_t)kt * BK;
+#pragma unroll
+    for (int t = 0; t < A_PW; ++t) {
+      const int q = wave + 4 * t;
+      if (q < A_INSTR) {  // wave-uniform
+        const int lane = threadIdx.x & 63;
+        const int r = 8 * q + (lane >> 3);
+        const int c = (lane & 7) ^ aswz(r);
+        const uint32_t o = (aoff[t] != kOob && k0 + c * 8 < K_) ? aoff[t] + (uint32_t)(k0 * ES)
+                                                                : kOob;
+        dma16(rsrc_a, o, base + q * 1024);
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < B_PW; ++t) {
+      const int q = wave + 4 * t;
+      const int m = q / (B_MAT / 1024);  // wave-uniform
+      const uint32_t o = boff[t] == kOob ? kOob : boff[t] + (uint32_t)kt * b_stage_bytes;
+      i32x4_t rb = rsrc_b[0];
+      if constexpr (NB > 1) {
+        if (m == 1) rb = rsrc_b[1];
+      }
+      dma16(rb, o, base + A_LDS + q * 1024);
+    }
+  }
+
+  __device__ __forceinline__ void compute_stage(const char* base) {
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int wm0 = (wave / WN) * (BM / WM);
+    const int wn0 = (wave % WN) * (BN / WN);
+    const int lr = lane & 15;
+    const int lg = lane >> 4;
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks) {
+      uint4 a[MI];
+#pragma unroll
+      for (int i = 0; i < MI; ++i) {
+        const int r = wm0 + i * 16 + lr;
+        const int c = ks * 4 + lg;
+        a[i] = *reinterpret_cast<const uint4*>(base + r * A_ROWB + ((c ^ aswz(r)) << 4));
+      }
+      uint4 b[NB][NI];
+#pragma unroll
+      for (int m = 0; m < NB; ++m)
+#pragma unroll
+        for (int j = 0; j < NI; ++j) {
+          i16x4_t h[2];
+#pragma unroll
+          for (int hh = 0; hh < 2; ++hh) {
+            const int k = ks * 32 + 8 * lg + 4 * hh + (lr >> 2);
+            const int n = wn0 + j * 16 + 4 * (lr & 3);
+            const int c = n >> 3;
+            const int pc = ((((c >> 1) ^ bswz(k)) << 1) | (c & 1));
+            const char* p = base + A_LDS + m * B_MAT + k * B_ROWB + (pc << 4) + ((n & 4) << 1);
+            h[hh] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) i16x4_t*)(p));
+          }
+          b[m][j] = __builtin_bit_cast(uint4, h);
+        }
+#pragma unroll
+      for (int m = 0; m < NB; ++m)
+#pragma unroll
+        for (int i = 0; i < MI; ++i)
+#pragma unroll
+          for (int j = 0; j < NI; ++j)
+            acc[m][i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                __builtin_bit_cast(bf16x8_t, a[i]), __builtin_bit_cast(bf16x8_t, b[m][j]),
+                acc[m][i][j], 0, 0, 0);
+    }
+  }
+
+  // One K step: stage kt is in `cur`; `nxt2` (the buffer stage kt-1 used)
+  // receives stage kt+2.
+  __device__ __forceinline__ void step(const char* cur, char* nxt2, int kt) {
+    wait_vmcnt<MIN_PW>();  // this wave's stage-kt loads have landed
+    __syncthreads();        // ... and every wave's; stage kt-1 reads are done
+    issue_stage(nxt2, kt + 2);
+    compute_stage(cur);
+  }
+
+  // Full K loop over the three stage buffers (distinct LDS objects, so the
+  // compiler can see that the loads in flight never write the buffer being
+  // read and needs no wait for them). Stages past the end of K are issued too
+  // (they load zeros without memory traffic) so every step has the same
+  // loads in flight.
+  __device__ __forceinline__ void mainloop(char* s0, char* s1, char* s2, int64_t K) {
+    zero_acc();
+    K_ = K;
+    const int nk = (int)((K + BK - 1) / BK);
+    if (nk <= 0) return;
+    wait_vmcnt<0>();  // nothing of an earlier tile still writing LDS
+    __syncthreads();
+    issue_stage(s0, 0);
+    issue_stage(s1, 1);
+    for (int kt = 0; kt < nk; kt += 3) {
+      step(s0, s2, kt);
+      if (kt + 1 < nk) step(s1, s0, kt + 1);
+      if (kt + 2 < nk) step(s2, s1, kt + 2);
+    }
+    wait_vmcnt<0>();
+  }
+
+  template <typename F>
+  __device__ __forceinline__ void for_each(F f) const {
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int wm0 = (wave / WN) * (BM / WM);
+    const int wn0 = (wave % WN) * (BN / WN);
+#pragma unroll
+    for (int m = 0; m < NB; ++m)
+#pragma unroll
+      for (int i = 0; i < MI; ++i)
+#pragma unroll
+        for (int j = 0; j < NI; ++j)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            f(m, wm0 + i * 16 + (lane >> 4) * 4 + r, wn0 + j * 16 + (lane & 15), acc[m][i][j][r]);
+  }
+};
+
+}  // namespace moe

@@ -17,9 +17,40 @@
 // Inside a range the tasks of a group of kGroupBlocks consecutive m-blocks are
 // ordered n-tile-major: tasks running side by side share both the A rows of
 // a few m-blocks and the weight strips of a few n-tiles.
+#include "gemm_direct.h"
 #include "gemm_tile.h"
 
 namespace moe {
+
+// Tile core of the persistent grouped GEMMs: bf16 loads straight into LDS
+// (gemm_direct.h); fp32 stages through registers (gemm_tile.h).
+template <typename T, int BM, int NB, int STAGING>
+struct TileSel {
+  using type = TileGemm<T, BM, 128, NB, false, STAGING>;
+};
+template <int BM, int NB, int STAGING>
+struct TileSel<bf16_t, BM, NB, STAGING> {
+  using type = TileGemmDirect<BM, NB>;
+};
+
+template <typename TG>
+constexpr bool is_direct() {
+  return TG::ES == 2 && TG::BK == 64 && sizeof(TG) > 0 && TG::LDS_BYTES == 3 * TG::STAGE;
+}
+
+// Run the K loop of tile core TG. The direct core gets three static LDS
+// arrays (one per stage); the register-staged core uses the dynamic buffer.
+template <typename TG>
+__device__ __forceinline__ void run_mainloop(TG& g, char* dyn, int64_t K) {
+  if constexpr (is_direct<TG>()) {
+    __shared__ __align__(16) char st0[TG::STAGE];
+    __shared__ __align__(16) char st1[TG::STAGE];
+    __shared__ __align__(16) char st2[TG::STAGE];
+    g.mainloop(st0, st1, st2, K);
+  } else {
+    g.mainloop(dyn, K);
+  }
+}
 
 constexpr int kGroupBlocks = 4;
 constexpr int kGateBM = 64;
@@ -88,6 +119,13 @@ __device__ __forceinline__ void decode_task(int64_t t, int64_t nb, int64_t nn, i
 
 // Claim the next task of [0, total): own XCD's range first, then the others.
 // q / tried persist across calls of one workgroup (thread 0 only).
+// A value every lane of the wave holds, made visibly wave-uniform (SGPR).
+__device__ __forceinline__ int64_t uniform64(int64_t v) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)v >> 32));
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
 __device__ __forceinline__ int64_t claim_task(int* counters, int64_t total, int& q, int& tried) {
   while (tried < kXcds) {
     const int64_t lo = total * q / kXcds;
@@ -126,7 +164,8 @@ __device__ __forceinline__ TaskSpace task_space(const ForwardParams& p, int BM, 
 // Ws_gate into hs.
 template <typename T, int BM, int BN>
 __global__ __launch_bounds__(256, 1) void upgate_kernel(ForwardParams p) {
-  using TG = TileGemm<T, BM, BN, 2, false, 2>;
+  using TG = typename TileSel<T, BM, 2, 2>::type;
+  static_assert(TG::BN == BN, "tile width");
   extern __shared__ __align__(16) char smem[];
   __shared__ int64_t s_task;
   __shared__ int s_tok[BM];
@@ -136,7 +175,7 @@ __global__ __launch_bounds__(256, 1) void upgate_kernel(ForwardParams p) {
   for (;;) {
     if (threadIdx.x == 0) s_task = claim_task(p.counters, ts.total, q, tried);
     __syncthreads();
-    const int64_t t = s_task;
+    const int64_t t = uniform64(s_task);
     if (t < 0) break;
     const bool shared = t >= ts.t_r;
     int64_t b, j;
@@ -161,7 +200,7 @@ __global__ __launch_bounds__(256, 1) void upgate_kernel(ForwardParams p) {
     const int64_t n0 = j * BN;
     const char* Bm[2];
     if (!shared) {
-      const int64_t e = p.expert_ids[b];
+      const int64_t e = __builtin_amdgcn_readfirstlane(p.expert_ids[b]);
       const size_t off = (size_t)e * p.H * p.D * sizeof(T);
       Bm[0] = reinterpret_cast<const char*>(p.Wu) + off;
       Bm[1] = reinterpret_cast<const char*>(p.Wg) + off;
@@ -174,7 +213,7 @@ __global__ __launch_bounds__(256, 1) void upgate_kernel(ForwardParams p) {
       const int tok = s_tok[r];
       return tok >= 0 ? (uint32_t)((int64_t)tok * H * sizeof(T)) : kOob;
     }, Bm, (uint32_t)(H * N * sizeof(T)), N, n0, N - n0);
-    g.mainloop(smem, p.H);
+    run_mainloop(g, smem, p.H);
     T* out = reinterpret_cast<T*>(shared ? p.hs : p.h);
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
@@ -207,7 +246,8 @@ __global__ __launch_bounds__(256, 1) void upgate_kernel(ForwardParams p) {
 // Shared task: y = hs[b*BM + r] . Ws_down[:, n-tile]; O_acc[s][n] += y.
 template <typename T, int BM, int BN>
 __global__ __launch_bounds__(256, 1) void down_kernel(ForwardParams p) {
-  using TG = TileGemm<T, BM, BN, 1>;
+  using TG = typename TileSel<T, BM, 1, 1>::type;
+  static_assert(TG::BN == BN, "tile width");
   extern __shared__ __align__(16) char smem[];
   __shared__ int64_t s_task;
   __shared__ int s_tok[BM];
@@ -219,7 +259,7 @@ __global__ __launch_bounds__(256, 1) void down_kernel(ForwardParams p) {
   for (;;) {
     if (threadIdx.x == 0) s_task = claim_task(counters, ts.total, q, tried);
     __syncthreads();
-    const int64_t t = s_task;
+    const int64_t t = uniform64(s_task);
     if (t < 0) break;
     const bool shared = t >= ts.t_r;
     int64_t b, j;
@@ -249,7 +289,7 @@ __global__ __launch_bounds__(256, 1) void down_kernel(ForwardParams p) {
     const int64_t n0 = j * BN;
     const char* Bm[1];
     if (!shared) {
-      const int64_t e = p.expert_ids[b];
+      const int64_t e = __builtin_amdgcn_readfirstlane(p.expert_ids[b]);
       Bm[0] = reinterpret_cast<const char*>(p.Wd) + (size_t)e * p.D * p.H * sizeof(T);
     } else {
       Bm[0] = reinterpret_cast<const char*>(p.Wsd);
@@ -260,7 +300,7 @@ __global__ __launch_bounds__(256, 1) void down_kernel(ForwardParams p) {
     g.setup(Ab, (uint32_t)(BM * K * sizeof(T)), [&](int r) -> uint32_t {
       return s_tok[r] >= 0 ? (uint32_t)(r * K * sizeof(T)) : kOob;
     }, Bm, (uint32_t)(K * p.H * sizeof(T)), p.H, n0, p.H - n0);
-    g.mainloop(smem, K);
+    run_mainloop(g, smem, K);
     float* O = p.Oacc;
     const int64_t H = p.H;
     g.for_each([&](int, int row, int col, float v) {
@@ -271,9 +311,12 @@ __global__ __launch_bounds__(256, 1) void down_kernel(ForwardParams p) {
   }
 }
 
-template <typename T, int BM, int BN, int NB>
+// dynamic LDS bytes of a persistent kernel (the direct core's stage buffers
+// are static)
+template <typename T, int BM, int NB, int STAGING>
 static int lds_bytes() {
-  return TileGemm<T, BM, BN, NB>::LDS_BYTES;
+  using TG = typename TileSel<T, BM, NB, STAGING>::type;
+  return is_direct<TG>() ? 0 : TG::LDS_BYTES;
 }
 
 static int num_cus() {
@@ -312,13 +355,13 @@ constexpr int down_bn() { return 128; }
 template <typename T, int BM>
 static hipError_t launch_upgate_t(const ForwardParams& p, hipStream_t st) {
   constexpr int BN = upgate_bn<BM>();
-  return launch_persistent(upgate_kernel<T, BM, BN>, lds_bytes<T, BM, BN, 2>(), p, st);
+  return launch_persistent(upgate_kernel<T, BM, BN>, lds_bytes<T, BM, 2, 2>(), p, st);
 }
 
 template <typename T, int BM>
 static hipError_t launch_down_t(const ForwardParams& p, hipStream_t st) {
   constexpr int BN = down_bn<BM>();
-  return launch_persistent(down_kernel<T, BM, BN>, lds_bytes<T, BM, BN, 1>(), p, st);
+  return launch_persistent(down_kernel<T, BM, BN>, lds_bytes<T, BM, 1, 1>(), p, st);
 }
 
 template <typename T>
