@@ -1,8 +1,9 @@
 // One workgroup's bf16 output tile of C_m = A . B_m (m < NB) on gfx950, with
 // both operands loaded straight from global memory into LDS.
 //
-// 256 threads (4 wave64s), tile BM rows x BN (= 128) columns per weight
-// matrix, K stages of 64 elements, NSTAGE = 3 LDS stages.
+// NW wave64s (8: two per SIMD, so one wave's MFMAs cover the other's LDS
+// and barrier waits), tile BM rows x BN (= 128) columns per weight matrix,
+// K stages of 64 elements, NSTAGE = 3 LDS stages.
 //
 //  - global -> LDS: buffer_load_dwordx4 with the lds bit (16 bytes per lane;
 //    lane l's bytes land at the LDS base in M0 + 16 l). No staging registers,
@@ -72,9 +73,11 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-template <int BM_, int NB_>
+template <int BM_, int NB_, int NW_ = 8>
 struct TileGemmDirect {
   static constexpr int BM = BM_, BN = 128, NB = NB_;
+  static constexpr int NW = NW_;              // waves per workgroup (2 per SIMD at 8)
+  static constexpr int THREADS = 64 * NW;
   static constexpr int ES = 2;
   static constexpr int BK = 64;
   static constexpr int NSTAGE = 3;
@@ -86,19 +89,19 @@ struct TileGemmDirect {
   static constexpr int STAGE = A_LDS + B_LDS;
   static constexpr int LDS_BYTES = NSTAGE * STAGE;  // three __shared__ arrays of STAGE bytes
   static constexpr int WM = BM >= 32 ? 2 : 1;
-  static constexpr int WN = 4 / WM;
+  static constexpr int WN = NW / WM;
   static constexpr int MI = BM / WM / 16;
   static constexpr int NI = BN / WN / 16;
   static constexpr int KSTEPS = BK / 32;
   // 1 KB (one wave instruction) units per stage
   static constexpr int A_INSTR = A_LDS / 1024;
   static constexpr int B_INSTR = B_LDS / 1024;
-  static constexpr int A_PW = (A_INSTR + 3) / 4;   // per wave (upper bound)
-  static constexpr int B_PW = B_INSTR / 4;
+  static constexpr int A_PW = (A_INSTR + NW - 1) / NW;   // per wave (upper bound)
+  static constexpr int B_PW = B_INSTR / NW;
   // loads every wave issues per stage (waves with fewer A units wait for less)
-  static constexpr int MIN_PW = A_INSTR / 4 + B_PW;
-  static_assert(B_INSTR % 4 == 0, "B loads split evenly over the waves");
-  static_assert(MI >= 1 && NI >= 1, "tile too small for four waves");
+  static constexpr int MIN_PW = A_INSTR / NW + B_PW;
+  static_assert(B_INSTR % NW == 0, "B loads split evenly over the waves");
+  static_assert(MI >= 1 && NI >= 1, "tile too small for the waves");
   static_assert(LDS_BYTES <= 160 * 1024, "LDS");
 
   f32x4_t acc[NB][MI][NI];
@@ -121,19 +124,22 @@ struct TileGemmDirect {
         for (int j = 0; j < NI; ++j) acc[m][i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
 
+  // A: buffer of a_bytes at a_base, row_off(r) = byte offset of row r or kOob.
+  // B[m]: base of weight matrix m (K x ldb, row-major) with b_bytes[m] bytes;
+  // the tile covers its columns n0 .. n0 + BN, of which ncols[m] are valid.
   template <typename RowOff>
   __device__ __forceinline__ void setup(const void* a_base, uint32_t a_bytes, RowOff row_off,
-                                        const char* const* B, uint32_t b_bytes, int64_t ldb,
-                                        int64_t n0, int64_t ncols) {
+                                        const char* const* B, const uint32_t* b_bytes,
+                                        int64_t ldb, int64_t n0, const int64_t* ncols) {
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     rsrc_a = make_srd(a_base, a_bytes);
 #pragma unroll
-    for (int m = 0; m < NB; ++m) rsrc_b[m] = make_srd(B[m], b_bytes);
+    for (int m = 0; m < NB; ++m) rsrc_b[m] = make_srd(B[m], b_bytes[m]);
     b_stage_bytes = (uint32_t)(BK * ldb * ES);
 #pragma unroll
     for (int t = 0; t < A_PW; ++t) {
-      const int q = wave + 4 * t;  // A instruction index: rows 8q .. 8q + 7
+      const int q = wave + NW * t;  // A instruction index: rows 8q .. 8q + 7
       uint32_t o = kOob;
       if (q < A_INSTR) {
         const int r = 8 * q + (lane >> 3);
@@ -145,11 +151,11 @@ struct TileGemmDirect {
     }
 #pragma unroll
     for (int t = 0; t < B_PW; ++t) {
-      const int q = wave + 4 * t;                 // B instruction index
+      const int q = wave + NW * t;                // B instruction index
       const int kr = (q % (B_MAT / 1024)) * 4 + (lane >> 4);  // k-row in the stage
       const int pc = lane & 15;                   // physical 16-byte chunk in the row
       const int c = (((pc >> 1) ^ bswz(kr)) << 1) | (pc & 1);  // logical chunk
-      const bool ok = (int64_t)c * 8 + 8 <= ncols;
+      const bool ok = (int64_t)c * 8 + 8 <= ncols[q / (B_MAT / 1024)];
       boff[t] = ok ? (uint32_t)(((int64_t)kr * ldb + n0 + c * 8) * ES) : kOob;
     }
   }
@@ -161,7 +167,7 @@ struct TileGemmDirect {
     const int64_t k0 = (int64_t)kt * BK;
 #pragma unroll
     for (int t = 0; t < A_PW; ++t) {
-      const int q = wave + 4 * t;
+      const int q = wave + NW * t;
       if (q < A_INSTR) {  // wave-uniform
         const int lane = threadIdx.x & 63;
         const int r = 8 * q + (lane >> 3);
@@ -173,7 +179,7 @@ struct TileGemmDirect {
     }
 #pragma unroll
     for (int t = 0; t < B_PW; ++t) {
-      const int q = wave + 4 * t;
+      const int q = wave + NW * t;
       const int m = q / (B_MAT / 1024);  // wave-uniform
       const uint32_t o = boff[t] == kOob ? kOob : boff[t] + (uint32_t)kt * b_stage_bytes;
       i32x4_t rb = rsrc_b[0];

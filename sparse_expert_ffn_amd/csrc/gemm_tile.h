@@ -57,6 +57,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 template <typename T, int BM_, int BN_, int NB_, bool RAGGED_B = false, int STAGING = 1>
 struct TileGemm {
   static constexpr int BM = BM_, BN = BN_, NB = NB_;
+  static constexpr int THREADS = 256;
   static constexpr int ES = sizeof(T);
   static constexpr int BK = 128 / ES;   // K elements per stage
   static constexpr int KB = BK / 8;     // 8-element units per row per stage
@@ -111,16 +112,16 @@ struct TileGemm {
 
   // A: buffer of a_bytes bytes at a_base; row_off(r) = byte offset of row r
   //    (K-contiguous) or kOob for a zero row.
-  // B[m]: base of the K x ldb matrix m (row-major), b_bytes = K * ldb * ES;
-  //    this tile covers columns n0 .. n0 + BN of it, ncols = N - n0 valid.
+  // B[m]: base of the K x ldb matrix m (row-major) with b_bytes[m] bytes;
+  //    this tile covers columns n0 .. n0 + BN of it, ncols_m[m] valid.
   template <typename RowOff>
   __device__ __forceinline__ void setup(const void* a_base, uint32_t a_bytes, RowOff row_off,
-                                        const char* const* B, uint32_t b_bytes, int64_t ldb,
-                                        int64_t n0, int64_t ncols) {
+                                        const char* const* B, const uint32_t* b_bytes,
+                                        int64_t ldb, int64_t n0, const int64_t* ncols_m) {
     const int tid = threadIdx.x;
     rsrc_a = make_rsrc(a_base, a_bytes);
 #pragma unroll
-    for (int m = 0; m < NB; ++m) rsrc_b[m] = make_rsrc(B[m], b_bytes);
+    for (int m = 0; m < NB; ++m) rsrc_b[m] = make_rsrc(B[m], b_bytes[m]);
     ldb_bytes = ldb * ES;
 #pragma unroll
     for (int i = 0; i < A_PT; ++i) {
@@ -137,6 +138,7 @@ struct TileGemm {
       const int c = tid + i * 256;
       const int nb = (c / KB) % NBLK;
       const int kb = c % KB;
+      const int64_t ncols = c < B_BLOCKS ? ncols_m[c / (KB * NBLK)] : 0;
       const bool ok = c < B_BLOCKS && (int64_t)nb * 8 + (RAGGED_B ? 1 : 8) <= ncols;
       boff[i] = ok ? (uint32_t)((n0 + nb * 8) * ES + (int64_t)kb * 8 * ldb_bytes) : kOob;
       bcols[i] = RAGGED_B ? (int)min<int64_t>(8, ncols - (int64_t)nb * 8) : 8;

@@ -69,10 +69,12 @@ __global__ __launch_bounds__(256) void gate_gemm_kernel(GateParams p) {
   TG g;
   const char* Bm[1] = {reinterpret_cast<const char*>(p.Wr)};
   const int64_t S = p.S, H = p.H;
+  const uint32_t bb[1] = {(uint32_t)(H * p.E * sizeof(T))};
+  const int64_t nc[1] = {p.E - n0};
   g.setup(p.A, (uint32_t)(S * H * sizeof(T)), [&](int r) -> uint32_t {
     const int64_t s = m0 + r;
     return s < S ? (uint32_t)(s * H * sizeof(T)) : kOob;
-  }, Bm, (uint32_t)(H * p.E * sizeof(T)), p.E, n0, p.E - n0);
+  }, Bm, bb, p.E, n0, nc);
   g.mainloop(smem, p.H);
   g.for_each([&](int, int row, int col, float v) {
     const int64_t s = m0 + row, e = n0 + col;
@@ -162,8 +164,13 @@ __device__ __forceinline__ TaskSpace task_space(const ForwardParams& p, int BM, 
 //   t = sorted_ids[b*BM + r] / k; sentinel rows are skipped.
 // Shared task (m-block b over tokens b*BM + r < S): the same with Ws_up,
 // Ws_gate into hs.
+template <typename T, int BM, int NB, int STAGING>
+constexpr int tile_threads() {
+  return TileSel<T, BM, NB, STAGING>::type::THREADS;
+}
+
 template <typename T, int BM, int BN>
-__global__ __launch_bounds__(256, 1) void upgate_kernel(ForwardParams p) {
+__global__ __launch_bounds__((tile_threads<T, BM, 2, 2>()), 1) void upgate_kernel(ForwardParams p) {
   using TG = typename TileSel<T, BM, 2, 2>::type;
   static_assert(TG::BN == BN, "tile width");
   extern __shared__ __align__(16) char smem[];
@@ -209,10 +216,12 @@ __global__ __launch_bounds__(256, 1) void upgate_kernel(ForwardParams p) {
       Bm[1] = reinterpret_cast<const char*>(p.Wsg);
     }
     const int64_t H = p.H;
+    const uint32_t bb[2] = {(uint32_t)(H * N * sizeof(T)), (uint32_t)(H * N * sizeof(T))};
+    const int64_t nc[2] = {N - n0, N - n0};
     g.setup(p.A, (uint32_t)(p.S * H * sizeof(T)), [&](int r) -> uint32_t {
       const int tok = s_tok[r];
       return tok >= 0 ? (uint32_t)((int64_t)tok * H * sizeof(T)) : kOob;
-    }, Bm, (uint32_t)(H * N * sizeof(T)), N, n0, N - n0);
+    }, Bm, bb, N, n0, nc);
     run_mainloop(g, smem, p.H);
     T* out = reinterpret_cast<T*>(shared ? p.hs : p.h);
     const int lane = threadIdx.x & 63;
@@ -244,15 +253,21 @@ __global__ __launch_bounds__(256, 1) void upgate_kernel(ForwardParams p) {
 // Routed task: y = h[b*BM + r] . W_down^e[:, n-tile];
 //   O_acc[t][n] += topk_weights[f] * y for f = sorted_ids[b*BM + r] != F.
 // Shared task: y = hs[b*BM + r] . Ws_down[:, n-tile]; O_acc[s][n] += y.
+// An n-tile is 2 x 128 columns: two adjacent column strips of the down
+// weights run as the tile core's two matrices, sharing the h rows.
+constexpr int kDownStrips = 2;
+
 template <typename T, int BM, int BN>
-__global__ __launch_bounds__(256, 1) void down_kernel(ForwardParams p) {
-  using TG = typename TileSel<T, BM, 1, 1>::type;
+__global__ __launch_bounds__((tile_threads<T, BM, kDownStrips, 1>()), 1) void down_kernel(
+    ForwardParams p) {
+  using TG = typename TileSel<T, BM, kDownStrips, 1>::type;
   static_assert(TG::BN == BN, "tile width");
+  constexpr int NT = kDownStrips * BN;  // columns per task
   extern __shared__ __align__(16) char smem[];
   __shared__ int64_t s_task;
   __shared__ int s_tok[BM];
   __shared__ float s_w[BM];
-  const TaskSpace ts = task_space(p, BM, BN, p.H, p.H);
+  const TaskSpace ts = task_space(p, BM, NT, p.H, p.H);
   int q = blockIdx.x % kXcds, tried = 0;
   int* counters = p.counters + kXcds;
   TG g;
@@ -286,26 +301,37 @@ __global__ __launch_bounds__(256, 1) void down_kernel(ForwardParams p) {
     }
     __syncthreads();
     const int64_t K = shared ? p.Ds : p.D;
-    const int64_t n0 = j * BN;
-    const char* Bm[1];
+    const int64_t n0 = j * NT;
+    const char* Wb;
     if (!shared) {
       const int64_t e = __builtin_amdgcn_readfirstlane(p.expert_ids[b]);
-      Bm[0] = reinterpret_cast<const char*>(p.Wd) + (size_t)e * p.D * p.H * sizeof(T);
+      Wb = reinterpret_cast<const char*>(p.Wd) + (size_t)e * p.D * p.H * sizeof(T);
     } else {
-      Bm[0] = reinterpret_cast<const char*>(p.Wsd);
+      Wb = reinterpret_cast<const char*>(p.Wsd);
+    }
+    const uint32_t wbytes = (uint32_t)(K * p.H * sizeof(T));
+    const char* Bm[kDownStrips];
+    uint32_t bb[kDownStrips];
+    int64_t nc[kDownStrips];
+#pragma unroll
+    for (int m = 0; m < kDownStrips; ++m) {
+      // strip m: columns n0 + m*BN .. of the [K][H] down weights
+      Bm[m] = Wb + (size_t)m * BN * sizeof(T);
+      bb[m] = wbytes - (uint32_t)(m * BN * sizeof(T));
+      nc[m] = p.H - n0 - m * BN;
     }
     // this m-block's BM rows of h (or hs), K-contiguous
     const char* Ab = reinterpret_cast<const char*>(shared ? p.hs : p.h) +
                      (size_t)b * BM * K * sizeof(T);
     g.setup(Ab, (uint32_t)(BM * K * sizeof(T)), [&](int r) -> uint32_t {
       return s_tok[r] >= 0 ? (uint32_t)(r * K * sizeof(T)) : kOob;
-    }, Bm, (uint32_t)(K * p.H * sizeof(T)), p.H, n0, p.H - n0);
+    }, Bm, bb, p.H, n0, nc);
     run_mainloop(g, smem, K);
     float* O = p.Oacc;
     const int64_t H = p.H;
-    g.for_each([&](int, int row, int col, float v) {
+    g.for_each([&](int m, int row, int col, float v) {
       const int tok = s_tok[row];
-      const int64_t n = n0 + col;
+      const int64_t n = n0 + m * BN + col;
       if (tok >= 0 && n < H) atomicAdd(O + (size_t)tok * H + n, s_w[row] * v);
     });
   }
@@ -333,16 +359,17 @@ static int num_cus() {
 }
 
 template <typename K>
-static hipError_t launch_persistent(K kernel, int lds, const ForwardParams& p, hipStream_t st) {
+static hipError_t launch_persistent(K kernel, int lds, int threads, const ForwardParams& p,
+                                    hipStream_t st) {
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, lds);
   if (e != hipSuccess) return e;
   int per_cu = 0;
-  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, 256, lds);
+  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, lds);
   if (e != hipSuccess) return e;
   if (per_cu < 1) per_cu = 1;
   const int grid = num_cus() * per_cu;
-  hipLaunchKernelGGL(kernel, dim3(grid), dim3(256), lds, st, p);
+  hipLaunchKernelGGL(kernel, dim3(grid), dim3(threads), lds, st, p);
   return hipGetLastError();
 }
 
@@ -355,13 +382,15 @@ constexpr int down_bn() { return 128; }
 template <typename T, int BM>
 static hipError_t launch_upgate_t(const ForwardParams& p, hipStream_t st) {
   constexpr int BN = upgate_bn<BM>();
-  return launch_persistent(upgate_kernel<T, BM, BN>, lds_bytes<T, BM, 2, 2>(), p, st);
+  return launch_persistent(upgate_kernel<T, BM, BN>, lds_bytes<T, BM, 2, 2>(),
+                           tile_threads<T, BM, 2, 2>(), p, st);
 }
 
 template <typename T, int BM>
 static hipError_t launch_down_t(const ForwardParams& p, hipStream_t st) {
   constexpr int BN = down_bn<BM>();
-  return launch_persistent(down_kernel<T, BM, BN>, lds_bytes<T, BM, 1, 1>(), p, st);
+  return launch_persistent(down_kernel<T, BM, BN>, lds_bytes<T, BM, kDownStrips, 1>(),
+                           tile_threads<T, BM, kDownStrips, 1>(), p, st);
 }
 
 template <typename T>
