@@ -40,6 +40,17 @@ namespace moe {
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
 typedef int i32x4_t __attribute__((ext_vector_type(4)));
 
+// Schedule knobs (compile time, chosen by measurement):
+//  MOE_FRAG_PIPE  1: read the next K step's operand fragments before the
+//                 current step's MFMAs (two fragment register sets).
+//  MOE_MFMA_PRIO  1: raise the wave's issue priority around its MFMA block.
+#ifndef MOE_FRAG_PIPE
+#define MOE_FRAG_PIPE 0
+#endif
+#ifndef MOE_MFMA_PRIO
+#define MOE_MFMA_PRIO 0
+#endif
+
 // Raw buffer descriptor (gfx9): base[47:0], stride 0, num_records = bytes,
 // dword3 0x00020000. Built from wave-uniform values so it lives in SGPRs.
 __device__ __forceinline__ i32x4_t make_srd(const void* base, uint32_t bytes) {
@@ -73,14 +84,14 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-template <int BM_, int NB_, int NW_ = 8>
+template <int BM_, int NB_, int NW_ = 8, int NSTAGE_ = 3>
 struct TileGemmDirect {
   static constexpr int BM = BM_, BN = 128, NB = NB_;
   static constexpr int NW = NW_;              // waves per workgroup (2 per SIMD at 8)
   static constexpr int THREADS = 64 * NW;
   static constexpr int ES = 2;
   static constexpr int BK = 64;
-  static constexpr int NSTAGE = 3;
+  static constexpr int NSTAGE = NSTAGE_;  // 3, or 2 when three stages do not fit
   static constexpr int A_ROWB = 128;
   static constexpr int B_ROWB = BN * ES;          // 256
   static constexpr int A_LDS = BM * A_ROWB;
@@ -190,49 +201,108 @@ struct TileGemmDirect {
     }
   }
 
-  __device__ __forceinline__ void compute_stage(const char* base) {
+  struct Frags {
+    uint4 a[MI];
+    uint4 b[NB][NI];
+  };
+
+  // Operand fragments of 32-wide K step ks of the stage buffer `base`.
+  __device__ __forceinline__ void read_frags(const char* base, int ks, Frags& f) const {
+#pragma unroll
+    for (int i = 0; i < MI; ++i) f.a[i] = read_a(base, ks, i);
+    read_frags_b(base, ks, f);
+  }
+
+  __device__ __forceinline__ void read_frags_b(const char* base, int ks, Frags& f) const {
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
-    const int wm0 = (wave / WN) * (BM / WM);
     const int wn0 = (wave % WN) * (BN / WN);
     const int lr = lane & 15;
     const int lg = lane >> 4;
 #pragma unroll
-    for (int ks = 0; ks < KSTEPS; ++ks) {
-      uint4 a[MI];
+    for (int m = 0; m < NB; ++m)
 #pragma unroll
-      for (int i = 0; i < MI; ++i) {
-        const int r = wm0 + i * 16 + lr;
-        const int c = ks * 4 + lg;
-        a[i] = *reinterpret_cast<const uint4*>(base + r * A_ROWB + ((c ^ aswz(r)) << 4));
-      }
-      uint4 b[NB][NI];
+      for (int j = 0; j < NI; ++j) {
+        i16x4_t h[2];
 #pragma unroll
-      for (int m = 0; m < NB; ++m)
-#pragma unroll
-        for (int j = 0; j < NI; ++j) {
-          i16x4_t h[2];
-#pragma unroll
-          for (int hh = 0; hh < 2; ++hh) {
-            const int k = ks * 32 + 8 * lg + 4 * hh + (lr >> 2);
-            const int n = wn0 + j * 16 + 4 * (lr & 3);
-            const int c = n >> 3;
-            const int pc = ((((c >> 1) ^ bswz(k)) << 1) | (c & 1));
-            const char* p = base + A_LDS + m * B_MAT + k * B_ROWB + (pc << 4) + ((n & 4) << 1);
-            h[hh] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (__attribute__((address_space(3))) i16x4_t*)(p));
-          }
-          b[m][j] = __builtin_bit_cast(uint4, h);
+        for (int hh = 0; hh < 2; ++hh) {
+          const int k = ks * 32 + 8 * lg + 4 * hh + (lr >> 2);
+          const int n = wn0 + j * 16 + 4 * (lr & 3);
+          const int c = n >> 3;
+          const int pc = ((((c >> 1) ^ bswz(k)) << 1) | (c & 1));
+          const char* p = base + A_LDS + m * B_MAT + k * B_ROWB + (pc << 4) + ((n & 4) << 1);
+          h[hh] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) i16x4_t*)(p));
         }
+        f.b[m][j] = __builtin_bit_cast(uint4, h);
+      }
+  }
+
+  __device__ __forceinline__ void mfmas(const Frags& f) {
+#if MOE_MFMA_PRIO
+    __builtin_amdgcn_s_setprio(1);
+#endif
 #pragma unroll
-      for (int m = 0; m < NB; ++m)
+    for (int m = 0; m < NB; ++m)
 #pragma unroll
-        for (int i = 0; i < MI; ++i)
+      for (int i = 0; i < MI; ++i)
 #pragma unroll
-          for (int j = 0; j < NI; ++j)
-            acc[m][i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                __builtin_bit_cast(bf16x8_t, a[i]), __builtin_bit_cast(bf16x8_t, b[m][j]),
-                acc[m][i][j], 0, 0, 0);
+        for (int j = 0; j < NI; ++j)
+          acc[m][i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              __builtin_bit_cast(bf16x8_t, f.a[i]), __builtin_bit_cast(bf16x8_t, f.b[m][j]),
+              acc[m][i][j], 0, 0, 0);
+#if MOE_MFMA_PRIO
+    __builtin_amdgcn_s_setprio(0);
+#endif
+  }
+
+  __device__ __forceinline__ uint4 read_a(const char* base, int ks, int i) const {
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int wm0 = (wave / WN) * (BM / WM);
+    const int r = wm0 + i * 16 + (lane & 15);
+    const int c = ks * 4 + (lane >> 4);
+    return *reinterpret_cast<const uint4*>(base + r * A_ROWB + ((c ^ aswz(r)) << 4));
+  }
+
+  // One stage. Large tiles (MI > 4) keep only the B fragments of a K step
+  // resident and read A one 16-row block at a time, each feeding NB * NI
+  // MFMAs (fewer live registers next to the accumulators).
+  __device__ __forceinline__ void compute_stage(const char* base) {
+    if constexpr (MI > 4) {
+#pragma unroll
+      for (int ks = 0; ks < KSTEPS; ++ks) {
+        Frags f;
+        read_frags_b(base, ks, f);
+#pragma unroll
+        for (int i = 0; i < MI; ++i) {
+          const uint4 a = read_a(base, ks, i);
+#pragma unroll
+          for (int m = 0; m < NB; ++m)
+#pragma unroll
+            for (int j = 0; j < NI; ++j)
+              acc[m][i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                  __builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, f.b[m][j]),
+                  acc[m][i][j], 0, 0, 0);
+        }
+      }
+    } else {
+#if MOE_FRAG_PIPE
+      Frags f[2];
+      read_frags(base, 0, f[0]);
+#pragma unroll
+      for (int ks = 0; ks < KSTEPS; ++ks) {
+        if (ks + 1 < KSTEPS) read_frags(base, ks + 1, f[(ks + 1) & 1]);
+        mfmas(f[ks & 1]);
+      }
+#else
+#pragma unroll
+      for (int ks = 0; ks < KSTEPS; ++ks) {
+        Frags f;
+        read_frags(base, ks, f);
+        mfmas(f);
+      }
+#endif
     }
   }
 
@@ -245,7 +315,7 @@ struct TileGemmDirect {
     compute_stage(cur);
   }
 
-  // Full K loop over the three stage buffers (distinct LDS objects, so the
+  // Full K loop over the stage buffers (distinct LDS objects, so the
   // compiler can see that the loads in flight never write the buffer being
   // read and needs no wait for them). Stages past the end of K are issued too
   // (they load zeros without memory traffic) so every step has the same
@@ -257,14 +327,30 @@ struct TileGemmDirect {
     if (nk <= 0) return;
     wait_vmcnt<0>();  // nothing of an earlier tile still writing LDS
     __syncthreads();
-    issue_stage(s0, 0);
-    issue_stage(s1, 1);
-    for (int kt = 0; kt < nk; kt += 3) {
-      step(s0, s2, kt);
-      if (kt + 1 < nk) step(s1, s0, kt + 1);
-      if (kt + 2 < nk) step(s2, s1, kt + 2);
+    if constexpr (NSTAGE == 3) {
+      issue_stage(s0, 0);
+      issue_stage(s1, 1);
+      for (int kt = 0; kt < nk; kt += 3) {
+        step(s0, s2, kt);
+        if (kt + 1 < nk) step(s1, s0, kt + 1);
+        if (kt + 2 < nk) step(s2, s1, kt + 2);
+      }
+    } else {
+      // two buffers: stage kt+1 is loaded while stage kt is multiplied
+      issue_stage(s0, 0);
+      for (int kt = 0; kt < nk; kt += 2) {
+        step2(s0, s1, kt);
+        if (kt + 1 < nk) step2(s1, s0, kt + 1);
+      }
     }
     wait_vmcnt<0>();
+  }
+
+  __device__ __forceinline__ void step2(const char* cur, char* nxt, int kt) {
+    wait_vmcnt<0>();   // this wave's stage-kt loads have landed
+    __syncthreads();   // ... and every wave's; stage kt-1 reads are done
+    issue_stage(nxt, kt + 1);
+    compute_stage(cur);
   }
 
   template <typename F>

@@ -30,12 +30,13 @@ struct TileSel {
 };
 template <int BM, int NB, int STAGING>
 struct TileSel<bf16_t, BM, NB, STAGING> {
-  using type = TileGemmDirect<BM, NB>;
+  // 256-row tiles need 64 KB per stage: two stages
+  using type = TileGemmDirect<BM, NB, 8, (BM >= 256 ? 2 : 3)>;
 };
 
 template <typename TG>
 constexpr bool is_direct() {
-  return TG::ES == 2 && TG::BK == 64 && sizeof(TG) > 0 && TG::LDS_BYTES == 3 * TG::STAGE;
+  return TG::THREADS == 512;
 }
 
 // Run the K loop of tile core TG. The direct core gets three static LDS
@@ -45,7 +46,7 @@ __device__ __forceinline__ void run_mainloop(TG& g, char* dyn, int64_t K) {
   if constexpr (is_direct<TG>()) {
     __shared__ __align__(16) char st0[TG::STAGE];
     __shared__ __align__(16) char st1[TG::STAGE];
-    __shared__ __align__(16) char st2[TG::STAGE];
+    __shared__ __align__(16) char st2[TG::NSTAGE > 2 ? TG::STAGE : 16];
     g.mainloop(st0, st1, st2, K);
   } else {
     g.mainloop(dyn, K);
@@ -400,6 +401,10 @@ static hipError_t dispatch_bm(const ForwardParams& p, int BM, bool up, hipStream
     case 32: return up ? launch_upgate_t<T, 32>(p, st) : launch_down_t<T, 32>(p, st);
     case 64: return up ? launch_upgate_t<T, 64>(p, st) : launch_down_t<T, 64>(p, st);
     case 128: return up ? launch_upgate_t<T, 128>(p, st) : launch_down_t<T, 128>(p, st);
+    case 256:
+      if constexpr (sizeof(T) == 2)
+        return up ? launch_upgate_t<T, 256>(p, st) : launch_down_t<T, 256>(p, st);
+      return hipErrorInvalidValue;
     default: return hipErrorInvalidValue;
   }
 }
@@ -413,8 +418,7 @@ hipError_t launch_forward_down(const ForwardParams& p, int dtype, int BM, hipStr
 }
 
 int forward_lds_ok(int dtype, int BM) {
-  (void)dtype;
-  return BM == 16 || BM == 32 || BM == 64 || BM == 128;
+  return BM == 16 || BM == 32 || BM == 64 || BM == 128 || (BM == 256 && dtype == 1);
 }
 
 // ------------------------------------------------------- setup and finalize

@@ -56,7 +56,8 @@ class MoEBuffers:
 
 def suggest_block_size(S: int, k: int, E: int) -> int:
     """Rows per sorted block from the mean rows per expert (vLLM's fused_moe
-    note uses 16 / 32 / 64 as the token count grows; 128 for prefill)."""
+    note uses 16 / 32 / 64 as the token count grows; 128 and 256 for
+    prefill, where the larger tile halves the weight traffic per flop)."""
     mean = S * k / max(E, 1)
     if mean <= 16:
         return 16
@@ -64,4 +65,6 @@ def suggest_block_size(S: int, k: int, E: int) -> int:
         return 32
     if mean <= 96:
         return 64
-    return 128
+    if mean < 192:
+        return 128
+    return 256

@@ -55,8 +55,9 @@ def run_case(orc, wl, bm=None, li=None, logits=None, poison=True):
 
 
 CASES = [("tiny_fp32", 64, 16), ("tiny_fp32", 64, 128), ("prefill_bal", 700, 128),
-         ("prefill_bal", 700, 16), ("prefill_bal", 333, 64), ("prefill_skew", 300, 128),
-         ("prefill_skew", 300, 32), ("decode", 64, 16), ("decode", 64, 128), ("decode", 1, 16)]
+         ("prefill_bal", 700, 256), ("prefill_bal", 700, 16), ("prefill_bal", 333, 64),
+         ("prefill_skew", 300, 128), ("prefill_skew", 300, 256), ("prefill_skew", 300, 32),
+         ("decode", 64, 16), ("decode", 64, 128), ("decode", 1, 16), ("dsv3", 40, 128)]
 
 
 @pytest.mark.parametrize("name,S,bm", CASES)
@@ -78,7 +79,7 @@ def _small(dtype, **kw):
 def test_ragged_tiles_and_shared(orc, dtype):
     """H, D, D_shared not multiples of the 128-wide tiles; K tails; shared expert."""
     wl = _small(dtype, D_shared=72)
-    for bm in (16, 64):
+    for bm in ((16, 64) if dtype == wk.F32 else (16, 64, 256)):
         err, tol, _, _ = run_case(orc, wl, bm)
         assert err <= tol, f"BM={bm}: {err:.3e}"
 
@@ -92,7 +93,8 @@ def test_capacity_drops(orc, dtype):
     assert err <= tol
 
 
-def test_hot_expert_and_empty_experts(orc):
+@pytest.mark.parametrize("bm", [128, 256])
+def test_hot_expert_and_empty_experts(orc, bm):
     """Every token picks expert 5 first: one expert holds S rows (many m-blocks),
     most experts are empty."""
     wl = _small(wk.BF16, S=1500, E=40, k=2)
@@ -101,7 +103,7 @@ def test_hot_expert_and_empty_experts(orc):
     G = rng.standard_normal((wl.S, wl.E)).astype(np.float32)
     G[:, 5] += 50.0
     G[:, 9] += 10.0 * (rng.random(wl.S) > 0.5)
-    err, tol, ref, _ = run_case(orc, wl, 128, li=li, logits=G)
+    err, tol, ref, _ = run_case(orc, wl, bm, li=li, logits=G)
     assert err <= tol
 
 
