@@ -3,17 +3,18 @@
 //
 // NW wave64s (8: two per SIMD, so one wave's MFMAs cover the other's LDS
 // and barrier waits), tile BM rows x BN (= 128) columns per weight matrix,
-// K stages of 64 elements, NSTAGE = 3 LDS stages.
+// K stages of BK (32 or 64) elements in a ring of as many LDS stage slots as
+// fit the budget.
 //
 //  - global -> LDS: buffer_load_dwordx4 with the lds bit (16 bytes per lane;
 //    lane l's bytes land at the LDS base in M0 + 16 l). No staging registers,
 //    no register transpose, no LDS store instructions.
 //    Zero rows, rows past K and columns past N use out-of-range offsets: the
 //    hardware writes zeros.
-//  - A in LDS: BM rows of 128 bytes, 16-byte chunk c of row r stored in slot
-//    c ^ key(r), key(r) = (r & 7) ^ ((r >> 3) & 1): the 16 rows one operand
-//    read touches land in 16 different 16-byte bank windows.
-//  - B in LDS: each matrix as [64 k-rows][BN columns], N-contiguous as in
+//  - A in LDS: BM rows of 2*BK bytes, 16-byte chunk c of row r stored in slot
+//    c ^ key(r) (see aswz): the 16 rows one operand read touches land in 16
+//    different 16-byte bank windows.
+//  - B in LDS: each matrix as [BK k-rows][BN columns], N-contiguous as in
 //    memory (256 bytes per row); its 32-byte column pairs are XOR-swizzled by
 //    g(k) = (k & 3) | ((k >> 3) & 1) << 2 so the 16 k-rows one transposed read
 //    touches fall in 8 different pair slots.
@@ -28,9 +29,8 @@
 //    k-rows + 4.
 //  - v_mfma_f32_16x16x32_bf16, fp32 accumulators (lane l: column l % 16, rows
 //    4 (l / 16) .. +3 of each 16x16 block).
-//  - Pipeline: stage kt+2's loads are issued right after the barrier that
-//    makes stage kt visible; each wave waits (vmcnt) only for its own stage-kt
-//    loads, then one barrier per stage.
+//  - Pipeline: NSTAGE-1 stages in flight; each wave waits (vmcnt) only for
+//    its own stage-kt loads, then one barrier per stage.
 #pragma once
 
 #include "gemm_tile.h"
@@ -84,21 +84,25 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-template <int BM_, int NB_, int NW_ = 8, int NSTAGE_ = 3>
+template <int BM_, int NB_, int NW_ = 8, int BK_ = 64, int LDS_BUDGET = 144 * 1024>
 struct TileGemmDirect {
   static constexpr int BM = BM_, BN = 128, NB = NB_;
   static constexpr int NW = NW_;              // waves per workgroup (2 per SIMD at 8)
   static constexpr int THREADS = 64 * NW;
   static constexpr int ES = 2;
-  static constexpr int BK = 64;
-  static constexpr int NSTAGE = NSTAGE_;  // 3, or 2 when three stages do not fit
-  static constexpr int A_ROWB = 128;
-  static constexpr int B_ROWB = BN * ES;          // 256
+  static constexpr int BK = BK_;              // 32 or 64 K elements per stage
+  static constexpr int ACH = BK / 8;          // 16-byte chunks per A row
+  static constexpr int A_ROWB = BK * ES;
+  static constexpr int B_ROWB = BN * ES;      // 256
   static constexpr int A_LDS = BM * A_ROWB;
-  static constexpr int B_MAT = BK * B_ROWB;        // 16 KB per matrix per stage
+  static constexpr int B_MAT = BK * B_ROWB;   // per matrix per stage
   static constexpr int B_LDS = NB * B_MAT;
   static constexpr int STAGE = A_LDS + B_LDS;
-  static constexpr int LDS_BYTES = NSTAGE * STAGE;  // three __shared__ arrays of STAGE bytes
+  // as many stages as fit the budget (one LDS array, stage kt in slot kt % NSTAGE)
+  static constexpr int NSTAGE = LDS_BUDGET / STAGE > 8 ? 8 : LDS_BUDGET / STAGE;
+  static constexpr int LDS_BYTES = NSTAGE * STAGE;
+  static_assert(NSTAGE >= 2, "at least two LDS stages");
+  static_assert(BK == 32 || BK == 64, "stage K");
   static constexpr int WM = BM >= 32 ? 2 : 1;
   static constexpr int WN = NW / WM;
   static constexpr int MI = BM / WM / 16;
@@ -111,6 +115,7 @@ struct TileGemmDirect {
   static constexpr int B_PW = B_INSTR / NW;
   // loads every wave issues per stage (waves with fewer A units wait for less)
   static constexpr int MIN_PW = A_INSTR / NW + B_PW;
+  static_assert((NSTAGE - 2) * (A_PW + B_PW) < 64, "vmcnt range");
   static_assert(B_INSTR % NW == 0, "B loads split evenly over the waves");
   static_assert(MI >= 1 && NI >= 1, "tile too small for the waves");
   static_assert(LDS_BYTES <= 160 * 1024, "LDS");
@@ -124,7 +129,14 @@ struct TileGemmDirect {
   int64_t K_;
 
   __device__ __forceinline__ static int bswz(int k) { return (k & 3) | (((k >> 3) & 1) << 2); }
-  __device__ __forceinline__ static int aswz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+  // A chunk swizzle: the 16 rows of an operand read hit 16 different 16-byte
+  // bank windows (8 chunks per 128-byte row, or 4 per 64-byte row)
+  __device__ __forceinline__ static int aswz(int r) {
+    if constexpr (ACH == 8)
+      return (r & 7) ^ ((r >> 3) & 1);
+    else
+      return (r >> 2) & 3;
+  }
 
   __device__ __forceinline__ void zero_acc() {
 #pragma unroll
@@ -150,11 +162,11 @@ struct TileGemmDirect {
     b_stage_bytes = (uint32_t)(BK * ldb * ES);
 #pragma unroll
     for (int t = 0; t < A_PW; ++t) {
-      const int q = wave + NW * t;  // A instruction index: rows 8q .. 8q + 7
+      const int q = wave + NW * t;  // A instruction index: 1 KB of consecutive rows
       uint32_t o = kOob;
       if (q < A_INSTR) {
-        const int r = 8 * q + (lane >> 3);
-        const int c = (lane & 7) ^ aswz(r);  // logical chunk stored in this lane's slot
+        const int r = q * (1024 / A_ROWB) + lane / ACH;
+        const int c = (lane % ACH) ^ aswz(r);  // logical chunk stored in this lane's slot
         const uint32_t ro = row_off(r);
         if (ro != kOob) o = ro + c * 16;
       }
@@ -181,8 +193,8 @@ struct TileGemmDirect {
       const int q = wave + NW * t;
       if (q < A_INSTR) {  // wave-uniform
         const int lane = threadIdx.x & 63;
-        const int r = 8 * q + (lane >> 3);
-        const int c = (lane & 7) ^ aswz(r);
+        const int r = q * (1024 / A_ROWB) + lane / ACH;
+        const int c = (lane % ACH) ^ aswz(r);
         const uint32_t o = (aoff[t] != kOob && k0 + c * 8 < K_) ? aoff[t] + (uint32_t)(k0 * ES)
                                                                 : kOob;
         dma16(rsrc_a, o, base + q * 1024);
@@ -265,92 +277,73 @@ struct TileGemmDirect {
     return *reinterpret_cast<const uint4*>(base + r * A_ROWB + ((c ^ aswz(r)) << 4));
   }
 
-  // One stage. Large tiles (MI > 4) keep only the B fragments of a K step
-  // resident and read A one 16-row block at a time, each feeding NB * NI
-  // MFMAs (fewer live registers next to the accumulators).
+  __device__ __forceinline__ void mfma_row(int i, const uint4& a, const uint4 (&b)[NB][NI]) {
+#pragma unroll
+    for (int m = 0; m < NB; ++m)
+#pragma unroll
+      for (int j = 0; j < NI; ++j)
+        acc[m][i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            __builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b[m][j]), acc[m][i][j],
+            0, 0, 0);
+  }
+
+  // One stage as a software pipeline over (K step, 16-row block): while the
+  // MFMAs of block i run, the A fragment of block i+1 is in flight, and at the
+  // end of a K step also the next step's B fragments, so LDS latency hides
+  // behind matrix work instead of stalling it.
   __device__ __forceinline__ void compute_stage(const char* base) {
-    if constexpr (MI > 4) {
+    Frags cur;
+    read_frags_b(base, 0, cur);
+    uint4 a_cur = read_a(base, 0, 0);
 #pragma unroll
-      for (int ks = 0; ks < KSTEPS; ++ks) {
-        Frags f;
-        read_frags_b(base, ks, f);
+    for (int ks = 0; ks < KSTEPS; ++ks) {
+      Frags nxt;
 #pragma unroll
-        for (int i = 0; i < MI; ++i) {
-          const uint4 a = read_a(base, ks, i);
-#pragma unroll
-          for (int m = 0; m < NB; ++m)
-#pragma unroll
-            for (int j = 0; j < NI; ++j)
-              acc[m][i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                  __builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, f.b[m][j]),
-                  acc[m][i][j], 0, 0, 0);
+      for (int i = 0; i < MI; ++i) {
+        uint4 a_nxt = a_cur;
+        if (i + 1 < MI) {
+          a_nxt = read_a(base, ks, i + 1);
+        } else if (ks + 1 < KSTEPS) {
+          read_frags_b(base, ks + 1, nxt);
+          a_nxt = read_a(base, ks + 1, 0);
         }
+        mfma_row(i, a_cur, cur.b);
+        a_cur = a_nxt;
       }
-    } else {
-#if MOE_FRAG_PIPE
-      Frags f[2];
-      read_frags(base, 0, f[0]);
+      if (ks + 1 < KSTEPS) {
 #pragma unroll
-      for (int ks = 0; ks < KSTEPS; ++ks) {
-        if (ks + 1 < KSTEPS) read_frags(base, ks + 1, f[(ks + 1) & 1]);
-        mfmas(f[ks & 1]);
-      }
-#else
+        for (int m = 0; m < NB; ++m)
 #pragma unroll
-      for (int ks = 0; ks < KSTEPS; ++ks) {
-        Frags f;
-        read_frags(base, ks, f);
-        mfmas(f);
+          for (int j = 0; j < NI; ++j) cur.b[m][j] = nxt.b[m][j];
       }
-#endif
     }
   }
 
-  // One K step: stage kt is in `cur`; `nxt2` (the buffer stage kt-1 used)
-  // receives stage kt+2.
-  __device__ __forceinline__ void step(const char* cur, char* nxt2, int kt) {
-    wait_vmcnt<MIN_PW>();  // this wave's stage-kt loads have landed
-    __syncthreads();        // ... and every wave's; stage kt-1 reads are done
-    issue_stage(nxt2, kt + 2);
-    compute_stage(cur);
-  }
-
-  // Full K loop over the stage buffers (distinct LDS objects, so the
-  // compiler can see that the loads in flight never write the buffer being
-  // read and needs no wait for them). Stages past the end of K are issued too
-  // (they load zeros without memory traffic) so every step has the same
-  // loads in flight.
-  __device__ __forceinline__ void mainloop(char* s0, char* s1, char* s2, int64_t K) {
+  // Full K loop over a ring of NSTAGE stage slots in one LDS array: NSTAGE-1
+  // stages are in flight; stage kt+NSTAGE-1 is issued right after the barrier
+  // that makes stage kt visible (and ends every read of the slot it reuses).
+  // Stages past the end of K are issued too (zeros, no memory traffic) so
+  // every step has the same loads in flight.
+  __device__ __forceinline__ void mainloop(char* lds, int64_t K) {
     zero_acc();
     K_ = K;
     const int nk = (int)((K + BK - 1) / BK);
     if (nk <= 0) return;
     wait_vmcnt<0>();  // nothing of an earlier tile still writing LDS
     __syncthreads();
-    if constexpr (NSTAGE == 3) {
-      issue_stage(s0, 0);
-      issue_stage(s1, 1);
-      for (int kt = 0; kt < nk; kt += 3) {
-        step(s0, s2, kt);
-        if (kt + 1 < nk) step(s1, s0, kt + 1);
-        if (kt + 2 < nk) step(s2, s1, kt + 2);
-      }
-    } else {
-      // two buffers: stage kt+1 is loaded while stage kt is multiplied
-      issue_stage(s0, 0);
-      for (int kt = 0; kt < nk; kt += 2) {
-        step2(s0, s1, kt);
-        if (kt + 1 < nk) step2(s1, s0, kt + 1);
-      }
+#pragma unroll
+    for (int s = 0; s + 1 < NSTAGE; ++s) issue_stage(lds + s * STAGE, s);
+    int slot = 0;                 // slot of stage kt
+    int slot_next = NSTAGE - 1;   // slot of stage kt + NSTAGE - 1
+    for (int kt = 0; kt < nk; ++kt) {
+      wait_vmcnt<(NSTAGE - 2) * MIN_PW>();  // this wave's stage-kt loads have landed
+      __syncthreads();                      // ... every wave's; stage kt-1 reads done
+      issue_stage(lds + slot_next * STAGE, kt + NSTAGE - 1);
+      compute_stage(lds + slot * STAGE);
+      slot = slot + 1 == NSTAGE ? 0 : slot + 1;
+      slot_next = slot_next + 1 == NSTAGE ? 0 : slot_next + 1;
     }
     wait_vmcnt<0>();
-  }
-
-  __device__ __forceinline__ void step2(const char* cur, char* nxt, int kt) {
-    wait_vmcnt<0>();   // this wave's stage-kt loads have landed
-    __syncthreads();   // ... and every wave's; stage kt-1 reads are done
-    issue_stage(nxt, kt + 1);
-    compute_stage(cur);
   }
 
   template <typename F>

@@ -28,10 +28,12 @@ template <typename T, int BM, int NB, int STAGING>
 struct TileSel {
   using type = TileGemm<T, BM, 128, NB, false, STAGING>;
 };
+#ifndef MOE_STAGE_K
+#define MOE_STAGE_K 64
+#endif
 template <int BM, int NB, int STAGING>
 struct TileSel<bf16_t, BM, NB, STAGING> {
-  // 256-row tiles need 64 KB per stage: two stages
-  using type = TileGemmDirect<BM, NB, 8, (BM >= 256 ? 2 : 3)>;
+  using type = TileGemmDirect<BM, NB, 8, MOE_STAGE_K>;
 };
 
 template <typename TG>
@@ -44,10 +46,8 @@ constexpr bool is_direct() {
 template <typename TG>
 __device__ __forceinline__ void run_mainloop(TG& g, char* dyn, int64_t K) {
   if constexpr (is_direct<TG>()) {
-    __shared__ __align__(16) char st0[TG::STAGE];
-    __shared__ __align__(16) char st1[TG::STAGE];
-    __shared__ __align__(16) char st2[TG::NSTAGE > 2 ? TG::STAGE : 16];
-    g.mainloop(st0, st1, st2, K);
+    __shared__ __align__(16) char ring[TG::LDS_BYTES];
+    g.mainloop(ring, K);
   } else {
     g.mainloop(dyn, K);
   }
