@@ -214,7 +214,7 @@ def main():
                   "touched_experts": cnt["touched"], "down_ms": down_ms,
                   "down_tflops": cnt["flops_down"] / (down_ms * 1e-3) / 1e12,
                   "setup_ms": stage_ms[0] / max(n_calls, 1),
-                  "finalize_ms": stage_ms[3] / max(n_calls, 1),
+                  "combine_ms": stage_ms[3] / max(n_calls, 1),
                   "wall_s": wall},
     }
     if not args.no_cpu_baseline:

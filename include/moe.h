@@ -85,12 +85,19 @@ typedef struct {
                           (the full softmax restricted and rescaled to sum 1);
                           0: the full softmax over all E scores at the chosen ids */
   int32_t dtype;       /* moe_dtype                                             */
-  int32_t flags;       /* 0, or MOE_OUTPUT_F32                                  */
+  int32_t flags;       /* 0 or a combination of the MOE_* flags below           */
 } moe_shape;
 
-/* flags: in bf16 mode, write O as fp32 (the fp32 accumulator itself, no final
+/* flags: in bf16 mode, write O as fp32 (the fp32 sum itself, no final
  * rounding to bf16). Ignored in fp32 mode, where O is fp32 anyway. */
 #define MOE_OUTPUT_F32 1
+/* flags: combine with fp32 atomic adds into one accumulator inside the down
+ * GEMM's epilogue, instead of the default: the epilogue writes each kept
+ * assignment's weighted row w * y to its own fp32 slot and one pass then adds
+ * each token's slots in slot order (then the shared expert's row), so the
+ * output is bit-reproducible run to run. The atomic form sums in whatever
+ * order the tiles finish. */
+#define MOE_COMBINE_ATOMIC 2
 
 /*
  * Gate scores and softmax top-k routing.
@@ -156,8 +163,10 @@ moe_status moe_align_block_size(const moe_shape* shape, const int32_t* topk_ids,
                                 void* workspace, size_t workspace_bytes, void* stream);
 
 /* Bytes of device workspace moe_forward needs for this shape. 0 on invalid
- * shape. Holds the fp32 combine accumulator (bf16 mode), the SwiGLU rows of
- * the routed and shared experts, and the task counters. */
+ * shape. Holds the SwiGLU rows of the routed and shared experts, the task
+ * counters, and the combine's fp32 slots [S*k][H] (+ [S][H] shared) and kept
+ * flags, or with MOE_COMBINE_ATOMIC the fp32 accumulator [S][H] (bf16
+ * output only). */
 size_t moe_forward_workspace_bytes(const moe_shape* shape);
 
 /*
@@ -174,7 +183,8 @@ size_t moe_forward_workspace_bytes(const moe_shape* shape);
  * O is fully overwritten. Tokens with no kept assignment (and no shared
  * expert) get O_t = 0. Accumulation is fp32; in bf16 mode h is stored as
  * bf16 and O is rounded once from fp32 to bf16, unless flags has
- * MOE_OUTPUT_F32 (then O is fp32).
+ * MOE_OUTPUT_F32 (then O is fp32). The sum over a token's experts runs in
+ * slot order (deterministic) unless flags has MOE_COMBINE_ATOMIC.
  *
  *   A         [S][H]              dtype
  *   W_up      [E][H][D]           dtype   (X in R^{E x H x D})
@@ -208,7 +218,8 @@ const char* moe_status_string(moe_status status);
  * events on its stream around each kernel it enqueues. moe_profile_collect
  * waits for those events, adds each stage's elapsed milliseconds to
  * stage_ms[stage] (stage_ms has room for max_stages floats; stages are
- * 0 = setup, 1 = up/gate GEMM, 2 = down GEMM, 3 = finalize), stores the
+ * 0 = setup, 1 = up/gate GEMM, 2 = down GEMM, 3 = combine / output cast),
+ * stores the
  * number of calls recorded in *n_calls, and forgets them. Not thread-safe.
  */
 moe_status moe_profile_enable(int enable);

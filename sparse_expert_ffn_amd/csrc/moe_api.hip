@@ -23,7 +23,7 @@ bool fits_buffer(int64_t bytes) { return bytes >= 0 && bytes < ((int64_t)1 << 31
 
 moe_status check_routing_dims(const moe_shape* s) {
   if (s == nullptr) return MOE_ERR_INVALID_ARGUMENT;
-  if (s->flags != 0 && s->flags != MOE_OUTPUT_F32) return MOE_ERR_INVALID_ARGUMENT;
+  if ((s->flags & ~(MOE_OUTPUT_F32 | MOE_COMBINE_ATOMIC)) != 0) return MOE_ERR_INVALID_ARGUMENT;
   if (s->dtype != MOE_F32 && s->dtype != MOE_BF16) return MOE_ERR_INVALID_ARGUMENT;
   if (s->S < 0 || s->E < 1 || s->k < 1 || s->k > s->E) return MOE_ERR_INVALID_ARGUMENT;
   if (s->E > kMaxE || s->k > kMaxK) return MOE_ERR_UNSUPPORTED;
@@ -74,25 +74,34 @@ AlignLayout align_layout(const moe_shape* s) {
   return L;
 }
 
-// bf16 output: accumulate in an fp32 workspace buffer, then cast into O.
-bool needs_cast(const moe_shape* s) {
+bool out_bf16(const moe_shape* s) {
   return s->dtype == MOE_BF16 && (s->flags & MOE_OUTPUT_F32) == 0;
 }
 
+bool atomic_combine(const moe_shape* s) { return (s->flags & MOE_COMBINE_ATOMIC) != 0; }
+
 struct ForwardLayout {
-  size_t counters, oacc, h, hs, total;
+  size_t counters, oacc, y, ys, kept, h, hs, total;
 };
 
 ForwardLayout forward_layout(const moe_shape* s) {
   const size_t es = s->dtype == MOE_BF16 ? 2 : 4;
   const int64_t BM = s->block_size;
-  const int64_t cap_rows = (s->S * s->k + s->E * (BM - 1) + BM - 1) / BM * BM;
+  const int64_t F = s->S * s->k;
+  const int64_t cap_rows = (F + s->E * (BM - 1) + BM - 1) / BM * BM;
   const int64_t s_rows = (s->S + BM - 1) / BM * BM;
+  const bool atom = atomic_combine(s);
   ForwardLayout L;
   L.counters = 0;
   L.oacc = round_up(kCounterInts * sizeof(int), kAlignUp);
-  const size_t oacc_bytes = needs_cast(s) ? (size_t)s->S * s->H * sizeof(float) : 0;
-  L.h = L.oacc + round_up(oacc_bytes, kAlignUp);
+  // atomic combine: fp32 accumulator unless O itself is fp32
+  const size_t oacc_bytes = (atom && out_bf16(s)) ? (size_t)s->S * s->H * sizeof(float) : 0;
+  L.y = L.oacc + round_up(oacc_bytes, kAlignUp);
+  const size_t y_bytes = atom ? 0 : (size_t)F * s->H * sizeof(float);
+  L.ys = L.y + round_up(y_bytes, kAlignUp);
+  const size_t ys_bytes = (atom || s->D_shared == 0) ? 0 : (size_t)s->S * s->H * sizeof(float);
+  L.kept = L.ys + round_up(ys_bytes, kAlignUp);
+  L.h = L.kept + round_up(atom ? 0 : (size_t)F, kAlignUp);
   L.hs = L.h + round_up((size_t)cap_rows * s->D * es, kAlignUp);
   L.total = L.hs + round_up((size_t)s_rows * s->D_shared * es, kAlignUp);
   return L;
@@ -264,8 +273,13 @@ moe_status moe_forward(const moe_shape* shape, const void* A, const void* W_up,
   p.expert_ids = expert_ids;
   p.ntpp = num_tokens_post_padded;
   p.O = O;
-  const bool cast = needs_cast(shape);
-  p.Oacc = cast ? reinterpret_cast<float*>(ws + L.oacc) : reinterpret_cast<float*>(O);
+  p.atomic_combine = atomic_combine(shape) ? 1 : 0;
+  p.out_bf16 = out_bf16(shape) ? 1 : 0;
+  p.Oacc = (p.atomic_combine && p.out_bf16) ? reinterpret_cast<float*>(ws + L.oacc)
+                                            : reinterpret_cast<float*>(O);
+  p.Y = reinterpret_cast<float*>(ws + L.y);
+  p.Ys = reinterpret_cast<float*>(ws + L.ys);
+  p.kept = reinterpret_cast<uint8_t*>(ws + L.kept);
   p.h = ws + L.h;
   p.hs = ws + L.hs;
   p.counters = reinterpret_cast<int*>(ws + L.counters);
@@ -284,14 +298,19 @@ moe_status moe_forward(const moe_shape* shape, const void* A, const void* W_up,
     std::lock_guard<std::mutex> lk(g_prof_mu);
     ++g_prof_calls;
   }
-  if (run_stage(0, hs, [&] { return launch_forward_setup(p, dt, hs); }) != hipSuccess)
+  if (run_stage(0, hs, [&] { return launch_forward_setup(p, hs); }) != hipSuccess)
     return MOE_ERR_HIP;
   if (run_stage(1, hs, [&] { return launch_forward_upgate(p, dt, BM, hs); }) != hipSuccess)
     return MOE_ERR_HIP;
   if (run_stage(2, hs, [&] { return launch_forward_down(p, dt, BM, hs); }) != hipSuccess)
     return MOE_ERR_HIP;
-  if (cast && run_stage(3, hs, [&] { return launch_forward_finalize(p, hs); }) != hipSuccess)
+  if (p.atomic_combine) {
+    if (p.out_bf16 &&
+        run_stage(3, hs, [&] { return launch_forward_finalize(p, hs); }) != hipSuccess)
+      return MOE_ERR_HIP;
+  } else if (run_stage(3, hs, [&] { return launch_forward_combine(p, hs); }) != hipSuccess) {
     return MOE_ERR_HIP;
+  }
   return MOE_OK;
 }
 

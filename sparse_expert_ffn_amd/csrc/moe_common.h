@@ -89,12 +89,17 @@ struct ForwardParams {
   const int32_t* sorted_ids;
   const int32_t* expert_ids;
   const int32_t* ntpp;
-  void* O;                // [S][H] dtype
-  float* Oacc;            // [S][H] fp32 accumulator (== O in fp32 mode)
+  void* O;                // [S][H] dtype (fp32 with out_f32)
+  float* Oacc;            // atomic combine: [S][H] fp32 accumulator (may be O)
+  float* Y;               // slot combine: [F][H] fp32 weighted rows
+  float* Ys;              // slot combine: [S][H] fp32 shared-expert rows
+  uint8_t* kept;          // slot combine: [F] 1 = assignment has a slot
   void* h;                // [cap_rows][D]
   void* hs;               // [round_up(S, BM)][Ds]
   int* counters;          // kCounterInts ints
   int64_t S, H, D, E, k, Ds, F;
+  int atomic_combine;     // 1: atomics into Oacc; 0: slots Y / Ys + combine pass
+  int out_bf16;           // O is bf16 (else fp32)
   int grid;               // persistent workgroups
 };
 
@@ -103,10 +108,11 @@ constexpr int kAlignSeg = 512;   // assignments per wave segment in the align ke
 hipError_t launch_gate(const GateParams& p, int dtype, hipStream_t st);
 hipError_t launch_topk(const TopkParams& p, hipStream_t st);
 hipError_t launch_align(const AlignParams& p, hipStream_t st);
-hipError_t launch_forward_setup(const ForwardParams& p, int dtype, hipStream_t st);
+hipError_t launch_forward_setup(const ForwardParams& p, hipStream_t st);
 hipError_t launch_forward_upgate(const ForwardParams& p, int dtype, int BM, hipStream_t st);
 hipError_t launch_forward_down(const ForwardParams& p, int dtype, int BM, hipStream_t st);
 hipError_t launch_forward_finalize(const ForwardParams& p, hipStream_t st);
+hipError_t launch_forward_combine(const ForwardParams& p, hipStream_t st);
 int forward_lds_ok(int dtype, int BM);
 
 }  // namespace moe

@@ -17,6 +17,8 @@
 // Inside a range the tasks of a group of kGroupBlocks consecutive m-blocks are
 // ordered n-tile-major: tasks running side by side share both the A rows of
 // a few m-blocks and the weight strips of a few n-tiles.
+#include <algorithm>
+
 #include "gemm_direct.h"
 #include "gemm_tile.h"
 
@@ -197,6 +199,9 @@ __global__ __launch_bounds__((tile_threads<T, BM, 2, 2>()), 1) void upgate_kerne
       if (!shared) {
         const int f = p.sorted_ids[b * BM + r];
         tok = f < p.F ? (int)(f / p.k) : -1;
+        // slot combine: the first n-tile's task of a block marks its kept
+        // assignments (the flags were cleared by the setup kernel)
+        if (!p.atomic_combine && j == 0 && f < p.F) p.kept[f] = 1;
       } else {
         const int64_t s = b * BM + r;
         tok = s < p.S ? (int)s : -1;
@@ -267,6 +272,7 @@ __global__ __launch_bounds__((tile_threads<T, BM, kDownStrips, 1>()), 1) void do
   extern __shared__ __align__(16) char smem[];
   __shared__ int64_t s_task;
   __shared__ int s_tok[BM];
+  __shared__ int s_f[BM];   // output row: slot f (routed) or token (shared)
   __shared__ float s_w[BM];
   const TaskSpace ts = task_space(p, BM, NT, p.H, p.H);
   int q = blockIdx.x % kXcds, tried = 0;
@@ -289,14 +295,17 @@ __global__ __launch_bounds__((tile_threads<T, BM, kDownStrips, 1>()), 1) void do
         const int f = p.sorted_ids[b * BM + r];
         if (f < p.F) {
           s_tok[r] = (int)(f / p.k);
+          s_f[r] = f;
           s_w[r] = p.topk_w[f];
         } else {
           s_tok[r] = -1;
+          s_f[r] = -1;
           s_w[r] = 0.f;
         }
       } else {
         const int64_t s = b * BM + r;
         s_tok[r] = s < p.S ? (int)s : -1;
+        s_f[r] = s_tok[r];
         s_w[r] = 1.f;
       }
     }
@@ -328,13 +337,23 @@ __global__ __launch_bounds__((tile_threads<T, BM, kDownStrips, 1>()), 1) void do
       return s_tok[r] >= 0 ? (uint32_t)(r * K * sizeof(T)) : kOob;
     }, Bm, bb, p.H, n0, nc);
     run_mainloop(g, smem, K);
-    float* O = p.Oacc;
     const int64_t H = p.H;
-    g.for_each([&](int m, int row, int col, float v) {
-      const int tok = s_tok[row];
-      const int64_t n = n0 + m * BN + col;
-      if (tok >= 0 && n < H) atomicAdd(O + (size_t)tok * H + n, s_w[row] * v);
-    });
+    if (p.atomic_combine) {
+      float* O = p.Oacc;
+      g.for_each([&](int m, int row, int col, float v) {
+        const int tok = s_tok[row];
+        const int64_t n = n0 + m * BN + col;
+        if (tok >= 0 && n < H) atomicAdd(O + (size_t)tok * H + n, s_w[row] * v);
+      });
+    } else {
+      // weighted row into its own slot: routed -> Y[f], shared -> Ys[token]
+      float* Yb = shared ? p.Ys : p.Y;
+      g.for_each([&](int m, int row, int col, float v) {
+        const int f = s_f[row];
+        const int64_t n = n0 + m * BN + col;
+        if (f >= 0 && n < H) Yb[(size_t)f * H + n] = s_w[row] * v;
+      });
+    }
   }
 }
 
@@ -421,26 +440,94 @@ int forward_lds_ok(int dtype, int BM) {
   return BM == 16 || BM == 32 || BM == 64 || BM == 128 || (BM == 256 && dtype == 1);
 }
 
-// ------------------------------------------------------- setup and finalize
-// Zero the fp32 accumulator and the task counters (a fill kernel rather than
-// a memset node, so the whole call can be captured in a HIP graph).
-__global__ __launch_bounds__(256) void setup_kernel(float* acc, int64_t n, int* counters) {
-  const int64_t n4 = n / 4;
+// ------------------------------------------------------- setup and combine
+// Clear what must start at zero with a fill kernel rather than a memset node,
+// so the whole call can be captured in a HIP graph: the task counters, and
+// either the fp32 accumulator (atomic combine) or the kept flags (slot combine).
+__global__ __launch_bounds__(256) void setup_kernel(float* acc, int64_t n, uint8_t* flags,
+                                                    int64_t nflags, int* counters) {
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   const int64_t i0 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  float4* a4 = reinterpret_cast<float4*>(acc);
-  for (int64_t i = i0; i < n4; i += stride) a4[i] = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int64_t i = n4 * 4 + i0; i < n; i += stride) acc[i] = 0.f;
+  if (acc != nullptr) {
+    const int64_t n4 = n / 4;
+    float4* a4 = reinterpret_cast<float4*>(acc);
+    for (int64_t i = i0; i < n4; i += stride) a4[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int64_t i = n4 * 4 + i0; i < n; i += stride) acc[i] = 0.f;
+  }
+  if (flags != nullptr) {
+    const int64_t n16 = nflags / 16;
+    uint4* f16 = reinterpret_cast<uint4*>(flags);
+    for (int64_t i = i0; i < n16; i += stride) f16[i] = make_uint4(0, 0, 0, 0);
+    for (int64_t i = n16 * 16 + i0; i < nflags; i += stride) flags[i] = 0;
+  }
   if (i0 < kCounterInts) counters[i0] = 0;
 }
 
-hipError_t launch_forward_setup(const ForwardParams& p, int dtype, hipStream_t st) {
-  (void)dtype;
-  const int64_t n = p.S * p.H;
-  int64_t blocks = (n / 4 + 255) / 256;
+hipError_t launch_forward_setup(const ForwardParams& p, hipStream_t st) {
+  float* acc = p.atomic_combine ? p.Oacc : nullptr;
+  const int64_t n = acc ? p.S * p.H : 0;
+  uint8_t* flags = p.atomic_combine ? nullptr : p.kept;
+  const int64_t nf = flags ? p.F : 0;
+  int64_t blocks = (std::max(n / 4, nf / 16) + 255) / 256;
   if (blocks < 1) blocks = 1;
   if (blocks > 4096) blocks = 4096;
-  hipLaunchKernelGGL(setup_kernel, dim3((unsigned)blocks), dim3(256), 0, st, p.Oacc, n, p.counters);
+  hipLaunchKernelGGL(setup_kernel, dim3((unsigned)blocks), dim3(256), 0, st, acc, n, flags, nf,
+                     p.counters);
+  return hipGetLastError();
+}
+
+// Slot combine: O[t][:] = sum_{j<k, kept} Y[t*k + j][:] (+ Ys[t][:]), summed in
+// that order in fp32, rounded once into O. 4 columns per thread step.
+template <bool OUT_BF16>
+__global__ __launch_bounds__(256) void combine_kernel(const float* Y, const float* Ys,
+                                                      const uint8_t* kept, void* O, int64_t S,
+                                                      int64_t H, int64_t k) {
+  const int64_t h4 = H / 4;
+  const int64_t total = S * h4;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += stride) {
+    const int64_t t = i / h4;
+    const int64_t c = (i - t * h4) * 4;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int64_t j = 0; j < k; ++j) {
+      const int64_t f = t * k + j;
+      if (kept[f]) {
+        const float4 y = *reinterpret_cast<const float4*>(Y + f * H + c);
+        acc.x += y.x;
+        acc.y += y.y;
+        acc.z += y.z;
+        acc.w += y.w;
+      }
+    }
+    if (Ys != nullptr) {
+      const float4 y = *reinterpret_cast<const float4*>(Ys + t * H + c);
+      acc.x += y.x;
+      acc.y += y.y;
+      acc.z += y.z;
+      acc.w += y.w;
+    }
+    if constexpr (OUT_BF16) {
+      const uint32_t w0 = f32_to_bf16(acc.x) | ((uint32_t)f32_to_bf16(acc.y) << 16);
+      const uint32_t w1 = f32_to_bf16(acc.z) | ((uint32_t)f32_to_bf16(acc.w) << 16);
+      *reinterpret_cast<uint2*>(reinterpret_cast<bf16_t*>(O) + t * H + c) = make_uint2(w0, w1);
+    } else {
+      *reinterpret_cast<float4*>(reinterpret_cast<float*>(O) + t * H + c) = acc;
+    }
+  }
+}
+
+hipError_t launch_forward_combine(const ForwardParams& p, hipStream_t st) {
+  const int64_t total = p.S * (p.H / 4);
+  if (total == 0) return hipSuccess;
+  int64_t blocks = (total + 255) / 256;
+  if (blocks > 8192) blocks = 8192;
+  const float* Ys = p.Ds > 0 ? p.Ys : nullptr;
+  if (p.out_bf16)
+    hipLaunchKernelGGL(combine_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, st, p.Y, Ys,
+                       p.kept, p.O, p.S, p.H, p.k);
+  else
+    hipLaunchKernelGGL(combine_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, st, p.Y, Ys,
+                       p.kept, p.O, p.S, p.H, p.k);
   return hipGetLastError();
 }
 

@@ -79,7 +79,7 @@ def test_gate_topk_validation(lib):
     assert gate(lib, shape(), A=FAKE + 4) == 2          # misaligned
     assert gate(lib, shape(S=0), ids=None, w=None) == 0  # empty call
     s = shape()
-    s.flags = 2
+    s.flags = 4                                         # undefined flag bit
     assert gate(lib, s) == 1
 
 

@@ -22,7 +22,7 @@ def orc():
     return oracle.default()
 
 
-def run_case(orc, wl, bm=None, li=None, logits=None, poison=True):
+def run_case(orc, wl, bm=None, li=None, logits=None, poison=True, atomic=False):
     """Oracle and GPU on one routing. bf16 layers run twice: with an fp32
     output (the parity bar applies to the fp32-accumulated result) and with a
     bf16 output (the bar plus that output's own rounding)."""
@@ -34,7 +34,7 @@ def run_case(orc, wl, bm=None, li=None, logits=None, poison=True):
     L = DeviceLayer(wl, li)
     outs = {}
     for out_f32 in ((False,) if wl.dtype == wk.F32 else (True, False)):
-        buf = buffers(wl, bm, out_f32)
+        buf = buffers(wl, bm, out_f32, atomic_combine=atomic)
         if poison:
             buf.forward_ws.fill_(0xFF)   # NaN patterns: any unwritten read shows up
             buf.align_ws.fill_(0xFF)
@@ -121,17 +121,38 @@ def test_all_dropped_but_shared(orc):
     assert err <= tol
 
 
-def test_repeat_calls_same_buffers(orc):
-    """Two forward passes on the same buffers give the same routing and an
-    output within the bar (fp32 atomics may reorder the combine's sums)."""
+@pytest.mark.parametrize("atomic", [False, True])
+def test_repeat_calls_same_buffers(orc, atomic):
+    """Two forward passes on the same buffers: the default slot combine is
+    bit-reproducible; the atomic combine may reorder its fp32 sums."""
     wl = wk.WORKLOADS["prefill_skew"].with_tokens(200)
     li = wk.draw_layer(wl)
     L = DeviceLayer(wl, li)
-    buf = buffers(wl, 64)
+    buf = buffers(wl, 64, atomic_combine=atomic)
     G = orc.gate_logits(li.A, li.Wr, li.bias)
     outs = []
     for _ in range(2):
         buf.route(logits_in=dev(G))
         outs.append(host(L.forward(buf)).copy())
     torch.cuda.synchronize()
-    assert np.max(np.abs(outs[0] - outs[1])) <= 1e-2 * np.sqrt(np.mean(outs[0] ** 2))
+    if atomic:
+        assert np.max(np.abs(outs[0] - outs[1])) <= 1e-2 * np.sqrt(np.mean(outs[0] ** 2))
+    else:
+        assert np.array_equal(outs[0], outs[1])
+
+
+ATOMIC_CASES = [("tiny_fp32", 64, 16), ("prefill_bal", 700, 256), ("prefill_skew", 300, 128),
+                ("decode", 64, 16), ("dsv3", 40, 128)]
+
+
+@pytest.mark.parametrize("name,S,bm", ATOMIC_CASES)
+def test_layer_parity_atomic_combine(orc, name, S, bm):
+    wl = wk.WORKLOADS[name].with_tokens(S)
+    err, tol, _, _ = run_case(orc, wl, bm, atomic=True)
+    assert err <= tol
+
+
+def test_capacity_drops_atomic(orc):
+    wl = _small(wk.BF16, capacity_factor=0.25)
+    err, tol, _, _ = run_case(orc, wl, 32, atomic=True)
+    assert err <= tol
