@@ -181,15 +181,17 @@ moe_status moe_gate_topk(const moe_shape* shape, const void* A, const void* W_ro
     G = logits_out;
   }
   hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+  TopkParams tp{G, topk_ids, topk_weights, shape->S, shape->E, shape->k, shape->renormalize};
   if (logits_in == nullptr) {
     GateParams gp{A, W_router, router_bias, logits_out, shape->S, shape->H, shape->E};
+    if (gate_topk_fusable(gp, shape->dtype))  // one kernel: scores and routing
+      return launch_gate_topk(gp, tp, hs) == hipSuccess ? MOE_OK : MOE_ERR_HIP;
     if (launch_gate(gp, shape->dtype, hs) != hipSuccess) return MOE_ERR_HIP;
   } else if (logits_out != nullptr && logits_out != logits_in) {
     if (hipMemcpyAsync(logits_out, logits_in, (size_t)shape->S * shape->E * sizeof(float),
                        hipMemcpyDeviceToDevice, hs) != hipSuccess)
       return MOE_ERR_HIP;
   }
-  TopkParams tp{G, topk_ids, topk_weights, shape->S, shape->E, shape->k, shape->renormalize};
   if (launch_topk(tp, hs) != hipSuccess) return MOE_ERR_HIP;
   return MOE_OK;
 }

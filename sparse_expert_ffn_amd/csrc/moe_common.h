@@ -106,6 +106,8 @@ struct ForwardParams {
 constexpr int kAlignSeg = 512;   // assignments per wave segment in the align kernels
 
 hipError_t launch_gate(const GateParams& p, int dtype, hipStream_t st);
+bool gate_topk_fusable(const GateParams& gp, int dtype);
+hipError_t launch_gate_topk(const GateParams& gp, const TopkParams& tp, hipStream_t st);
 hipError_t launch_topk(const TopkParams& p, hipStream_t st);
 hipError_t launch_align(const AlignParams& p, hipStream_t st);
 hipError_t launch_forward_setup(const ForwardParams& p, hipStream_t st);

@@ -21,6 +21,7 @@
 
 #include "gemm_direct.h"
 #include "gemm_tile.h"
+#include "topk.h"
 
 namespace moe {
 
@@ -89,15 +90,124 @@ __global__ __launch_bounds__(256) void gate_gemm_kernel(GateParams p) {
   });
 }
 
+// bf16 gate scores on the LDS-direct core (E a multiple of 8): BMG-row tiles,
+// 128 experts per tile, 72 KB of LDS so two workgroups share a CU.
+template <int BMG>
+__global__ __launch_bounds__(512, 2) void gate_gemm_direct_kernel(GateParams p) {
+  using TG = TileGemmDirect<BMG, 1, 8, 64, 72 * 1024>;
+  __shared__ __align__(16) char ring[TG::LDS_BYTES];
+  const int64_t n_tiles = (p.E + TG::BN - 1) / TG::BN;
+  const int64_t m0 = (int64_t)(blockIdx.x / n_tiles) * BMG;
+  const int64_t n0 = (int64_t)(blockIdx.x % n_tiles) * TG::BN;
+  TG g;
+  const char* Bm[1] = {reinterpret_cast<const char*>(p.Wr)};
+  const int64_t S = p.S, H = p.H;
+  const uint32_t bb[1] = {(uint32_t)(H * p.E * sizeof(bf16_t))};
+  const int64_t nc[1] = {p.E - n0};
+  g.setup(p.A, (uint32_t)(S * H * sizeof(bf16_t)), [&](int r) -> uint32_t {
+    const int64_t s = m0 + r;
+    return s < S ? (uint32_t)(s * H * sizeof(bf16_t)) : kOob;
+  }, Bm, bb, p.E, n0, nc);
+  g.mainloop(ring, p.H);
+  g.for_each([&](int, int row, int col, float v) {
+    const int64_t s = m0 + row, e = n0 + col;
+    if (s < p.S && e < p.E) {
+      float out = v;
+      if (p.bias) out = out + p.bias[e];
+      p.G[(size_t)s * p.E + e] = out;
+    }
+  });
+}
+
+template <int BMG>
+static hipError_t launch_gate_direct(const GateParams& p, hipStream_t st) {
+  const int64_t tiles = ((p.S + BMG - 1) / BMG) * ((p.E + 127) / 128);
+  hipLaunchKernelGGL(gate_gemm_direct_kernel<BMG>, dim3((unsigned)tiles), dim3(512), 0, st, p);
+  return hipGetLastError();
+}
+
+// Fused gate + top-k (the gate producing the routing table directly): one
+// workgroup computes the scores of BMG tokens for all E <= NB * 128 experts
+// on the LDS-direct core, stages the fp32 score tile (bias added) in LDS,
+// writes it to G coalesced, and each wave ranks its tokens from LDS.
+template <int BMG, int NB>
+__global__ __launch_bounds__(512, 1) void gate_topk_kernel(GateParams gp, TopkParams tp) {
+  using TG = TileGemmDirect<BMG, NB, 8, 64, 120 * 1024>;
+  static_assert(TG::LDS_BYTES >= BMG * NB * 128 * (int)sizeof(float), "score tile fits the ring");
+  __shared__ __align__(16) char ring[TG::LDS_BYTES];
+  __shared__ float s_sel[8][32];
+  const int64_t m0 = (int64_t)blockIdx.x * BMG;
+  const int64_t S = gp.S, H = gp.H, E = gp.E;
+  TG g;
+  const char* Bm[NB];
+  uint32_t bb[NB];
+  int64_t nc[NB];
+#pragma unroll
+  for (int m = 0; m < NB; ++m) {
+    Bm[m] = reinterpret_cast<const char*>(gp.Wr) + (size_t)m * 128 * sizeof(bf16_t);
+    bb[m] = (uint32_t)(H * E * sizeof(bf16_t)) - (uint32_t)(m * 128 * sizeof(bf16_t));
+    nc[m] = E - m * 128;
+  }
+  g.setup(gp.A, (uint32_t)(S * H * sizeof(bf16_t)), [&](int r) -> uint32_t {
+    const int64_t s = m0 + r;
+    return s < S ? (uint32_t)(s * H * sizeof(bf16_t)) : kOob;
+  }, Bm, bb, E, 0, nc);
+  g.mainloop(ring, H);
+  __syncthreads();  // every wave is done with the LDS ring
+  float* tile = reinterpret_cast<float*>(ring);  // [BMG][E] fp32 scores
+  g.for_each([&](int m, int row, int col, float v) {
+    const int64_t e = m * 128 + col;
+    if (e < E) tile[row * E + e] = gp.bias ? v + gp.bias[e] : v;
+  });
+  __syncthreads();
+  const int rows = (int)min<int64_t>(BMG, S - m0);
+  for (int i = threadIdx.x; i < rows * E; i += 512) gp.G[(size_t)m0 * E + i] = tile[i];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  for (int r = wave; r < rows; r += 8) {
+    const int64_t s = m0 + r;
+    topk_one(tile + r * E, E, tp.k, tp.renormalize, tp.ids + s * tp.k, tp.w + s * tp.k, lane,
+             s_sel[wave]);
+  }
+}
+
+template <int BMG, int NB>
+static hipError_t launch_gate_topk_t(const GateParams& gp, const TopkParams& tp,
+                                     hipStream_t st) {
+  const int64_t tiles = (gp.S + BMG - 1) / BMG;
+  hipLaunchKernelGGL((gate_topk_kernel<BMG, NB>), dim3((unsigned)tiles), dim3(512), 0, st, gp,
+                     tp);
+  return hipGetLastError();
+}
+
+bool gate_topk_fusable(const GateParams& gp, int dtype) {
+  return dtype == 1 && gp.E % 8 == 0 && gp.E <= 256;
+}
+
+hipError_t launch_gate_topk(const GateParams& gp, const TopkParams& tp, hipStream_t st) {
+  if (gp.S == 0) return hipSuccess;
+  const bool two = gp.E > 128;
+  // enough row tiles to cover the CUs, else smaller ones
+  if (gp.S >= 64 * 256) return two ? launch_gate_topk_t<64, 2>(gp, tp, st)
+                                   : launch_gate_topk_t<64, 1>(gp, tp, st);
+  if (gp.S >= 32 * 256) return two ? launch_gate_topk_t<32, 2>(gp, tp, st)
+                                   : launch_gate_topk_t<32, 1>(gp, tp, st);
+  return two ? launch_gate_topk_t<16, 2>(gp, tp, st) : launch_gate_topk_t<16, 1>(gp, tp, st);
+}
+
 hipError_t launch_gate(const GateParams& p, int dtype, hipStream_t st) {
   if (p.S == 0) return hipSuccess;
-  const int64_t tiles = ((p.S + kGateBM - 1) / kGateBM) * ((p.E + kGateBN - 1) / kGateBN);
   const bool ragged = (p.E % 8) != 0;
+  if (dtype == 1 && !ragged) {
+    // enough row tiles to cover the CUs, else smaller ones
+    const int64_t ntile = (p.E + 127) / 128;
+    if (((p.S + 63) / 64) * ntile >= 256) return launch_gate_direct<64>(p, st);
+    if (((p.S + 31) / 32) * ntile >= 128) return launch_gate_direct<32>(p, st);
+    return launch_gate_direct<16>(p, st);
+  }
+  const int64_t tiles = ((p.S + kGateBM - 1) / kGateBM) * ((p.E + kGateBN - 1) / kGateBN);
   if (dtype == 1) {
-    if (ragged)
-      hipLaunchKernelGGL((gate_gemm_kernel<bf16_t, true>), dim3((unsigned)tiles), dim3(256), 0, st, p);
-    else
-      hipLaunchKernelGGL((gate_gemm_kernel<bf16_t, false>), dim3((unsigned)tiles), dim3(256), 0, st, p);
+    hipLaunchKernelGGL((gate_gemm_kernel<bf16_t, true>), dim3((unsigned)tiles), dim3(256), 0, st, p);
   } else {
     if (ragged)
       hipLaunchKernelGGL((gate_gemm_kernel<float, true>), dim3((unsigned)tiles), dim3(256), 0, st, p);

@@ -3,80 +3,26 @@
 #include <float.h>
 
 #include "moe_common.h"
+#include "topk.h"
 
 namespace moe {
 
 // ------------------------------------------------------------------ top-k
-// One wave64 per token; lane l holds the scores of experts l, l+64, ... (E <=
-// 1024 -> at most 16 per lane). k rounds of: lane-local best, then a 6-step
-// butterfly over the wave; the order is (score descending, expert index
-// ascending), NaN ranking as -inf. The router weights are then computed in
-// double from the chosen fp32 scores and rounded once to fp32.
-constexpr int kTopkMaxPerLane = 16;
-
-__device__ __forceinline__ bool topk_better(float v, int i, float bv, int bi) {
-  return v > bv || (v == bv && i < bi);
-}
-
+// (per-token selection in topk.h, shared with the fused gate kernel)
 __global__ __launch_bounds__(256) void topk_softmax_kernel(TopkParams p) {
   __shared__ float s_sel[4][32];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int64_t s = (int64_t)blockIdx.x * 4 + wave;
-  if (s >= p.S) return;  // a whole wave leaves; no block barrier below
-  const int E = (int)p.E;
-  const int k = (int)p.k;
-  const float* g = p.G + (size_t)s * E;
-  float v[kTopkMaxPerLane];
-  uint32_t taken = 0;
-#pragma unroll
-  for (int i = 0; i < kTopkMaxPerLane; ++i) {
-    const int e = lane + 64 * i;
-    float x = (e < E) ? g[e] : -INFINITY;
-    v[i] = (x != x) ? -INFINITY : x;
-  }
-  for (int j = 0; j < k; ++j) {
-    float bv = -INFINITY;
-    int bi = 0x7fffffff;
-#pragma unroll
-    for (int i = 0; i < kTopkMaxPerLane; ++i) {
-      const int e = lane + 64 * i;
-      if (e < E && !((taken >> i) & 1u) && topk_better(v[i], e, bv, bi)) {
-        bv = v[i];
-        bi = e;
-      }
-    }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-      const float ov = __shfl_xor(bv, off);
-      const int oi = __shfl_xor(bi, off);
-      if (topk_better(ov, oi, bv, bi)) {
-        bv = ov;
-        bi = oi;
-      }
-    }
-    if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
-    if (lane == 0) {
-      p.ids[(size_t)s * k + j] = bi;
-      s_sel[wave][j] = bv;
-    }
-  }
-  if (lane == 0) {
-    const double m = (double)s_sel[wave][0];
-    double den = 0.0;
-    if (p.renormalize) {
-      for (int j = 0; j < k; ++j) den += exp((double)s_sel[wave][j] - m);
-    } else {
-      for (int e = 0; e < E; ++e) den += exp((double)g[e] - m);
-    }
-    for (int j = 0; j < k; ++j)
-      p.w[(size_t)s * k + j] = (float)(exp((double)s_sel[wave][j] - m) / den);
-  }
+  // each wave handles tokens s, s + 4 * gridDim.x, ... (no block barrier below)
+  for (int64_t s = (int64_t)blockIdx.x * 4 + wave; s < p.S; s += (int64_t)gridDim.x * 4)
+    topk_one(p.G + (size_t)s * p.E, p.E, p.k, p.renormalize, p.ids + (size_t)s * p.k,
+             p.w + (size_t)s * p.k, lane, s_sel[wave]);
 }
 
 hipError_t launch_topk(const TopkParams& p, hipStream_t st) {
   if (p.S == 0) return hipSuccess;
-  const unsigned blocks = (unsigned)((p.S + 3) / 4);
+  int64_t want = (p.S + 3) / 4;
+  const unsigned blocks = (unsigned)(want < 1024 ? want : 1024);
   hipLaunchKernelGGL(topk_softmax_kernel, dim3(blocks), dim3(256), 0, st, p);
   return hipGetLastError();
 }
@@ -119,11 +65,19 @@ __global__ __launch_bounds__(1024) void align_scan_kernel(AlignParams p) {
   const int E = (int)p.E;
   int64_t cnt = 0;
   if (e < E) {
-    for (int64_t seg = 0; seg < p.nseg; ++seg) {
-      int* c = p.seg_counts + (size_t)seg * E + e;
-      const int v = *c;
-      *c = (int)cnt;
-      cnt += v;
+    // exclusive prefix over segments, in place; loads issued 16 at a time so
+    // they overlap (each thread walks one expert's column)
+    constexpr int kBatch = 16;
+    int* col = p.seg_counts + e;
+    for (int64_t s0 = 0; s0 < p.nseg; s0 += kBatch) {
+      int v[kBatch];
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) v[u] = (s0 + u < p.nseg) ? col[(size_t)(s0 + u) * E] : 0;
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        if (s0 + u < p.nseg) col[(size_t)(s0 + u) * E] = (int)cnt;
+        cnt += v[u];
+      }
     }
   }
   const int64_t kept = (p.C > 0 && cnt > p.C) ? p.C : cnt;

@@ -90,3 +90,20 @@ def test_topk_fp32_mode_and_empty(orc):
     assert np.array_equal(ids, ids_o)
     shape = moe.make_shape(0, 8, 8, 8, 2)
     assert moe.moe_gate_topk(shape, None, None, None, None, None, None, None) == 0
+
+
+@pytest.mark.parametrize("name,S", CASES + [("prefill_bal", 16384), ("dsv3", 4096)])
+def test_fused_gate_topk_consistent(orc, name, S):
+    """Scores computed on the GPU (fused gate + top-k for bf16, E <= 256):
+    the oracle's top-k of the GPU's own scores reproduces its ids and weights
+    bit for bit."""
+    wl = wk.WORKLOADS[name].with_tokens(S)
+    A, Wr, bias = wk.draw_routing_inputs(wl)
+    buf = buffers(wl)
+    moe.moe_gate_topk(buf.shape, dev(A), dev(Wr), dev(bias), None, buf.logits, buf.topk_ids,
+                      buf.topk_weights)
+    torch.cuda.synchronize()
+    G = buf.logits.cpu().numpy()
+    ids_o, w_o = orc.topk_softmax(G, wl.k, wl.renormalize)
+    assert np.array_equal(buf.topk_ids.cpu().numpy(), ids_o)
+    assert np.array_equal(buf.topk_weights.cpu().numpy().view(np.uint32), w_o.view(np.uint32))
