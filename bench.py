@@ -39,6 +39,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=32)
     ap.add_argument("--workload", default="prefill_bal")
     ap.add_argument("--block-size", type=int, default=0)
+    ap.add_argument("--tokens", type=int, default=0,
+                    help="override the workload's token count S (capacity recomputed)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU work of the oracle baseline sample")
@@ -121,6 +123,8 @@ def main():
 
     moe.load_library()
     wl = wk.WORKLOADS[args.workload]
+    if args.tokens > 0:
+        wl = wl.with_tokens(args.tokens)
     bm = args.block_size or suggest_block_size(wl.S, wl.k, wl.E)
     dev = "cuda"
 

@@ -319,12 +319,63 @@ struct TileGemmDirect {
     }
   }
 
+  // The same for a wave whose row blocks i >= nact (0 <= nact < MI) hold
+  // only zero rows: their fragments and MFMAs are skipped (a block of
+  // padding rows contributes nothing; its accumulators stay zero).
+  __device__ __forceinline__ void compute_stage_partial(const char* base, int nact) {
+    if (nact <= 0) return;
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks) {
+      Frags f;
+      read_frags_b(base, ks, f);
+#pragma unroll
+      for (int i = 0; i < MI; ++i)
+        if (i < nact) mfma_row(i, read_a(base, ks, i), f.b);
+    }
+  }
+
+  // Number of this wave's 16-row blocks up to the last row for which
+  // valid(r) holds (r = tile row); blocks after it are padding only.
+  template <typename Valid>
+  __device__ __forceinline__ int active_blocks(Valid valid) const {
+    constexpr int R = BM / WM;  // rows per wave
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int wm0 = (wave / WN) * R;
+    int last = -1;
+#pragma unroll
+    for (int b = 0; b < R; b += 64) {
+      const int r = b + lane;
+      const uint64_t m = __ballot(r < R && valid(wm0 + r));
+      if (m) last = b + 63 - __clzll(m);
+    }
+    return __builtin_amdgcn_readfirstlane((last + 16) / 16);
+  }
+
   // Full K loop over a ring of NSTAGE stage slots in one LDS array: NSTAGE-1
   // stages are in flight; stage kt+NSTAGE-1 is issued right after the barrier
   // that makes stage kt visible (and ends every read of the slot it reuses).
   // Stages past the end of K are issued too (zeros, no memory traffic) so
-  // every step has the same loads in flight.
-  __device__ __forceinline__ void mainloop(char* lds, int64_t K) {
+  // every step has the same loads in flight. nact: this wave's row blocks
+  // that hold a row (active_blocks), MI when all do.
+  template <bool FULL>
+  __device__ __forceinline__ void kloop(char* lds, int nk, int nact) {
+    int slot = 0;                 // slot of stage kt
+    int slot_next = NSTAGE - 1;   // slot of stage kt + NSTAGE - 1
+    for (int kt = 0; kt < nk; ++kt) {
+      wait_vmcnt<(NSTAGE - 2) * MIN_PW>();  // this wave's stage-kt loads have landed
+      __syncthreads();                      // ... every wave's; stage kt-1 reads done
+      issue_stage(lds + slot_next * STAGE, kt + NSTAGE - 1);
+      if constexpr (FULL)
+        compute_stage(lds + slot * STAGE);
+      else
+        compute_stage_partial(lds + slot * STAGE, nact);
+      slot = slot + 1 == NSTAGE ? 0 : slot + 1;
+      slot_next = slot_next + 1 == NSTAGE ? 0 : slot_next + 1;
+    }
+  }
+
+  __device__ __forceinline__ void mainloop(char* lds, int64_t K, int nact = MI) {
     zero_acc();
     K_ = K;
     const int nk = (int)((K + BK - 1) / BK);
@@ -333,16 +384,10 @@ struct TileGemmDirect {
     __syncthreads();
 #pragma unroll
     for (int s = 0; s + 1 < NSTAGE; ++s) issue_stage(lds + s * STAGE, s);
-    int slot = 0;                 // slot of stage kt
-    int slot_next = NSTAGE - 1;   // slot of stage kt + NSTAGE - 1
-    for (int kt = 0; kt < nk; ++kt) {
-      wait_vmcnt<(NSTAGE - 2) * MIN_PW>();  // this wave's stage-kt loads have landed
-      __syncthreads();                      // ... every wave's; stage kt-1 reads done
-      issue_stage(lds + slot_next * STAGE, kt + NSTAGE - 1);
-      compute_stage(lds + slot * STAGE);
-      slot = slot + 1 == NSTAGE ? 0 : slot + 1;
-      slot_next = slot_next + 1 == NSTAGE ? 0 : slot_next + 1;
-    }
+    if (nact >= MI)
+      kloop<true>(lds, nk, MI);
+    else
+      kloop<false>(lds, nk, nact);
     wait_vmcnt<0>();
   }
 

@@ -31,12 +31,18 @@ template <typename T, int BM, int NB, int STAGING>
 struct TileSel {
   using type = TileGemm<T, BM, 128, NB, false, STAGING>;
 };
+// Stage K: 32 for 256-row tiles (four 32 KB stages, three in flight), 64
+// otherwise (measured). MOE_STAGE_K overrides it for all tiles.
 #ifndef MOE_STAGE_K
-#define MOE_STAGE_K 64
+#define MOE_STAGE_K 0
 #endif
+template <int BM>
+constexpr int stage_k() {
+  return MOE_STAGE_K > 0 ? MOE_STAGE_K : (BM >= 256 ? 32 : 64);
+}
 template <int BM, int NB, int STAGING>
 struct TileSel<bf16_t, BM, NB, STAGING> {
-  using type = TileGemmDirect<BM, NB, 8, MOE_STAGE_K>;
+  using type = TileGemmDirect<BM, NB, 8, stage_k<BM>()>;
 };
 
 template <typename TG>
@@ -44,13 +50,14 @@ constexpr bool is_direct() {
   return TG::THREADS == 512;
 }
 
-// Run the K loop of tile core TG. The direct core gets three static LDS
-// arrays (one per stage); the register-staged core uses the dynamic buffer.
-template <typename TG>
-__device__ __forceinline__ void run_mainloop(TG& g, char* dyn, int64_t K) {
+// Run the K loop of tile core TG. The direct core gets a static LDS ring and
+// skips each wave's row blocks past the last row for which valid(r) holds;
+// the register-staged core uses the dynamic buffer and computes every row.
+template <typename TG, typename Valid>
+__device__ __forceinline__ void run_mainloop(TG& g, char* dyn, int64_t K, Valid valid) {
   if constexpr (is_direct<TG>()) {
     __shared__ __align__(16) char ring[TG::LDS_BYTES];
-    g.mainloop(ring, K);
+    g.mainloop(ring, K, g.active_blocks(valid));
   } else {
     g.mainloop(dyn, K);
   }
@@ -338,7 +345,7 @@ __global__ __launch_bounds__((tile_threads<T, BM, 2, 2>()), 1) void upgate_kerne
       const int tok = s_tok[r];
       return tok >= 0 ? (uint32_t)((int64_t)tok * H * sizeof(T)) : kOob;
     }, Bm, bb, N, n0, nc);
-    run_mainloop(g, smem, p.H);
+    run_mainloop(g, smem, p.H, [&](int r) { return s_tok[r] >= 0; });
     T* out = reinterpret_cast<T*>(shared ? p.hs : p.h);
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
@@ -446,7 +453,7 @@ __global__ __launch_bounds__((tile_threads<T, BM, kDownStrips, 1>()), 1) void do
     g.setup(Ab, (uint32_t)(BM * K * sizeof(T)), [&](int r) -> uint32_t {
       return s_tok[r] >= 0 ? (uint32_t)(r * K * sizeof(T)) : kOob;
     }, Bm, bb, p.H, n0, nc);
-    run_mainloop(g, smem, K);
+    run_mainloop(g, smem, K, [&](int r) { return s_tok[r] >= 0; });
     const int64_t H = p.H;
     if (p.atomic_combine) {
       float* O = p.Oacc;

@@ -57,14 +57,17 @@ class MoEBuffers:
 def suggest_block_size(S: int, k: int, E: int) -> int:
     """Rows per sorted block from the mean rows per expert (vLLM's fused_moe
     note uses 16 / 32 / 64 as the token count grows; 128 and 256 for
-    prefill, where the larger tile halves the weight traffic per flop)."""
+    prefill, where the larger tile halves the weight traffic per flop).
+    From 96 rows per expert on, 256-row blocks: one block holds most
+    experts' rows (each expert's weights stream once) and the GEMM kernels
+    skip the 16-row groups of a block that hold only padding."""
     mean = S * k / max(E, 1)
     if mean <= 16:
         return 16
     if mean <= 48:
         return 32
-    if mean <= 96:
+    if mean <= 80:
         return 64
-    if mean < 192:
+    if mean < 96:
         return 128
     return 256
