@@ -125,7 +125,7 @@ def main():
     wl = wk.WORKLOADS[args.workload]
     if args.tokens > 0:
         wl = wl.with_tokens(args.tokens)
-    bm = args.block_size or suggest_block_size(wl.S, wl.k, wl.E)
+    bm = args.block_size or suggest_block_size(wl.S, wl.k, wl.E, wl.capacity, wl.dtype)
     dev = "cuda"
 
     def td(a):

@@ -142,7 +142,6 @@ __global__ __launch_bounds__(512, 1) void gate_topk_kernel(GateParams gp, TopkPa
   using TG = TileGemmDirect<BMG, NB, 8, 64, 120 * 1024>;
   static_assert(TG::LDS_BYTES >= BMG * NB * 128 * (int)sizeof(float), "score tile fits the ring");
   __shared__ __align__(16) char ring[TG::LDS_BYTES];
-  __shared__ float s_sel[8][32];
   const int64_t m0 = (int64_t)blockIdx.x * BMG;
   const int64_t S = gp.S, H = gp.H, E = gp.E;
   TG g;
@@ -173,8 +172,7 @@ __global__ __launch_bounds__(512, 1) void gate_topk_kernel(GateParams gp, TopkPa
   const int wave = threadIdx.x >> 6;
   for (int r = wave; r < rows; r += 8) {
     const int64_t s = m0 + r;
-    topk_one(tile + r * E, E, tp.k, tp.renormalize, tp.ids + s * tp.k, tp.w + s * tp.k, lane,
-             s_sel[wave]);
+    topk_one(tile + r * E, E, tp.k, tp.renormalize, tp.ids + s * tp.k, tp.w + s * tp.k, lane);
   }
 }
 

@@ -10,13 +10,12 @@ namespace moe {
 // ------------------------------------------------------------------ top-k
 // (per-token selection in topk.h, shared with the fused gate kernel)
 __global__ __launch_bounds__(256) void topk_softmax_kernel(TopkParams p) {
-  __shared__ float s_sel[4][32];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   // each wave handles tokens s, s + 4 * gridDim.x, ... (no block barrier below)
   for (int64_t s = (int64_t)blockIdx.x * 4 + wave; s < p.S; s += (int64_t)gridDim.x * 4)
     topk_one(p.G + (size_t)s * p.E, p.E, p.k, p.renormalize, p.ids + (size_t)s * p.k,
-             p.w + (size_t)s * p.k, lane, s_sel[wave]);
+             p.w + (size_t)s * p.k, lane);
 }
 
 hipError_t launch_topk(const TopkParams& p, hipStream_t st) {

@@ -54,20 +54,20 @@ class MoEBuffers:
         return self.forward(A, W_up, W_gate, W_down, Ws_up, Ws_gate, Ws_down, stream)
 
 
-def suggest_block_size(S: int, k: int, E: int) -> int:
-    """Rows per sorted block from the mean rows per expert (vLLM's fused_moe
-    note uses 16 / 32 / 64 as the token count grows; 128 and 256 for
-    prefill, where the larger tile halves the weight traffic per flop).
-    From 96 rows per expert on, 256-row blocks: one block holds most
-    experts' rows (each expert's weights stream once) and the GEMM kernels
-    skip the 16-row groups of a block that hold only padding."""
+def suggest_block_size(S: int, k: int, E: int, capacity: int = 0, dtype: int = 1) -> int:
+    """Rows per sorted block (vLLM's fused_moe note grows the block with the
+    token count: 16 / 32 / 64, larger for prefill). The GEMM kernels skip
+    16-row groups that hold only padding, so a block large enough for one
+    expert's rows costs little more than their own work and streams that
+    expert's weights once: pick the smallest block that holds the expected
+    largest expert, taken as 1.25x the mean rows per expert, or the
+    capacity when that is smaller (no expert keeps more). 256 for bf16 only."""
     mean = S * k / max(E, 1)
-    if mean <= 16:
-        return 16
-    if mean <= 48:
-        return 32
-    if mean <= 80:
-        return 64
-    if mean < 96:
-        return 128
-    return 256
+    want = 1.25 * mean
+    if capacity > 0:
+        want = min(want, capacity)
+    top = 256 if dtype == 1 else 128
+    for bm in (16, 32, 64, 128, 256):
+        if bm >= want or bm == top:
+            return bm
+    return top

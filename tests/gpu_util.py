@@ -76,7 +76,7 @@ def bf16_output_excess(g16, o):
 
 
 def block_size_for(wl):
-    return suggest_block_size(wl.S, wl.k, wl.E)
+    return suggest_block_size(wl.S, wl.k, wl.E, wl.capacity, wl.dtype)
 
 
 def buffers(wl, block_size=None, out_f32=False, atomic_combine=False):
