@@ -104,6 +104,7 @@ struct ForwardParams {
 };
 
 constexpr int kAlignSeg = 512;   // assignments per wave segment in the align kernels
+constexpr int64_t kAlignSmallF = 8192;  // up to this many: the one-workgroup align
 
 hipError_t launch_gate(const GateParams& p, int dtype, hipStream_t st);
 bool gate_topk_fusable(const GateParams& gp, int dtype);
