@@ -74,9 +74,9 @@ __device__ __forceinline__ int64_t wave_inclusive_scan(int64_t x, int lane) {
 // padding, the exclusive cumsum of the padded counts (wave scans, then the
 // wave totals), the outputs counts / offsets / kept / num_tokens_post_padded,
 // the sentinel slots and the expert of every block. Leaves the offsets
-// (s_off[E..1023] = total) and the kept counts in LDS.
+// (s_off[E..1023] = total), the kept and the padded counts in LDS.
 __device__ __forceinline__ void align_layout(const AlignParams& p, int64_t cnt, int64_t* s_off,
-                                             int* s_kept, int64_t* s_wsum) {
+                                             int* s_kept, int* s_pad, int64_t* s_wsum) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -94,6 +94,7 @@ __device__ __forceinline__ void align_layout(const AlignParams& p, int64_t cnt, 
   const int64_t off = before + incl - pad;
   s_off[tid] = (tid < E) ? off : total;
   s_kept[tid] = (int)kept;
+  s_pad[tid] = (int)pad;
   if (tid < E) {
     p.counts[tid] = (int32_t)kept;
     p.offsets[tid] = off;
@@ -101,17 +102,14 @@ __device__ __forceinline__ void align_layout(const AlignParams& p, int64_t cnt, 
   }
   if (tid == 0) *p.ntpp = (int32_t)total;
   __syncthreads();
-  // sentinels: slots kept .. pad-1 of every expert, (expert, slot) pairs
-  // spread over all threads (E * (BM - 1) fits in 32 bits: the sorted
-  // array's capacity does)
-  const int bm1 = (int)(BM - 1);
-  const int pairs = E * bm1;
-  for (int i = tid; i < pairs; i += 1024) {
-    const int ex = i / bm1;
-    const int r = i - ex * bm1;
+  // sentinels: slots kept .. pad-1 of every expert; wave w fills experts
+  // w, w + 16, ..., its lanes consecutive slots (every padded count fits in
+  // 32 bits: the sorted array's capacity does)
+  for (int ex = wave; ex < E; ex += 16) {
     const int kx = s_kept[ex];
-    const int64_t px = ((int64_t)kx + BM - 1) / BM * BM;  // padded count
-    if (kx + r < px) p.sorted_ids[s_off[ex] + kx + r] = (int32_t)p.F;
+    const int px = s_pad[ex];
+    int32_t* dst = p.sorted_ids + s_off[ex];
+    for (int r = kx + lane; r < px; r += 64) dst[r] = (int32_t)p.F;
   }
   // expert of every block: the last expert whose offset is <= the block start
   const int64_t nblocks = total / BM;
@@ -147,6 +145,7 @@ __global__ __launch_bounds__(1024) void align_scan_kernel(AlignParams p) {
   __shared__ int64_t s_wsum[16];
   __shared__ int64_t s_off[1024];
   __shared__ int s_kept[1024];
+  __shared__ int s_pad[1024];
   const int tid = threadIdx.x;
   const int E = (int)p.E;
   const int64_t nseg = p.nseg;
@@ -201,7 +200,7 @@ __global__ __launch_bounds__(1024) void align_scan_kernel(AlignParams p) {
         }
     }
   }
-  align_layout(p, cnt, s_off, s_kept, s_wsum);
+  align_layout(p, cnt, s_off, s_kept, s_pad, s_wsum);
 }
 
 // The whole align in one workgroup for small F: the 16 waves take 16
@@ -213,6 +212,7 @@ __global__ __launch_bounds__(1024) void align_small_kernel(AlignParams p) {
   __shared__ int64_t s_wsum[16];
   __shared__ int64_t s_off[1024];
   __shared__ int s_kept[1024];
+  __shared__ int s_pad[1024];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -235,7 +235,7 @@ __global__ __launch_bounds__(1024) void align_small_kernel(AlignParams p) {
     }
     cnt = run;
   }
-  align_layout(p, cnt, s_off, s_kept, s_wsum);  // ends with every LDS write visible
+  align_layout(p, cnt, s_off, s_kept, s_pad, s_wsum);  // ends with every LDS write visible
   int nbits = 0;
   while ((1 << nbits) < E) ++nbits;
   const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
