@@ -67,6 +67,23 @@ def layer_counts(wl, counts_e, bm):
             "bytes": bytes_w + bytes_io, "bytes_up": bytes_up}
 
 
+def measured_traffic(workload, block_size):
+    """HBM bytes per launch of the up/gate kernel from the committed counter
+    record (profiles/upgate_<workload>_traffic.json: FETCH_SIZE and
+    WRITE_SIZE per dispatch, scaled by a plain device copy's readings), or
+    None when there is no record for this workload and block size or the
+    kernel sources have changed since it was taken."""
+    from sparse_expert_ffn_amd import buildlib
+    path = os.path.join(ROOT, "profiles", f"upgate_{workload}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("block_size") != block_size or rec.get("source_sha256") != buildlib.source_digest():
+        return None
+    return float(rec["hbm_bytes_per_launch"])
+
+
 def copy_calibration():
     import torch
     n = 1 << 30
@@ -209,7 +226,8 @@ def main():
                    "D_shared": wl.D_shared, "capacity": wl.capacity, "block_size": bm,
                    "parallelism": "single GPU"},
         "roofline": {"bound": "mfma", "achieved": up_tflops, "peak": peak, "unit": "TFLOP/s",
-                     "frac": up_tflops / peak, "traffic": None,
+                     "frac": up_tflops / peak, "traffic": measured_traffic(wl.name, bm),
+                     "traffic_unit": "HBM bytes per launch",
                      "kernel": "up/gate grouped GEMM + SwiGLU",
                      "avg_launch_ms": up_ms, "flops_per_launch": cnt["flops_up"]},
         "layer": {"tflops": layer_tflops, "mfma_frac": layer_tflops / peak,

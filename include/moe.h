@@ -79,8 +79,9 @@ typedef struct {
                           ascending token order; those past slot C are dropped
                           and contribute nothing (weights are not rescaled).  */
   int32_t block_size;  /* BM rows per sorted block. moe_align_block_size
-                          accepts any value >= 1; moe_forward takes 16, 32, 64
-                          or 128 and must see the value the align call used.  */
+                          accepts any value >= 1; moe_forward takes 16, 32, 64,
+                          128, or 256 (bf16 only) and must see the value the
+                          align call used.                                      */
   int32_t renormalize; /* 1: router weights = softmax over the k chosen scores
                           (the full softmax restricted and rescaled to sum 1);
                           0: the full softmax over all E scores at the chosen ids */
@@ -198,9 +199,10 @@ size_t moe_forward_workspace_bytes(const moe_shape* shape);
  *                                 outputs for this shape
  *   O         [S][H]              dtype out (fp32 with MOE_OUTPUT_F32)
  *   workspace >= moe_forward_workspace_bytes(shape) bytes, any contents
- * Requires H, D, D_shared multiples of 8, block_size in {16,32,64,128}, 16-byte
- * aligned arrays, and each of A, one expert's weight matrix and the workspace's
- * SwiGLU rows under 2 GiB (else MOE_ERR_UNSUPPORTED).
+ * Requires H, D, D_shared multiples of 8, block_size in {16,32,64,128} (and
+ * 256 for bf16), 16-byte aligned arrays, and each of A, one expert's weight
+ * matrix and the workspace's SwiGLU rows under 2 GiB (else
+ * MOE_ERR_UNSUPPORTED).
  */
 moe_status moe_forward(const moe_shape* shape, const void* A, const void* W_up,
                        const void* W_gate, const void* W_down, const void* Ws_up,

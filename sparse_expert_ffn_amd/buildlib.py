@@ -24,6 +24,21 @@ def sources():
     return sorted(glob.glob(os.path.join(PKG, "csrc", "*.hip")))
 
 
+def source_digest() -> str:
+    """SHA-256 over what determines the compiled kernels: the HIP sources
+    and headers under csrc/ and the compiler flags. Measurement records
+    (hardware counters) carry it, so that a record taken on other kernels is
+    recognised as stale."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(PKG, "csrc", "*"))):
+        h.update(os.path.relpath(f, ROOT).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    h.update(" ".join(HIPCC_FLAGS).encode())
+    return h.hexdigest()
+
+
 def build(verbose: bool = False, extra: list[str] | None = None, out: str = LIB) -> str:
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
     cmd = [hipcc, *HIPCC_FLAGS, *(extra or []), "-I", os.path.join(ROOT, "include"),
