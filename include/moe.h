@@ -124,10 +124,21 @@ typedef struct {
  * and each of them under 2 GiB (else MOE_ERR_UNSUPPORTED).
  *   topk_ids     [S][k]   int32 out
  *   topk_weights [S][k]   fp32 out
+ *   workspace    >= moe_gate_workspace_bytes(shape) bytes, any contents; may
+ *                be NULL when that is 0. It holds per-split partial scores
+ *                when the GEMM is split along H (few tokens or a long H);
+ *                the splits are added in a fixed order, so the scores are
+ *                the same on every call. Too small: MOE_ERR_WORKSPACE_TOO_SMALL.
  */
 moe_status moe_gate_topk(const moe_shape* shape, const void* A, const void* W_router,
                          const float* router_bias, const float* logits_in, float* logits_out,
-                         int32_t* topk_ids, float* topk_weights, void* stream);
+                         int32_t* topk_ids, float* topk_weights, void* workspace,
+                         size_t workspace_bytes, void* stream);
+
+/* Bytes of device workspace moe_gate_topk needs for this shape when it
+ * computes the scores (depends on S, H, E, dtype only; 0 when the GEMM is
+ * not split). 0 on invalid shape. */
+size_t moe_gate_workspace_bytes(const moe_shape* shape);
 
 /* Bytes of device workspace moe_align_block_size needs for this shape
  * (depends on S, k, E only). 0 on invalid shape. */

@@ -15,7 +15,8 @@ import ctypes
 import os
 
 __all__ = ["MOE_F32", "MOE_BF16", "MoeError", "moe_shape", "make_shape", "load_library",
-           "moe_gate_topk", "moe_align_workspace_bytes", "moe_align_block_size",
+           "moe_gate_workspace_bytes", "moe_gate_topk", "moe_align_workspace_bytes",
+           "moe_align_block_size",
            "moe_forward_workspace_bytes", "moe_forward", "moe_status_string",
            "moe_profile_enable", "moe_profile_collect", "build", "LIB_PATH", "STATUS"]
 
@@ -33,7 +34,8 @@ STATUS = {0: "MOE_OK", 1: "MOE_ERR_INVALID_ARGUMENT", 2: "MOE_ERR_UNSUPPORTED",
           3: "MOE_ERR_WORKSPACE_TOO_SMALL", 4: "MOE_ERR_HIP"}
 
 # names of the entry points declared in include/moe.h
-EXPORTS = ("moe_gate_topk", "moe_align_workspace_bytes", "moe_align_block_size",
+EXPORTS = ("moe_gate_workspace_bytes", "moe_gate_topk", "moe_align_workspace_bytes",
+           "moe_align_block_size",
            "moe_forward_workspace_bytes", "moe_forward", "moe_status_string",
            "moe_profile_enable", "moe_profile_collect")
 
@@ -84,7 +86,9 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib = ctypes.CDLL(p)
     vp, i64, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t
     sp = ctypes.POINTER(moe_shape)
-    lib.moe_gate_topk.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.moe_gate_workspace_bytes.argtypes = [sp]
+    lib.moe_gate_workspace_bytes.restype = sz
+    lib.moe_gate_topk.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.moe_align_workspace_bytes.argtypes = [sp]
     lib.moe_align_workspace_bytes.restype = sz
     lib.moe_align_block_size.argtypes = [sp, vp, vp, vp, vp, vp, vp, sz, vp]
@@ -151,11 +155,16 @@ def moe_status_string(code: int) -> str:
     return load_library().moe_status_string(code).decode()
 
 
+def moe_gate_workspace_bytes(shape) -> int:
+    return int(load_library().moe_gate_workspace_bytes(ctypes.byref(shape)))
+
+
 def moe_gate_topk(shape, A, W_router, router_bias, logits_in, logits_out, topk_ids,
-                  topk_weights, stream=None, check=True) -> int:
+                  topk_weights, workspace=None, stream=None, check=True) -> int:
+    wa, wn = _ws(workspace)
     code = load_library().moe_gate_topk(
         ctypes.byref(shape), _addr(A), _addr(W_router), _addr(router_bias), _addr(logits_in),
-        _addr(logits_out), _addr(topk_ids), _addr(topk_weights), _stream(stream))
+        _addr(logits_out), _addr(topk_ids), _addr(topk_weights), wa, wn, _stream(stream))
     if check:
         _check("moe_gate_topk", code)
     return code

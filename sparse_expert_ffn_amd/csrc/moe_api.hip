@@ -162,9 +162,17 @@ const char* moe_status_string(moe_status status) {
   return "MOE_ERR_UNKNOWN";
 }
 
+size_t moe_gate_workspace_bytes(const moe_shape* shape) {
+  if (check_routing_dims(shape) != MOE_OK) return 0;
+  const GateSplit g = gate_split_plan(shape->S, shape->H, shape->E, shape->dtype);
+  if (g.splits < 2) return 0;
+  return round_up((size_t)g.splits * shape->S * shape->E * sizeof(float), kAlignUp);
+}
+
 moe_status moe_gate_topk(const moe_shape* shape, const void* A, const void* W_router,
                          const float* router_bias, const float* logits_in, float* logits_out,
-                         int32_t* topk_ids, float* topk_weights, void* stream) {
+                         int32_t* topk_ids, float* topk_weights, void* workspace,
+                         size_t workspace_bytes, void* stream) {
   moe_status st = check_routing_dims(shape);
   if (st != MOE_OK) return st;
   if (shape->renormalize != 0 && shape->renormalize != 1) return MOE_ERR_INVALID_ARGUMENT;
@@ -184,6 +192,15 @@ moe_status moe_gate_topk(const moe_shape* shape, const void* A, const void* W_ro
   TopkParams tp{G, topk_ids, topk_weights, shape->S, shape->E, shape->k, shape->renormalize};
   if (logits_in == nullptr) {
     GateParams gp{A, W_router, router_bias, logits_out, shape->S, shape->H, shape->E};
+    const GateSplit plan = gate_split_plan(shape->S, shape->H, shape->E, shape->dtype);
+    if (plan.splits >= 2) {  // H split: partial scores, then sum + routing
+      if (workspace == nullptr || workspace_bytes < moe_gate_workspace_bytes(shape))
+        return MOE_ERR_WORKSPACE_TOO_SMALL;
+      if (!aligned16(workspace)) return MOE_ERR_UNSUPPORTED;
+      return launch_gate_split(gp, tp, plan, static_cast<float*>(workspace), hs) == hipSuccess
+                 ? MOE_OK
+                 : MOE_ERR_HIP;
+    }
     if (gate_topk_fusable(gp, shape->dtype))  // one kernel: scores and routing
       return launch_gate_topk(gp, tp, hs) == hipSuccess ? MOE_OK : MOE_ERR_HIP;
     if (launch_gate(gp, shape->dtype, hs) != hipSuccess) return MOE_ERR_HIP;

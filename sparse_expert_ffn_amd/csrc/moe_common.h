@@ -106,6 +106,16 @@ struct ForwardParams {
 constexpr int kAlignSeg = 512;   // assignments per wave segment in the align kernels
 constexpr int64_t kAlignSmallF = 8192;  // up to this many: the one-workgroup align
 
+// The split gate: bmg rows per tile, the H loop cut into `splits` ranges of
+// kc elements (splits == 1: not split).
+struct GateSplit {
+  int bmg;
+  int splits;
+  int64_t kc;
+};
+GateSplit gate_split_plan(int64_t S, int64_t H, int64_t E, int dtype);
+hipError_t launch_gate_split(const GateParams& gp, const TopkParams& tp, const GateSplit& plan,
+                             float* part, hipStream_t st);
 hipError_t launch_gate(const GateParams& p, int dtype, hipStream_t st);
 bool gate_topk_fusable(const GateParams& gp, int dtype);
 hipError_t launch_gate_topk(const GateParams& gp, const TopkParams& tp, hipStream_t st);

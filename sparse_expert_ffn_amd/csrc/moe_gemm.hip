@@ -200,6 +200,128 @@ hipError_t launch_gate_topk(const GateParams& gp, const TopkParams& tp, hipStrea
   return two ? launch_gate_topk_t<16, 2>(gp, tp, st) : launch_gate_topk_t<16, 1>(gp, tp, st);
 }
 
+// Split gate (bf16, E <= 256, E % 8 == 0): when the fused kernel would have
+// few row tiles, or a long K loop per tile, the H loop is cut into `splits`
+// ranges of kc elements. gate_split_kernel writes each range's fp32 partial
+// scores to part[split][S][E]; gate_reduce_topk_kernel adds them in split
+// order (a fixed order: the same scores on every call), adds the bias,
+// writes G and ranks each token from LDS.
+GateSplit gate_split_plan(int64_t S, int64_t H, int64_t E, int dtype) {
+  GateSplit g{0, 1, 0};
+  if (dtype != 1 || E % 8 != 0 || E > 256 || S < 1 || H < 1) return g;
+  // the fused kernel's row tiles (see launch_gate_topk)
+  const int64_t bm_fused = S >= 64 * 256 ? 64 : (S >= 32 * 256 ? 32 : 16);
+  const int64_t fused_tiles = (S + bm_fused - 1) / bm_fused;
+  const int64_t stages = (H + 63) / 64;
+  if (fused_tiles >= 256 && stages <= 64) return g;  // fused kernel fills the GPU
+  const int bmg = S >= 4096 ? 64 : 16;
+  const int64_t tiles = (S + bmg - 1) / bmg * ((E + 127) / 128);
+  int64_t splits = std::max<int64_t>(1, 512 / tiles);
+  splits = std::min<int64_t>(splits, std::max<int64_t>(1, stages / 2));  // >= 2 stages each
+  splits = std::min<int64_t>(splits, 64);
+  if (splits < 2) return g;
+  const int64_t kc = (stages + splits - 1) / splits * 64;
+  g.bmg = bmg;
+  g.splits = (int)((H + kc - 1) / kc);  // no empty split
+  g.kc = kc;
+  return g.splits >= 2 ? g : GateSplit{0, 1, 0};
+}
+
+template <int BMG>
+__global__ __launch_bounds__(512, 2) void gate_split_kernel(GateParams p, float* part,
+                                                            int64_t kc) {
+  using TG = TileGemmDirect<BMG, 1, 8, 64, 72 * 1024>;
+  __shared__ __align__(16) char ring[TG::LDS_BYTES];
+  const int64_t n_tiles = (p.E + TG::BN - 1) / TG::BN;
+  const int64_t tiles = (p.S + BMG - 1) / BMG * n_tiles;
+  const int64_t sp = blockIdx.x / tiles;  // split (tiles of one split share W_router rows)
+  const int64_t tile = blockIdx.x - sp * tiles;
+  const int64_t m0 = (tile / n_tiles) * BMG;
+  const int64_t n0 = (tile % n_tiles) * TG::BN;
+  const int64_t k0 = sp * kc;
+  const int64_t K = min(kc, p.H - k0);
+  const int64_t S = p.S, H = p.H, E = p.E;
+  TG g;
+  const char* Bm[1] = {reinterpret_cast<const char*>(p.Wr) + (size_t)k0 * E * sizeof(bf16_t)};
+  const uint32_t bb[1] = {(uint32_t)((H - k0) * E * sizeof(bf16_t))};
+  const int64_t nc[1] = {E - n0};
+  const bf16_t* a0 = reinterpret_cast<const bf16_t*>(p.A) + k0;
+  g.setup(a0, (uint32_t)((S * H - k0) * sizeof(bf16_t)), [&](int r) -> uint32_t {
+    const int64_t s = m0 + r;
+    return s < S ? (uint32_t)(s * H * sizeof(bf16_t)) : kOob;
+  }, Bm, bb, E, n0, nc);
+  g.mainloop(ring, K);
+  float* out = part + (size_t)sp * S * E;
+  g.for_each([&](int, int row, int col, float v) {
+    const int64_t s = m0 + row, e = n0 + col;
+    if (s < S && e < E) out[(size_t)s * E + e] = v;
+  });
+}
+
+__global__ __launch_bounds__(256) void gate_reduce_topk_kernel(const float* part, int splits,
+                                                               GateParams gp, TopkParams tp) {
+  __shared__ float s_row[4][256];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int64_t S = gp.S, E = gp.E;
+  // a uniform loop (the block barriers below): 4 tokens per step
+  for (int64_t base = (int64_t)blockIdx.x * 4; base < S; base += (int64_t)gridDim.x * 4) {
+    const int64_t s = base + wave;
+    if (s < S) {
+      // lane: experts lane + 64 i (i < 4); the partials of 8 splits are
+      // loaded together, then added in split order
+      float acc[4];
+      const float* p0 = part + (size_t)s * E + lane;
+      const size_t step = (size_t)S * E;  // one split
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[i] = (lane + 64 * i < E) ? p0[64 * i] : 0.f;
+      for (int j0 = 1; j0 < splits; j0 += 8) {
+        float v[8][4];
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            v[u][i] = (j0 + u < splits && lane + 64 * i < E) ? p0[(j0 + u) * step + 64 * i] : 0.f;
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+          if (j0 + u < splits)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[i] += v[u][i];
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int64_t e = lane + 64 * i;
+        if (e < E) {
+          const float x = gp.bias ? acc[i] + gp.bias[e] : acc[i];
+          s_row[wave][e] = x;
+          gp.G[(size_t)s * E + e] = x;
+        }
+      }
+    }
+    __syncthreads();
+    if (s < S)
+      topk_one(s_row[wave], E, tp.k, tp.renormalize, tp.ids + s * tp.k, tp.w + s * tp.k, lane);
+    __syncthreads();
+  }
+}
+
+hipError_t launch_gate_split(const GateParams& gp, const TopkParams& tp, const GateSplit& plan,
+                             float* part, hipStream_t st) {
+  const int64_t tiles = (gp.S + plan.bmg - 1) / plan.bmg * ((gp.E + 127) / 128);
+  const unsigned grid = (unsigned)(tiles * plan.splits);
+  if (plan.bmg == 64)
+    hipLaunchKernelGGL(gate_split_kernel<64>, dim3(grid), dim3(512), 0, st, gp, part, plan.kc);
+  else
+    hipLaunchKernelGGL(gate_split_kernel<16>, dim3(grid), dim3(512), 0, st, gp, part, plan.kc);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t want = (gp.S + 3) / 4;
+  const unsigned blocks = (unsigned)(want < 1024 ? want : 1024);
+  hipLaunchKernelGGL(gate_reduce_topk_kernel, dim3(blocks), dim3(256), 0, st, part, plan.splits,
+                     gp, tp);
+  return hipGetLastError();
+}
+
 hipError_t launch_gate(const GateParams& p, int dtype, hipStream_t st) {
   if (p.S == 0) return hipSuccess;
   const bool ragged = (p.E % 8) != 0;

@@ -9,7 +9,7 @@ from __future__ import annotations
 import torch
 
 from . import (MOE_BF16, make_shape, moe_align_block_size, moe_align_workspace_bytes,
-               moe_forward, moe_forward_workspace_bytes, moe_gate_topk)
+               moe_forward, moe_forward_workspace_bytes, moe_gate_topk, moe_gate_workspace_bytes)
 
 
 class MoEBuffers:
@@ -28,6 +28,8 @@ class MoEBuffers:
         self.expert_ids = torch.empty(max(cap // block_size, 1), dtype=i32, device=dev)
         self.ntpp = torch.empty(1, dtype=i32, device=dev)
         self.expert_counts = torch.empty(E, dtype=i32, device=dev)
+        gate_ws = moe_gate_workspace_bytes(self.shape)
+        self.gate_ws = torch.empty(gate_ws, dtype=torch.uint8, device=dev) if gate_ws else None
         self.align_ws = torch.empty(max(moe_align_workspace_bytes(self.shape), 1),
                                     dtype=torch.uint8, device=dev)
         self.forward_ws = torch.empty(max(moe_forward_workspace_bytes(self.shape), 1),
@@ -36,7 +38,7 @@ class MoEBuffers:
 
     def route(self, A=None, W_router=None, router_bias=None, logits_in=None, stream=None):
         moe_gate_topk(self.shape, A, W_router, router_bias, logits_in, self.logits,
-                      self.topk_ids, self.topk_weights, stream)
+                      self.topk_ids, self.topk_weights, self.gate_ws, stream)
         moe_align_block_size(self.shape, self.topk_ids, self.sorted_ids, self.expert_ids,
                              self.ntpp, self.expert_counts, self.align_ws, stream)
 

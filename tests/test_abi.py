@@ -58,11 +58,12 @@ def shape(**kw):
 
 
 def gate(lib, s, **kw):
-    args = dict(A=FAKE, Wr=FAKE, bias=None, lin=None, lout=FAKE, ids=FAKE, w=FAKE)
+    args = dict(A=FAKE, Wr=FAKE, bias=None, lin=None, lout=FAKE, ids=FAKE, w=FAKE, ws=None,
+                wsn=0)
     args.update(kw)
     return lib.moe_gate_topk(ctypes.byref(s) if s is not None else None, args["A"], args["Wr"],
                              args["bias"], args["lin"], args["lout"], args["ids"], args["w"],
-                             None)
+                             args["ws"], args["wsn"], None)
 
 
 def test_gate_topk_validation(lib):
@@ -78,6 +79,13 @@ def test_gate_topk_validation(lib):
     assert gate(lib, shape(H=100)) == 2                 # H not a multiple of 8
     assert gate(lib, shape(), A=FAKE + 4) == 2          # misaligned
     assert gate(lib, shape(S=0), ids=None, w=None) == 0  # empty call
+    # few tokens and a long H: the GEMM is split along H and needs a workspace
+    dec = shape(S=64, H=2048, E=256, k=8)
+    need = moe.moe_gate_workspace_bytes(dec)
+    assert need > 0
+    assert gate(lib, dec) == 3                          # no workspace
+    assert gate(lib, dec, ws=FAKE, wsn=need - 1) == 3   # too small
+    assert gate(lib, dec, ws=FAKE + 4, wsn=need) == 2   # misaligned
     s = shape()
     s.flags = 4                                         # undefined flag bit
     assert gate(lib, s) == 1
@@ -101,6 +109,16 @@ def test_align_validation(lib):
 
 
 def test_workspace_sizes(lib):
+    # gate: split only for few row tiles or a long H (bf16, E <= 256); the
+    # partial scores of every split, fp32
+    assert moe.moe_gate_workspace_bytes(shape(S=16384, H=2048, E=64)) == 0
+    assert moe.moe_gate_workspace_bytes(shape(S=64, H=2048, E=256, dtype=moe.MOE_F32)) == 0
+    assert moe.moe_gate_workspace_bytes(shape(S=64, H=2048, E=1024, k=8)) == 0
+    d = moe.moe_gate_workspace_bytes(shape(S=64, H=2048, E=256, k=8))
+    assert d >= 2 * 64 * 256 * 4 and d % (64 * 256 * 4) == 0
+    v3 = moe.moe_gate_workspace_bytes(shape(S=4096, H=7168, E=256, k=8))
+    assert v3 >= 2 * 4096 * 256 * 4 and v3 % (4096 * 256 * 4) == 0
+    assert moe.moe_gate_workspace_bytes(shape(k=9)) == 0
     for bm in (1, 16, 48, 128):
         s = shape(block_size=bm)
         assert moe.moe_align_workspace_bytes(s) > 0

@@ -42,7 +42,7 @@ def test_fullsize(name):
     buf = buffers(wl, out_f32=True)
     log(f"[{name}] GPU gate scores, block size {buf.shape.block_size}")
     moe.moe_gate_topk(buf.shape, L.A, L.Wr, L.bias, None, buf.logits, buf.topk_ids,
-                      buf.topk_weights)
+                      buf.topk_weights, buf.gate_ws)
     torch.cuda.synchronize()
     G = buf.logits.cpu().numpy().astype(np.float64)
     gerr = float(np.max(np.abs(G - G_o)) / rms(G_o))

@@ -28,7 +28,7 @@ def test_gate_scores(orc, name, S):
     G_o = orc.gate_logits(A, Wr, bias)
     buf = buffers(wl)
     moe.moe_gate_topk(buf.shape, dev(A), dev(Wr), dev(bias), None, buf.logits, buf.topk_ids,
-                      buf.topk_weights)
+                      buf.topk_weights, buf.gate_ws)
     torch.cuda.synchronize()
     G = buf.logits.cpu().numpy()
     err = float(np.max(np.abs(G.astype(np.float64) - G_o)) / rms(G_o))
@@ -101,7 +101,7 @@ def test_fused_gate_topk_consistent(orc, name, S):
     A, Wr, bias = wk.draw_routing_inputs(wl)
     buf = buffers(wl)
     moe.moe_gate_topk(buf.shape, dev(A), dev(Wr), dev(bias), None, buf.logits, buf.topk_ids,
-                      buf.topk_weights)
+                      buf.topk_weights, buf.gate_ws)
     torch.cuda.synchronize()
     G = buf.logits.cpu().numpy()
     ids_o, w_o = orc.topk_softmax(G, wl.k, wl.renormalize)
