@@ -41,6 +41,9 @@ def parse():
     ap.add_argument("--block-size", type=int, default=0)
     ap.add_argument("--tokens", type=int, default=0,
                     help="override the workload's token count S (capacity recomputed)")
+    ap.add_argument("--sched", choices=("queue", "quota"), default="queue",
+                    help="grouped-GEMM scheduler: per-XCD atomic task queues (default) or "
+                         "the static per-expert workgroup quota (ablation baseline)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU work of the oracle baseline sample")
@@ -175,7 +178,7 @@ def main():
         Wsg = td(wk.draw_tensor(wl, wk.T_WSGATE, (wl.H, wl.D_shared), ssu))
         Wsd = td(wk.draw_tensor(wl, wk.T_WSDOWN, (wl.D_shared, wl.H), ssd))
     buf = MoEBuffers(wl.S, wl.H, wl.D, wl.E, wl.k, wl.D_shared, wl.capacity, bm,
-                     wl.renormalize, wl.dtype, device=dev)
+                     wl.renormalize, wl.dtype, sched_quota=args.sched == "quota", device=dev)
     stream = torch.cuda.current_stream()
 
     def step():
@@ -224,7 +227,7 @@ def main():
         "data": "synthetic (seeded PCG64 normals, pages' distributions)",
         "config": {"workload": wl.name, "S": wl.S, "H": wl.H, "D": wl.D, "E": wl.E, "k": wl.k,
                    "D_shared": wl.D_shared, "capacity": wl.capacity, "block_size": bm,
-                   "parallelism": "single GPU"},
+                   "scheduler": args.sched, "parallelism": "single GPU"},
         "roofline": {"bound": "mfma", "achieved": up_tflops, "peak": peak, "unit": "TFLOP/s",
                      "frac": up_tflops / peak, "traffic": measured_traffic(wl.name, bm),
                      "traffic_unit": "HBM bytes per launch",

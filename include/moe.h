@@ -99,6 +99,13 @@ typedef struct {
  * output is bit-reproducible run to run. The atomic form sums in whatever
  * order the tiles finish. */
 #define MOE_COMBINE_ATOMIC 2
+/* flags (ablation baseline, not for production): schedule the grouped GEMMs
+ * with a static per-expert quota of workgroups (about grid / E each, the
+ * fixed SMs-per-expert comparator of the Weave review, sections 1.2-1.3)
+ * instead of the atomic task queues with work stealing. Same tiles, same
+ * results; under a skewed routing the hot experts' workgroups queue while the
+ * others idle. */
+#define MOE_SCHED_QUOTA 4
 
 /*
  * Gate scores and softmax top-k routing.

@@ -23,7 +23,8 @@ bool fits_buffer(int64_t bytes) { return bytes >= 0 && bytes < ((int64_t)1 << 31
 
 moe_status check_routing_dims(const moe_shape* s) {
   if (s == nullptr) return MOE_ERR_INVALID_ARGUMENT;
-  if ((s->flags & ~(MOE_OUTPUT_F32 | MOE_COMBINE_ATOMIC)) != 0) return MOE_ERR_INVALID_ARGUMENT;
+  if ((s->flags & ~(MOE_OUTPUT_F32 | MOE_COMBINE_ATOMIC | MOE_SCHED_QUOTA)) != 0)
+    return MOE_ERR_INVALID_ARGUMENT;
   if (s->dtype != MOE_F32 && s->dtype != MOE_BF16) return MOE_ERR_INVALID_ARGUMENT;
   if (s->S < 0 || s->E < 1 || s->k < 1 || s->k > s->E) return MOE_ERR_INVALID_ARGUMENT;
   if (s->E > kMaxE || s->k > kMaxK) return MOE_ERR_UNSUPPORTED;
@@ -294,6 +295,7 @@ moe_status moe_forward(const moe_shape* shape, const void* A, const void* W_up,
   p.O = O;
   p.atomic_combine = atomic_combine(shape) ? 1 : 0;
   p.out_bf16 = out_bf16(shape) ? 1 : 0;
+  p.sched_quota = (shape->flags & MOE_SCHED_QUOTA) ? 1 : 0;
   p.Oacc = (p.atomic_combine && p.out_bf16) ? reinterpret_cast<float*>(ws + L.oacc)
                                             : reinterpret_cast<float*>(O);
   p.Y = reinterpret_cast<float*>(ws + L.y);

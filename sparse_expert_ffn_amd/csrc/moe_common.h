@@ -12,7 +12,13 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kXcds = 8;          // MI355X: 8 XCDs, workgroups dispatched round-robin
-constexpr int kCounterInts = 64;  // task counters at the head of the forward workspace
+// Task counters at the head of the forward workspace: per-XCD queues of the
+// two grouped GEMMs at [0, 16); with the per-expert quota scheduler, one
+// counter per expert plus one for the shared expert's tasks per GEMM at
+// kQuotaBase + g * kQuotaStride.
+constexpr int kQuotaBase = 64;
+constexpr int kQuotaStride = 1024 + 16;
+constexpr int kCounterInts = kQuotaBase + 2 * kQuotaStride;
 
 __device__ __forceinline__ float bf16_to_f32(bf16_t x) {
   return __uint_as_float(((uint32_t)x) << 16);
@@ -99,6 +105,7 @@ struct ForwardParams {
   int* counters;          // kCounterInts ints
   int64_t S, H, D, E, k, Ds, F;
   int atomic_combine;     // 1: atomics into Oacc; 0: slots Y / Ys + combine pass
+  int sched_quota;        // 1: static per-expert workgroup quota (ablation baseline)
   int out_bf16;           // O is bf16 (else fp32)
   int grid;               // persistent workgroups
 };

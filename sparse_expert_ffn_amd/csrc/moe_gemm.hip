@@ -382,6 +382,53 @@ __device__ __forceinline__ int64_t claim_task(int* counters, int64_t total, int&
   return -1;
 }
 
+// ---------------------------------------------------- quota scheduler
+// Ablation baseline (the Weave review's comparator, sections 1.2-1.3: a fixed
+// number of SMs per expert): workgroup g serves only the experts
+// [g*E/grid, max(g*E/grid + 1, (g+1)*E/grid)), so each expert gets about
+// grid/E workgroups whatever its load, and claims that expert's tasks from a
+// per-expert counter; afterwards, shared-expert tasks from one counter. The
+// returned task ids are those of the queue scheduler (same tiles, same
+// results).
+struct QuotaState {
+  int e, e_hi;
+  int64_t b0, nblk;  // current expert's blocks; b0 < 0: not looked up yet
+  int phase;         // 0 routed, 1 shared, 2 done
+};
+
+__device__ __forceinline__ QuotaState quota_init(int64_t E) {
+  QuotaState st;
+  const int64_t g = blockIdx.x, G = gridDim.x;
+  st.e = (int)(g * E / G);
+  st.e_hi = (int)max(g * E / G + 1, (g + 1) * E / G);
+  st.b0 = -1;
+  st.nblk = 0;
+  st.phase = 0;
+  return st;
+}
+
+// first block of the sorted expert ids with expert >= e (expert_ids ascend)
+__device__ __forceinline__ int64_t first_block(const int32_t* expert_ids, int64_t nb, int e) {
+  int64_t lo = 0, hi = nb;
+  while (lo < hi) {
+    const int64_t mid = (lo + hi) >> 1;
+    if (expert_ids[mid] < e)
+      lo = mid + 1;
+    else
+      hi = mid;
+  }
+  return lo;
+}
+
+// Task id of (m-block b, n-tile j) in the queue scheduler's order (the
+// inverse of decode_task).
+__device__ __forceinline__ int64_t encode_task(int64_t b, int64_t j, int64_t nb, int64_t nn) {
+  const int64_t grp = b / kGroupBlocks;
+  const int64_t b0 = grp * kGroupBlocks;
+  const int64_t gsz = min((int64_t)kGroupBlocks, nb - b0);
+  return grp * kGroupBlocks * nn + j * gsz + (b - b0);
+}
+
 struct TaskSpace {
   int64_t nb_r, nn_r, nb_s, nn_s, t_r, total;
 };
@@ -396,6 +443,39 @@ __device__ __forceinline__ TaskSpace task_space(const ForwardParams& p, int BM, 
   ts.t_r = ts.nb_r * ts.nn_r;
   ts.total = ts.t_r + ts.nb_s * ts.nn_s;
   return ts;
+}
+
+__device__ __forceinline__ int64_t claim_quota(const ForwardParams& p, const TaskSpace& ts,
+                                               int* ctr, QuotaState& st) {
+  for (;;) {
+    if (st.phase == 0) {
+      if (st.e >= st.e_hi) {
+        st.phase = 1;
+        continue;
+      }
+      if (st.b0 < 0) {
+        st.b0 = first_block(p.expert_ids, ts.nb_r, st.e);
+        st.nblk = first_block(p.expert_ids, ts.nb_r, st.e + 1) - st.b0;
+      }
+      const int64_t u = atomicAdd(&ctr[st.e], 1);
+      if (u < st.nblk * ts.nn_r)
+        return encode_task(st.b0 + u / ts.nn_r, u % ts.nn_r, ts.nb_r, ts.nn_r);
+      ++st.e;
+      st.b0 = -1;
+      continue;
+    }
+    if (st.phase == 1) {
+      st.phase = 2;
+      if (ts.total > ts.t_r) {
+        const int64_t u = atomicAdd(&ctr[kQuotaStride - 1], 1);
+        if (ts.t_r + u < ts.total) {
+          st.phase = 1;
+          return ts.t_r + u;
+        }
+      }
+    }
+    return -1;
+  }
 }
 
 // ---------------------------------------------------- up/gate GEMM + SwiGLU
@@ -418,9 +498,12 @@ __global__ __launch_bounds__((tile_threads<T, BM, 2, 2>()), 1) void upgate_kerne
   __shared__ int s_tok[BM];
   const TaskSpace ts = task_space(p, BM, BN, p.D, p.Ds);
   int q = blockIdx.x % kXcds, tried = 0;
+  QuotaState qs = quota_init(p.E);
   TG g;
   for (;;) {
-    if (threadIdx.x == 0) s_task = claim_task(p.counters, ts.total, q, tried);
+    if (threadIdx.x == 0)
+      s_task = p.sched_quota ? claim_quota(p, ts, p.counters + kQuotaBase, qs)
+                             : claim_task(p.counters, ts.total, q, tried);
     __syncthreads();
     const int64_t t = uniform64(s_task);
     if (t < 0) break;
@@ -514,9 +597,12 @@ __global__ __launch_bounds__((tile_threads<T, BM, kDownStrips, 1>()), 1) void do
   const TaskSpace ts = task_space(p, BM, NT, p.H, p.H);
   int q = blockIdx.x % kXcds, tried = 0;
   int* counters = p.counters + kXcds;
+  QuotaState qs = quota_init(p.E);
   TG g;
   for (;;) {
-    if (threadIdx.x == 0) s_task = claim_task(counters, ts.total, q, tried);
+    if (threadIdx.x == 0)
+      s_task = p.sched_quota ? claim_quota(p, ts, p.counters + kQuotaBase + kQuotaStride, qs)
+                             : claim_task(counters, ts.total, q, tried);
     __syncthreads();
     const int64_t t = uniform64(s_task);
     if (t < 0) break;
@@ -697,7 +783,7 @@ __global__ __launch_bounds__(256) void setup_kernel(float* acc, int64_t n, uint8
     for (int64_t i = i0; i < n16; i += stride) f16[i] = make_uint4(0, 0, 0, 0);
     for (int64_t i = n16 * 16 + i0; i < nflags; i += stride) flags[i] = 0;
   }
-  if (i0 < kCounterInts) counters[i0] = 0;
+  for (int64_t i = i0; i < kCounterInts; i += stride) counters[i] = 0;
 }
 
 hipError_t launch_forward_setup(const ForwardParams& p, hipStream_t st) {

@@ -87,7 +87,7 @@ def test_gate_topk_validation(lib):
     assert gate(lib, dec, ws=FAKE, wsn=need - 1) == 3   # too small
     assert gate(lib, dec, ws=FAKE + 4, wsn=need) == 2   # misaligned
     s = shape()
-    s.flags = 4                                         # undefined flag bit
+    s.flags = 8                                         # undefined flag bit
     assert gate(lib, s) == 1
 
 

@@ -156,3 +156,36 @@ def test_capacity_drops_atomic(orc):
     wl = _small(wk.BF16, capacity_factor=0.25)
     err, tol, _, _ = run_case(orc, wl, 32, atomic=True)
     assert err <= tol
+
+
+QUOTA_CASES = [("prefill_skew", 300, 128), ("dsv3", 40, 256), ("decode", 64, 16),
+               ("tiny_fp32", 64, 16), ("many_experts", 300, 32)]
+
+
+@pytest.mark.parametrize("name,S,bm", QUOTA_CASES)
+def test_quota_scheduler_same_output(orc, name, S, bm):
+    """The static per-expert quota scheduler (ablation baseline) runs the same
+    tiles as the queue scheduler: bit-identical output. many_experts has more
+    experts (600) than workgroups, so each workgroup serves several; dsv3 adds
+    the shared expert's tasks."""
+    if name == "many_experts":
+        wl = _small(wk.BF16, S=S, E=600, k=4)
+    else:
+        wl = wk.WORKLOADS[name].with_tokens(S)
+    li = wk.draw_layer(wl)
+    L = DeviceLayer(wl, li)
+    G = orc.gate_logits(li.A, li.Wr, li.bias)
+    outs = []
+    for quota in (False, True):
+        buf = buffers(wl, bm, out_f32=True, sched_quota=quota)
+        buf.forward_ws.fill_(0xFF)
+        buf.route(logits_in=dev(G))
+        outs.append(host(L.forward(buf)).copy())
+    torch.cuda.synchronize()
+    assert np.all(np.isfinite(outs[1]))
+    assert np.array_equal(outs[0], outs[1])
+    ref = orc.layer(li.A, li.Wr, li.bias, li.W_up, li.W_gate, li.W_down, wl.k,
+                    renormalize=wl.renormalize, capacity=wl.capacity, Ws_up=li.Ws_up,
+                    Ws_gate=li.Ws_gate, Ws_down=li.Ws_down, logits=G)
+    err, tol = parity(wl, outs[1], ref["O"])
+    assert err <= tol
