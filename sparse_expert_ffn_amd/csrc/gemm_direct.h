@@ -86,6 +86,7 @@ __device__ __forceinline__ void wait_vmcnt() {
 
 template <int BM_, int NB_, int NW_ = 8, int BK_ = 64, int LDS_BUDGET = 144 * 1024>
 struct TileGemmDirect {
+  static constexpr bool DIRECT = true;  // the LDS-direct core (vs gemm_tile.h)
   static constexpr int BM = BM_, BN = 128, NB = NB_;
   static constexpr int NW = NW_;              // waves per workgroup (2 per SIMD at 8)
   static constexpr int THREADS = 64 * NW;

@@ -57,6 +57,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 template <typename T, int BM_, int BN_, int NB_, bool RAGGED_B = false, int STAGING = 1>
 struct TileGemm {
   static constexpr int BM = BM_, BN = BN_, NB = NB_;
+  static constexpr bool DIRECT = false;  // register-staged core (vs gemm_direct.h)
   static constexpr int THREADS = 256;
   static constexpr int ES = sizeof(T);
   static constexpr int BK = 128 / ES;   // K elements per stage

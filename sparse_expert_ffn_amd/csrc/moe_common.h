@@ -111,7 +111,12 @@ struct ForwardParams {
 };
 
 constexpr int kAlignSeg = 512;   // assignments per wave segment in the align kernels
-constexpr int64_t kAlignSmallF = 8192;  // up to this many: the one-workgroup align
+#ifndef MOE_ALIGN_SMALL_F
+#define MOE_ALIGN_SMALL_F 16384
+#endif
+// Up to this many assignments the one-workgroup align; the crossover with the
+// three-launch path was measured between 16K and 32K assignments (E = 64, 256).
+constexpr int64_t kAlignSmallF = MOE_ALIGN_SMALL_F;
 
 // The split gate: bmg rows per tile, the H loop cut into `splits` ranges of
 // kc elements (splits == 1: not split).

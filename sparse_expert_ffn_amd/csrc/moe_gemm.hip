@@ -47,7 +47,7 @@ struct TileSel<bf16_t, BM, NB, STAGING> {
 
 template <typename TG>
 constexpr bool is_direct() {
-  return TG::THREADS == 512;
+  return TG::DIRECT;
 }
 
 // Run the K loop of tile core TG. The direct core gets a static LDS ring and
