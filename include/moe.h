@@ -94,10 +94,10 @@ typedef struct {
 #define MOE_OUTPUT_F32 1
 /* flags: combine with fp32 atomic adds into one accumulator inside the down
  * GEMM's epilogue, instead of the default: the epilogue writes each kept
- * assignment's weighted row w * y to its own fp32 slot and one pass then adds
- * each token's slots in slot order (then the shared expert's row), so the
- * output is bit-reproducible run to run. The atomic form sums in whatever
- * order the tiles finish. */
+ * assignment's row y to its own fp32 slot and one pass then adds each
+ * token's w * y (the product rounded to fp32) in slot order (then the shared
+ * expert's row), so the output is bit-reproducible run to run. The atomic
+ * form sums in whatever order the tiles finish. */
 #define MOE_COMBINE_ATOMIC 2
 /* flags (ablation baseline, not for production): schedule the grouped GEMMs
  * with a static per-expert quota of workgroups (about grid / E each, the

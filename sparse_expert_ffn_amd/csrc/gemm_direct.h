@@ -69,10 +69,33 @@ __device__ __forceinline__ i32x4_t make_srd(const void* base, uint32_t bytes) {
 // front of later LDS reads of other stage buffers: the K loop orders these
 // loads itself (vmcnt wait on the issuing wave, then a workgroup barrier).
 // The instruction has no register result.
+//
+// The compiler does not look inside the asm, so it does not insert the wait
+// states a vector memory instruction needs after a VALU op wrote one of its
+// SGPRs (5 on gfx9: v_readlane / v_readfirstlane results, or SGPRs restored
+// from VGPR lanes under SGPR pressure). SGPR_FROM_VALU = true puts them in the
+// asm (s_nop 4); the default form relies on the descriptor being built by
+// scalar code, which a test checks on the compiled kernels.
+template <bool SGPR_FROM_VALU = false>
 __device__ __forceinline__ void dma16(i32x4_t srd, uint32_t voff, const void* lds_dst) {
   const uint32_t m0v = (uint32_t)reinterpret_cast<uintptr_t>(
       (const __attribute__((address_space(3))) char*)lds_dst);
-  asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(srd), "{m0}"(m0v)
+  if constexpr (SGPR_FROM_VALU)
+    asm volatile("s_nop 4\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(srd),
+                 "{m0}"(m0v)
+                 : "memory");
+  else
+    asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(srd), "{m0}"(m0v)
+                 : "memory");
+}
+
+// 4 bytes per lane from buffer `srd` at byte offset voff into LDS at
+// lds_dst + 4 * lane (same form as dma16, with the wait states).
+__device__ __forceinline__ void dma4(i32x4_t srd, uint32_t voff, const void* lds_dst) {
+  const uint32_t m0v = (uint32_t)reinterpret_cast<uintptr_t>(
+      (const __attribute__((address_space(3))) char*)lds_dst);
+  asm volatile("s_nop 4\n\tbuffer_load_dword %0, %1, 0 offen lds" ::"v"(voff), "s"(srd),
+               "{m0}"(m0v)
                : "memory");
 }
 
@@ -185,6 +208,9 @@ struct TileGemmDirect {
   }
 
   // Issue the LDS-direct loads of K stage kt into the stage buffer `base`.
+  // SGPR_FROM_VALU: the caller cannot rule out that the compiler restores the
+  // buffer descriptors from VGPR lanes right before (see dma16).
+  template <bool SGPR_FROM_VALU = false>
   __device__ __forceinline__ void issue_stage(char* base, int kt) {
     // wave-uniform (scalar) so the buffer resources stay in SGPRs
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -198,7 +224,7 @@ struct TileGemmDirect {
         const int c = (lane % ACH) ^ aswz(r);
         const uint32_t o = (aoff[t] != kOob && k0 + c * 8 < K_) ? aoff[t] + (uint32_t)(k0 * ES)
                                                                 : kOob;
-        dma16(rsrc_a, o, base + q * 1024);
+        dma16<SGPR_FROM_VALU>(rsrc_a, o, base + q * 1024);
       }
     }
 #pragma unroll
@@ -210,7 +236,7 @@ struct TileGemmDirect {
       if constexpr (NB > 1) {
         if (m == 1) rb = rsrc_b[1];
       }
-      dma16(rb, o, base + A_LDS + q * 1024);
+      dma16<SGPR_FROM_VALU>(rb, o, base + A_LDS + q * 1024);
     }
   }
 
@@ -375,6 +401,9 @@ struct TileGemmDirect {
       slot_next = slot_next + 1 == NSTAGE ? 0 : slot_next + 1;
     }
   }
+
+  // K of the tile set up last (the streaming kernels set it per task).
+  __device__ __forceinline__ void set_k(int64_t K) { K_ = K; }
 
   __device__ __forceinline__ void mainloop(char* lds, int64_t K, int nact = MI) {
     zero_acc();

@@ -18,6 +18,7 @@
 // ordered n-tile-major: tasks running side by side share both the A rows of
 // a few m-blocks and the weight strips of a few n-tiles.
 #include <algorithm>
+#include <type_traits>
 
 #include "gemm_direct.h"
 #include "gemm_tile.h"
@@ -669,15 +670,238 @@ __global__ __launch_bounds__((tile_threads<T, BM, kDownStrips, 1>()), 1) void do
         if (tok >= 0 && n < H) atomicAdd(O + (size_t)tok * H + n, s_w[row] * v);
       });
     } else {
-      // weighted row into its own slot: routed -> Y[f], shared -> Ys[token]
+      // the row into its own slot: routed -> Y[f], shared -> Ys[token]; the
+      // combine applies the router weight
       float* Yb = shared ? p.Ys : p.Y;
       g.for_each([&](int m, int row, int col, float v) {
         const int f = s_f[row];
         const int64_t n = n0 + m * BN + col;
-        if (f >= 0 && n < H) Yb[(size_t)f * H + n] = s_w[row] * v;
+        if (f >= 0 && n < H) Yb[(size_t)f * H + n] = v;
       });
     }
   }
+}
+
+// ------------------------------------------ streaming down GEMM (bf16)
+// The persistent kernels above refill the LDS ring at every task: claim,
+// row metadata, the first stages' latency, then the epilogue's stores drain
+// before the next task's loads go out. With a short K loop (decode: 12
+// stages of the down projection) that is a large share of each task. Here
+// the ring streams across tasks instead:
+//  - each workgroup's tasks are fixed in advance (static_tasks: the XCD's
+//    contiguous range, one task per workgroup per round, the position in the
+//    round rotating with the round so that full and partial m-blocks spread
+//    evenly), so the next task is known without an atomic whose result would
+//    have to be waited for;
+//  - its row metadata (the m-block's sorted ids and expert) is copied into
+//    LDS by LDS-direct loads when the compute side starts the task before it;
+//  - the issue side moves on to the next task's stages NSTAGE-1 stages
+//    before the compute side finishes the current one, whose epilogue stores
+//    then drain behind loads already in flight.
+// Every iteration issues exactly one stage (zeros past the last task), so the
+// per-wave vmcnt waits of the direct core stay exact; extra loads and stores
+// only make them stricter. Requires at least 2*NSTAGE-1 K stages per task (the
+// metadata of task i+1 has then landed before the issue side reaches it).
+// Measured against the queue kernel: faster for short K loops over small
+// tiles (decode down, 16-row tiles, 12 stages: -10%), slower for long K
+// loops, for the up/gate projection and for tiles of uneven cost (skewed
+// routing at 128 rows: +26%, the static order loses the queue's balancing),
+// so the launcher uses it only there. Slot combine only (the epilogue writes
+// unweighted rows; no gather of weights).
+
+struct StaticTasks {
+  int64_t lo, n, R, r;  // XCD range start / size, its workgroups, this one's rank
+  __device__ __forceinline__ int64_t at(int64_t i) const {
+    const int64_t pos = i * R + (r + i) % R;
+    return pos < n ? lo + pos : -1;
+  }
+};
+
+__device__ __forceinline__ StaticTasks static_tasks(int64_t total) {
+  const int64_t G = gridDim.x, g = blockIdx.x;
+  const int64_t X = G < kXcds ? G : kXcds;
+  const int64_t x = g % X;
+  StaticTasks st;
+  st.lo = total * x / X;
+  st.n = total * (x + 1) / X - st.lo;
+  st.R = (G - x + X - 1) / X;
+  st.r = g / X;
+  return st;
+}
+
+struct StreamTask {
+  int64_t t, b, j, K, nk;  // t < 0: none
+  bool shared;
+};
+
+__device__ __forceinline__ StreamTask stream_task(const TaskSpace& ts, int64_t t, int64_t KR,
+                                                  int64_t KS, int BK) {
+  StreamTask k;
+  k.t = t;
+  k.shared = t >= ts.t_r;
+  k.b = k.j = 0;
+  k.K = k.nk = 0;
+  if (t < 0) return k;
+  if (!k.shared)
+    decode_task(t, ts.nb_r, ts.nn_r, k.b, k.j);
+  else
+    decode_task(t - ts.t_r, ts.nb_s, ts.nn_s, k.b, k.j);
+  k.K = k.shared ? KS : KR;
+  k.nk = (k.K + BK - 1) / BK;
+  return k;
+}
+
+// Row metadata of one task in LDS (routed tasks): the m-block's sorted ids
+// (F = sentinel) and its expert.
+struct StreamMeta {
+  int32_t f[256];
+  int32_t e[4];
+};
+
+template <int BM>
+__device__ __forceinline__ void stream_meta_direct(const ForwardParams& p, const StreamTask& k,
+                                                   StreamMeta& m) {
+  if (k.t < 0 || k.shared) return;
+  if (threadIdx.x < BM) m.f[threadIdx.x] = p.sorted_ids[k.b * BM + threadIdx.x];
+  if (threadIdx.x == 0) m.e[0] = p.expert_ids[k.b];
+}
+
+template <int BM>
+__device__ __forceinline__ void stream_meta_dma(const ForwardParams& p, const TaskSpace& ts,
+                                                const StreamTask& k, StreamMeta& m) {
+  if (k.t < 0 || k.shared) return;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (wave != 0) return;
+  const int lane = threadIdx.x & 63;
+  const i32x4_t srd_s = make_srd(p.sorted_ids, (uint32_t)(ts.nb_r * BM * sizeof(int32_t)));
+  const i32x4_t srd_e = make_srd(p.expert_ids, (uint32_t)(ts.nb_r * sizeof(int32_t)));
+  // (the descriptors may come back from VGPR lanes: the wait-state form)
+  if (lane < BM / 4) dma16<true>(srd_s, (uint32_t)(k.b * BM * 4 + lane * 16), m.f);
+  if (lane == 0) dma4(srd_e, (uint32_t)(k.b * 4), m.e);
+}
+
+// Row r of a task holds a row: routed, a sorted id below F; shared, a token.
+__device__ __forceinline__ bool stream_row_valid(const ForwardParams& p, const StreamTask& k,
+                                                 const StreamMeta& m, int BM, int r) {
+  return k.shared ? (k.b * BM + r < p.S) : (m.f[r] < p.F);
+}
+
+// Issue-side setup of task k (the expert's down strips, the h rows).
+template <typename TG>
+__device__ __forceinline__ void stream_setup(TG& g, const ForwardParams& p, const StreamTask& k,
+                                             const StreamMeta& m) {
+  constexpr int BM = TG::BM;
+  const int64_t H = p.H;
+  const int64_t K = k.K;
+  const int e = k.shared ? -1 : __builtin_amdgcn_readfirstlane(m.e[0]);
+  const int64_t n0 = k.j * kDownStrips * TG::BN;
+  const char* Wb = k.shared ? reinterpret_cast<const char*>(p.Wsd)
+                            : reinterpret_cast<const char*>(p.Wd) +
+                                  (size_t)e * p.D * p.H * sizeof(bf16_t);
+  const uint32_t wbytes = (uint32_t)(K * H * sizeof(bf16_t));
+  const char* Bm[kDownStrips];
+  uint32_t bb[kDownStrips];
+  int64_t nc[kDownStrips];
+#pragma unroll
+  for (int mm = 0; mm < kDownStrips; ++mm) {
+    Bm[mm] = Wb + (size_t)mm * TG::BN * sizeof(bf16_t);
+    bb[mm] = wbytes - (uint32_t)(mm * TG::BN * sizeof(bf16_t));
+    nc[mm] = H - n0 - mm * TG::BN;
+  }
+  const char* Ab = reinterpret_cast<const char*>(k.shared ? p.hs : p.h) +
+                   (size_t)k.b * BM * K * sizeof(bf16_t);
+  g.setup(Ab, (uint32_t)(BM * K * sizeof(bf16_t)), [&](int r) -> uint32_t {
+    return stream_row_valid(p, k, m, BM, r) ? (uint32_t)(r * K * sizeof(bf16_t)) : kOob;
+  }, Bm, bb, H, n0, nc);
+  g.set_k(K);
+}
+
+template <typename TG>
+__device__ __forceinline__ void stream_epilogue(const TG& g, const ForwardParams& p,
+                                                const StreamTask& k, const StreamMeta& m) {
+  constexpr int BM = TG::BM;
+  const int64_t H = p.H;
+  const int64_t n0 = k.j * kDownStrips * TG::BN;
+  float* Yb = k.shared ? p.Ys : p.Y;
+  g.for_each([&](int mm, int row, int col, float v) {
+    const int64_t n = n0 + mm * TG::BN + col;
+    if (stream_row_valid(p, k, m, BM, row) && n < H) {
+      const int64_t orow = k.shared ? k.b * BM + row : m.f[row];
+      Yb[(size_t)orow * H + n] = v;
+    }
+  });
+}
+
+template <int BM>
+__global__ __launch_bounds__(512, 1) void down_stream_kernel(ForwardParams p) {
+  using TG = typename TileSel<bf16_t, BM, kDownStrips, 1>::type;
+  static_assert(TG::DIRECT, "the streaming kernel runs on the LDS-direct core");
+  constexpr int NSTAGE = TG::NSTAGE;
+  __shared__ __align__(16) char ring[TG::LDS_BYTES];
+  __shared__ StreamMeta meta[2];
+  const TaskSpace ts = task_space(p, BM, kDownStrips * TG::BN, p.H, p.H);
+  const StaticTasks st = static_tasks(ts.total);
+  auto task = [&](int64_t i) { return stream_task(ts, st.at(i), p.D, p.Ds, TG::BK); };
+  StreamTask c = task(0);  // the task the compute side works on
+  if (c.t < 0) return;
+  stream_meta_direct<BM>(p, c, meta[0]);
+  stream_meta_direct<BM>(p, task(1), meta[1]);
+  __syncthreads();
+  TG g;
+  int64_t ii = 0;         // task the issue side is on
+  StreamTask is = c;
+  int64_t ikt = 0;        // its next stage
+  stream_setup(g, p, is, meta[0]);
+  auto issue_next = [&](int slot) {
+    if (ikt >= is.nk) {
+      const StreamTask nx = task(ii + 1);
+      if (nx.t >= 0) {  // its metadata landed at least NSTAGE iterations ago
+        ++ii;
+        is = nx;
+        ikt = 0;
+        stream_setup(g, p, is, meta[ii & 1]);
+      }
+    }
+    // (the wait-state form: under this kernel's SGPR pressure the compiler
+    // may restore the descriptors from VGPR lanes right before the loads)
+    g.template issue_stage<true>(ring + slot * TG::STAGE, (int)ikt);  // past the last task: zeros
+    ++ikt;
+  };
+  g.zero_acc();
+#pragma unroll
+  for (int sl = 0; sl + 1 < NSTAGE; ++sl) issue_next(sl);
+  int64_t ci = 0;         // compute task index
+  int slot_c = 0, slot_i = NSTAGE - 1;
+  int nact_c = g.active_blocks([&](int r) { return stream_row_valid(p, c, meta[0], BM, r); });
+  // one K loop per compute task, with or without the padding-block skip
+  // (separate loops: the accumulators are written on one path only)
+  auto kloop = [&](auto full) {
+    for (int64_t ckt = 0; ckt < c.nk; ++ckt) {
+      wait_vmcnt<(NSTAGE - 2) * TG::MIN_PW>();  // this wave's loads of the stage have landed
+      __syncthreads();                          // ... every wave's; the previous stage's reads done
+      issue_next(slot_i);
+      slot_i = slot_i + 1 == NSTAGE ? 0 : slot_i + 1;
+      if (ckt == 0 && ci >= 1) stream_meta_dma<BM>(p, ts, task(ci + 1), meta[(ci + 1) & 1]);
+      if constexpr (decltype(full)::value)
+        g.compute_stage(ring + slot_c * TG::STAGE);
+      else
+        g.compute_stage_partial(ring + slot_c * TG::STAGE, nact_c);
+      slot_c = slot_c + 1 == NSTAGE ? 0 : slot_c + 1;
+    }
+  };
+  for (;;) {
+    if (nact_c >= TG::MI)
+      kloop(std::true_type{});
+    else
+      kloop(std::false_type{});
+    stream_epilogue(g, p, c, meta[ci & 1]);
+    ++ci;
+    c = task(ci);
+    if (c.t < 0) break;
+    g.zero_acc();
+    nact_c = g.active_blocks([&](int r) { return stream_row_valid(p, c, meta[ci & 1], BM, r); });
+  }
+  wait_vmcnt<0>();  // no LDS-direct load may land after the workgroup ends
 }
 
 // dynamic LDS bytes of a persistent kernel (the direct core's stage buffers
@@ -722,6 +946,22 @@ constexpr int upgate_bn() { return 128; }
 template <int BM>
 constexpr int down_bn() { return 128; }
 
+// The streaming down kernel: bf16, slot combine, the queue scheduler (the
+// quota ablation keeps the kernels it compares), tiles of at most 32 rows
+// (a task's cost is then its weight stream, the same for every task: the
+// static order cannot fall out of balance) and 2*NSTAGE-1 .. 16 K stages per
+// task (routed and shared).
+template <int BM>
+static bool down_stream_ok(const ForwardParams& p) {
+  using TG = typename TileSel<bf16_t, BM, kDownStrips, 1>::type;
+  if (BM > 32) return false;
+  const int64_t kmin = p.Ds > 0 ? std::min(p.D, p.Ds) : p.D;
+  const int64_t kmax = p.Ds > 0 ? std::max(p.D, p.Ds) : p.D;
+  return !p.atomic_combine && !p.sched_quota &&
+         (kmin + TG::BK - 1) / TG::BK >= 2 * TG::NSTAGE - 1 &&
+         (kmax + TG::BK - 1) / TG::BK <= 16;
+}
+
 template <typename T, int BM>
 static hipError_t launch_upgate_t(const ForwardParams& p, hipStream_t st) {
   constexpr int BN = upgate_bn<BM>();
@@ -731,6 +971,10 @@ static hipError_t launch_upgate_t(const ForwardParams& p, hipStream_t st) {
 
 template <typename T, int BM>
 static hipError_t launch_down_t(const ForwardParams& p, hipStream_t st) {
+  if constexpr (sizeof(T) == 2) {
+    if (down_stream_ok<BM>(p))
+      return launch_persistent(down_stream_kernel<BM>, 0, 512, p, st);
+  }
   constexpr int BN = down_bn<BM>();
   return launch_persistent(down_kernel<T, BM, BN>, lds_bytes<T, BM, kDownStrips, 1>(),
                            tile_threads<T, BM, kDownStrips, 1>(), p, st);
@@ -799,12 +1043,14 @@ hipError_t launch_forward_setup(const ForwardParams& p, hipStream_t st) {
   return hipGetLastError();
 }
 
-// Slot combine: O[t][:] = sum_{j<k, kept} Y[t*k + j][:] (+ Ys[t][:]), summed in
-// that order in fp32, rounded once into O. 4 columns per thread step.
+// Slot combine: O[t][:] = sum_{j<k, kept} w[f] * Y[f][:] (f = t*k + j) (+ Ys[t][:]):
+// each product rounded to fp32, summed in slot order in fp32, rounded once
+// into O. 4 columns per thread step.
 template <bool OUT_BF16>
 __global__ __launch_bounds__(256) void combine_kernel(const float* Y, const float* Ys,
-                                                      const uint8_t* kept, void* O, int64_t S,
-                                                      int64_t H, int64_t k) {
+                                                      const uint8_t* kept, const float* w,
+                                                      void* O, int64_t S, int64_t H,
+                                                      int64_t k) {
   const int64_t h4 = H / 4;
   const int64_t total = S * h4;
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
@@ -816,10 +1062,11 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* Y, const floa
       const int64_t f = t * k + j;
       if (kept[f]) {
         const float4 y = *reinterpret_cast<const float4*>(Y + f * H + c);
-        acc.x += y.x;
-        acc.y += y.y;
-        acc.z += y.z;
-        acc.w += y.w;
+        const float wf = w[f];
+        acc.x += __fmul_rn(wf, y.x);  // the product rounded, not fused into the add
+        acc.y += __fmul_rn(wf, y.y);
+        acc.z += __fmul_rn(wf, y.z);
+        acc.w += __fmul_rn(wf, y.w);
       }
     }
     if (Ys != nullptr) {
@@ -847,10 +1094,10 @@ hipError_t launch_forward_combine(const ForwardParams& p, hipStream_t st) {
   const float* Ys = p.Ds > 0 ? p.Ys : nullptr;
   if (p.out_bf16)
     hipLaunchKernelGGL(combine_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, st, p.Y, Ys,
-                       p.kept, p.O, p.S, p.H, p.k);
+                       p.kept, p.topk_w, p.O, p.S, p.H, p.k);
   else
     hipLaunchKernelGGL(combine_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, st, p.Y, Ys,
-                       p.kept, p.O, p.S, p.H, p.k);
+                       p.kept, p.topk_w, p.O, p.S, p.H, p.k);
   return hipGetLastError();
 }
 
