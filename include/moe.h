@@ -234,15 +234,17 @@ const char* moe_status_string(moe_status status);
 
 /*
  * Per-stage timing of moe_forward (measurement aid, not part of the layer).
- * After moe_profile_enable(1), each moe_forward call records a pair of HIP
- * events on its stream around each kernel it enqueues. moe_profile_collect
+ * stages are 0 = setup, 1 = up/gate GEMM, 2 = down GEMM, 3 = combine /
+ * output cast. After moe_profile_enable(stage_mask) with bit s of stage_mask
+ * set, each moe_forward call records a pair of HIP events on its stream around
+ * the kernel of stage s; stage_mask 0 turns timing off, a mask outside 0..15
+ * returns MOE_ERR_INVALID_ARGUMENT. Each recorded pair adds two marker packets
+ * to the stream, so time only the stages you need. moe_profile_collect
  * waits for those events, adds each stage's elapsed milliseconds to
- * stage_ms[stage] (stage_ms has room for max_stages floats; stages are
- * 0 = setup, 1 = up/gate GEMM, 2 = down GEMM, 3 = combine / output cast),
- * stores the
+ * stage_ms[stage] (stage_ms has room for max_stages floats), stores the
  * number of calls recorded in *n_calls, and forgets them. Not thread-safe.
  */
-moe_status moe_profile_enable(int enable);
+moe_status moe_profile_enable(int stage_mask);
 moe_status moe_profile_collect(float* stage_ms, int max_stages, int* n_calls);
 
 #ifdef __cplusplus

@@ -205,8 +205,11 @@ def moe_forward(shape, A, W_up, W_gate, W_down, Ws_up, Ws_gate, Ws_down, topk_we
     return code
 
 
-def moe_profile_enable(enable: bool) -> None:
-    _check("moe_profile_enable", load_library().moe_profile_enable(1 if enable else 0))
+def moe_profile_enable(enable: bool, stages=(0, 1, 2, 3)) -> None:
+    """Time the given moe_forward stages (0 setup, 1 up/gate, 2 down, 3
+    combine) with HIP events on the call's stream, or stop timing."""
+    mask = sum(1 << s for s in set(stages)) if enable else 0
+    _check("moe_profile_enable", load_library().moe_profile_enable(mask))
 
 
 def moe_profile_collect(n_stages: int = 4):

@@ -116,6 +116,7 @@ struct ProfileRecord {
 
 std::mutex g_prof_mu;
 bool g_prof_on = false;
+unsigned g_prof_mask = 0;  // bit s: time stage s
 int g_prof_calls = 0;
 std::vector<ProfileRecord> g_prof;
 std::vector<hipEvent_t> g_event_pool;
@@ -134,7 +135,7 @@ hipEvent_t take_event() {
 // Launch one stage, bracketed by events when timing is on.
 template <typename F>
 hipError_t run_stage(int stage, hipStream_t st, F launch) {
-  if (!g_prof_on) return launch();
+  if (!g_prof_on || !((g_prof_mask >> stage) & 1u)) return launch();
   std::lock_guard<std::mutex> lk(g_prof_mu);
   ProfileRecord r{stage, take_event(), take_event()};
   if (r.start == nullptr || r.stop == nullptr) return hipErrorOutOfMemory;
@@ -335,9 +336,11 @@ moe_status moe_forward(const moe_shape* shape, const void* A, const void* W_up,
   return MOE_OK;
 }
 
-moe_status moe_profile_enable(int enable) {
+moe_status moe_profile_enable(int stage_mask) {
+  if (stage_mask < 0 || stage_mask > 15) return MOE_ERR_INVALID_ARGUMENT;
   std::lock_guard<std::mutex> lk(g_prof_mu);
-  g_prof_on = enable != 0;
+  g_prof_on = stage_mask != 0;
+  g_prof_mask = (unsigned)stage_mask;
   return MOE_OK;
 }
 
