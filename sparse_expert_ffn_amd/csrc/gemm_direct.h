@@ -41,11 +41,15 @@ typedef short i16x4_t __attribute__((ext_vector_type(4)));
 typedef int i32x4_t __attribute__((ext_vector_type(4)));
 
 // Schedule knobs (compile time, chosen by measurement):
-//  MOE_FRAG_PIPE  1: read the next K step's operand fragments before the
-//                 current step's MFMAs (two fragment register sets).
+//  MOE_PINGPONG   1: the two waves of each SIMD run half a stage apart
+//                 (kloop_pp), so one's LDS reads overlap the other's MFMAs.
 //  MOE_MFMA_PRIO  1: raise the wave's issue priority around its MFMA block.
-#ifndef MOE_FRAG_PIPE
-#define MOE_FRAG_PIPE 0
+#ifndef MOE_PINGPONG
+#define MOE_PINGPONG 0
+#endif
+//  MOE_A_DIST     A fragment reads in flight ahead of their MFMAs.
+#ifndef MOE_A_DIST
+#define MOE_A_DIST 3
 #endif
 #ifndef MOE_MFMA_PRIO
 #define MOE_MFMA_PRIO 0
@@ -132,6 +136,7 @@ struct TileGemmDirect {
   static constexpr int MI = BM / WM / 16;
   static constexpr int NI = BN / WN / 16;
   static constexpr int KSTEPS = BK / 32;
+  static constexpr int ADIST = MOE_A_DIST;
   // 1 KB (one wave instruction) units per stage
   static constexpr int A_INSTR = A_LDS / 1024;
   static constexpr int B_INSTR = B_LDS / 1024;
@@ -241,16 +246,9 @@ struct TileGemmDirect {
   }
 
   struct Frags {
-    uint4 a[MI];
     uint4 b[NB][NI];
   };
-
-  // Operand fragments of 32-wide K step ks of the stage buffer `base`.
-  __device__ __forceinline__ void read_frags(const char* base, int ks, Frags& f) const {
-#pragma unroll
-    for (int i = 0; i < MI; ++i) f.a[i] = read_a(base, ks, i);
-    read_frags_b(base, ks, f);
-  }
+  Frags fb_[KSTEPS];  // the stage's B fragments, one set per 32-wide K step
 
   __device__ __forceinline__ void read_frags_b(const char* base, int ks, Frags& f) const {
     const int lane = threadIdx.x & 63;
@@ -277,24 +275,6 @@ struct TileGemmDirect {
       }
   }
 
-  __device__ __forceinline__ void mfmas(const Frags& f) {
-#if MOE_MFMA_PRIO
-    __builtin_amdgcn_s_setprio(1);
-#endif
-#pragma unroll
-    for (int m = 0; m < NB; ++m)
-#pragma unroll
-      for (int i = 0; i < MI; ++i)
-#pragma unroll
-        for (int j = 0; j < NI; ++j)
-          acc[m][i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-              __builtin_bit_cast(bf16x8_t, f.a[i]), __builtin_bit_cast(bf16x8_t, f.b[m][j]),
-              acc[m][i][j], 0, 0, 0);
-#if MOE_MFMA_PRIO
-    __builtin_amdgcn_s_setprio(0);
-#endif
-  }
-
   __device__ __forceinline__ uint4 read_a(const char* base, int ks, int i) const {
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
@@ -314,50 +294,47 @@ struct TileGemmDirect {
             0, 0, 0);
   }
 
-  // One stage as a software pipeline over (K step, 16-row block): while the
-  // MFMAs of block i run, the A fragment of block i+1 is in flight, and at the
-  // end of a K step also the next step's B fragments, so LDS latency hides
-  // behind matrix work instead of stalling it.
-  __device__ __forceinline__ void compute_stage(const char* base) {
-    Frags cur;
-    read_frags_b(base, 0, cur);
-    uint4 a_cur = read_a(base, 0, 0);
+  // MFMAs of this wave's row blocks [LO, HI) over one stage, as straight-line
+  // code whose instruction order is pinned with scheduling-group barriers
+  // (the compiler's own schedule, at this register pressure, reads one A
+  // fragment at a time and waits for it before its MFMAs). Each K step reads
+  // its B fragments (READ_B; else they are in fb_ from an earlier call) and
+  // the first ADIST A fragments, then alternates the MFMAs of block i with
+  // the read of block i + ADIST: ADIST LDS reads stay in flight behind the
+  // matrix work.
+  template <int LO, int HI, bool READ_B>
+  __device__ __forceinline__ void compute_range(const char* base) {
+    if constexpr (HI > LO) {
+      constexpr int NBLK = HI - LO;
+      constexpr int D = ADIST < NBLK ? ADIST : NBLK;
 #pragma unroll
-    for (int ks = 0; ks < KSTEPS; ++ks) {
-      Frags nxt;
+      for (int ks = 0; ks < KSTEPS; ++ks) {
+        if constexpr (READ_B) read_frags_b(base, ks, fb_[ks]);
+        uint4 a[NBLK];
 #pragma unroll
-      for (int i = 0; i < MI; ++i) {
-        uint4 a_nxt = a_cur;
-        if (i + 1 < MI) {
-          a_nxt = read_a(base, ks, i + 1);
-        } else if (ks + 1 < KSTEPS) {
-          read_frags_b(base, ks + 1, nxt);
-          a_nxt = read_a(base, ks + 1, 0);
+        for (int i = 0; i < D; ++i) a[i] = read_a(base, ks, LO + i);
+        __builtin_amdgcn_sched_group_barrier(0x100, (READ_B ? 2 * NB * NI : 0) + D, 0);
+#pragma unroll
+        for (int i = 0; i < NBLK; ++i) {
+          if (i + D < NBLK) a[i + D] = read_a(base, ks, LO + i + D);
+          mfma_row(LO + i, a[i], fb_[ks].b);
+          __builtin_amdgcn_sched_group_barrier(0x008, NB * NI, 0);
+          if (i + D < NBLK) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         }
-        mfma_row(i, a_cur, cur.b);
-        a_cur = a_nxt;
-      }
-      if (ks + 1 < KSTEPS) {
-#pragma unroll
-        for (int m = 0; m < NB; ++m)
-#pragma unroll
-          for (int j = 0; j < NI; ++j) cur.b[m][j] = nxt.b[m][j];
       }
     }
   }
 
-  // The same for a wave whose row blocks i >= nact (0 <= nact < MI) hold
-  // only zero rows: their fragments and MFMAs are skipped (a block of
-  // padding rows contributes nothing; its accumulators stay zero).
-  __device__ __forceinline__ void compute_stage_partial(const char* base, int nact) {
-    if (nact <= 0) return;
-#pragma unroll
-    for (int ks = 0; ks < KSTEPS; ++ks) {
-      Frags f;
-      read_frags_b(base, ks, f);
-#pragma unroll
-      for (int i = 0; i < MI; ++i)
-        if (i < nact) mfma_row(i, read_a(base, ks, i), f.b);
+  // Row blocks [0, nact) of one stage (0 <= nact <= MI): blocks after the
+  // wave's last real row hold only padding, contribute nothing and are
+  // skipped (their accumulators stay zero).
+  template <int NA = MI>
+  __device__ __forceinline__ void compute_stage_n(const char* base, int nact) {
+    if constexpr (NA > 0) {
+      if (nact >= NA)
+        compute_range<0, NA, true>(base);
+      else
+        compute_stage_n<NA - 1>(base, nact);
     }
   }
 
@@ -379,26 +356,85 @@ struct TileGemmDirect {
     return __builtin_amdgcn_readfirstlane((last + 16) / 16);
   }
 
-  // Full K loop over a ring of NSTAGE stage slots in one LDS array: NSTAGE-1
-  // stages are in flight; stage kt+NSTAGE-1 is issued right after the barrier
-  // that makes stage kt visible (and ends every read of the slot it reuses).
-  // Stages past the end of K are issued too (zeros, no memory traffic) so
-  // every step has the same loads in flight. nact: this wave's row blocks
-  // that hold a row (active_blocks), MI when all do.
-  template <bool FULL>
-  __device__ __forceinline__ void kloop(char* lds, int nk, int nact) {
+  // K loop over a ring of NSTAGE stage slots in one LDS array for a wave
+  // with NA active row blocks: NSTAGE-1 stages are in flight; stage
+  // kt+NSTAGE-1 is issued right after the barrier that makes stage kt
+  // visible (and ends every read of the slot it reuses). Stages past the end
+  // of K are issued too (zeros, no memory traffic) so every step has the same
+  // loads in flight.
+  template <int NA>
+  __device__ __forceinline__ void kloop(char* lds, int nk) {
     int slot = 0;                 // slot of stage kt
     int slot_next = NSTAGE - 1;   // slot of stage kt + NSTAGE - 1
     for (int kt = 0; kt < nk; ++kt) {
       wait_vmcnt<(NSTAGE - 2) * MIN_PW>();  // this wave's stage-kt loads have landed
       __syncthreads();                      // ... every wave's; stage kt-1 reads done
       issue_stage(lds + slot_next * STAGE, kt + NSTAGE - 1);
-      if constexpr (FULL)
-        compute_stage(lds + slot * STAGE);
-      else
-        compute_stage_partial(lds + slot * STAGE, nact);
+      compute_range<0, NA, true>(lds + slot * STAGE);
       slot = slot + 1 == NSTAGE ? 0 : slot + 1;
       slot_next = slot_next + 1 == NSTAGE ? 0 : slot_next + 1;
+    }
+  }
+
+  // ---- ping-pong schedule (two waves per SIMD, half a stage apart)
+  // Waves 0 .. NW/2-1 lead, waves NW/2 .. NW-1 (the other wave of each SIMD:
+  // waves are placed on SIMDs round-robin) lag by one barrier. A stage is
+  // two halves with a barrier before each; half h runs the wave's row blocks
+  // [h MI/2, (h+1) MI/2) (half 0 also reads the stage's B fragments, kept in
+  // registers for half 1). Because the laggers pass each barrier one half
+  // behind, on every SIMD one wave waits for its LDS reads while the other's
+  // MFMAs run.
+  //
+  // Barrier numbering (leaders: P(kt) = #2kt+1, Q(kt) = #2kt+2; laggers take
+  // one extra barrier first, so their P(kt) = #2kt+2, Q(kt) = #2kt+3):
+  //  - stage kt+1 is read from P(kt+1) = #2kt+3 (leaders) on. Every wave waits
+  //    for its own stage-(kt+1) loads before its Q(kt), which is #2kt+2 or
+  //    #2kt+3: all of them have landed by #2kt+3.
+  //  - stage kt+NSTAGE-1 goes into the slot of stage kt-1 right after the
+  //    issuing wave's Q(kt) (#2kt+2 or later). The last reads of stage kt-1
+  //    are the laggers' second half, which ends at their P(kt) = #2kt+2.
+  //  - the leaders take one barrier after the loop, so both groups leave it
+  //    having passed the same number of barriers.
+  static constexpr bool PP_OK = MOE_PINGPONG && NW == 8 && MI >= 2 && MI % 2 == 0 && NSTAGE >= 3;
+
+  template <int NA>
+  __device__ __forceinline__ void kloop_pp(char* lds, int nk) {
+    constexpr int HB = MI / 2;
+    constexpr int H0 = NA < HB ? NA : HB;
+    const bool lag = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) >= NW / 2;
+    wait_vmcnt<(NSTAGE - 2) * MIN_PW>();  // this wave's stage-0 loads have landed
+    if (lag) __syncthreads();
+    int slot = 0;                // slot of stage kt
+    int slot_prev = NSTAGE - 1;  // slot of stage kt-1 = slot of stage kt+NSTAGE-1
+    for (int kt = 0; kt < nk; ++kt) {
+      __syncthreads();  // P(kt)
+      compute_range<0, H0, true>(lds + slot * STAGE);
+      wait_vmcnt<(NSTAGE - 3) * MIN_PW>();  // this wave's stage-(kt+1) loads have landed
+      __syncthreads();  // Q(kt)
+      issue_stage(lds + slot_prev * STAGE, kt + NSTAGE - 1);
+      compute_range<HB, NA, false>(lds + slot * STAGE);
+      slot_prev = slot;
+      slot = slot + 1 == NSTAGE ? 0 : slot + 1;
+    }
+    if (!lag) __syncthreads();
+  }
+
+  // The K loop for this wave's number of active row blocks (one
+  // instantiation per count, so that each is straight-line code).
+  template <int NA = MI>
+  __device__ __forceinline__ void kloop_n(char* lds, int nk, int nact) {
+    if constexpr (NA == 0) {
+      if constexpr (PP_OK)
+        kloop_pp<0>(lds, nk);
+      else
+        kloop<0>(lds, nk);
+    } else if (nact >= NA) {
+      if constexpr (PP_OK)
+        kloop_pp<NA>(lds, nk);
+      else
+        kloop<NA>(lds, nk);
+    } else {
+      kloop_n<NA - 1>(lds, nk, nact);
     }
   }
 
@@ -414,19 +450,21 @@ struct TileGemmDirect {
     __syncthreads();
 #pragma unroll
     for (int s = 0; s + 1 < NSTAGE; ++s) issue_stage(lds + s * STAGE, s);
-    if (nact >= MI)
-      kloop<true>(lds, nk, MI);
-    else
-      kloop<false>(lds, nk, nact);
+    kloop_n(lds, nk, nact);
     wait_vmcnt<0>();
   }
 
+  // f(matrix, tile row, tile column, value) for each accumulator element.
   template <typename F>
   __device__ __forceinline__ void for_each(F f) const {
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
-    const int wm0 = (wave / WN) * (BM / WM);
-    const int wn0 = (wave % WN) * (BN / WN);
+    // this lane's first row and column, opaque to the optimiser: the row and
+    // column indices are formed here rather than hoisted out of a caller's
+    // task loop and held in registers through its K loop
+    int lrow = (wave / WN) * (BM / WM) + (lane >> 4) * 4;
+    int lcol = (wave % WN) * (BN / WN) + (lane & 15);
+    asm volatile("" : "+v"(lrow), "+v"(lcol));
 #pragma unroll
     for (int m = 0; m < NB; ++m)
 #pragma unroll
@@ -435,7 +473,7 @@ struct TileGemmDirect {
         for (int j = 0; j < NI; ++j)
 #pragma unroll
           for (int r = 0; r < 4; ++r)
-            f(m, wm0 + i * 16 + (lane >> 4) * 4 + r, wn0 + j * 16 + (lane & 15), acc[m][i][j][r]);
+            f(m, lrow + i * 16 + r, lcol + j * 16, acc[m][i][j][r]);
   }
 };
 

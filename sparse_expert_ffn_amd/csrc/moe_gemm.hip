@@ -553,8 +553,12 @@ __global__ __launch_bounds__((tile_threads<T, BM, 2, 2>()), 1) void upgate_kerne
     T* out = reinterpret_cast<T*>(shared ? p.hs : p.h);
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
-    const int wm0 = (wave / TG::WN) * (BM / TG::WM);
-    const int wn0 = (wave % TG::WN) * (BN / TG::WN);
+    // this lane's first tile row and column; opaque to the optimiser, so the
+    // 32 row indices below are formed here, per task, instead of being
+    // hoisted out of the task loop and held in registers through the K loop
+    int lrow = (wave / TG::WN) * (BM / TG::WM) + (lane >> 4) * 4;
+    int lcol = (wave % TG::WN) * (BN / TG::WN) + (lane & 15);
+    asm volatile("" : "+v"(lrow), "+v"(lcol));
 #pragma unroll
     for (int i = 0; i < TG::MI; ++i) {
       // one 16-row block at a time: keeps the accumulator reads from being
@@ -564,8 +568,8 @@ __global__ __launch_bounds__((tile_threads<T, BM, 2, 2>()), 1) void upgate_kerne
       for (int jj = 0; jj < TG::NI; ++jj)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const int row = wm0 + i * 16 + (lane >> 4) * 4 + r;
-          const int64_t col = n0 + wn0 + jj * 16 + (lane & 15);
+          const int row = lrow + i * 16 + r;
+          const int64_t col = n0 + lcol + jj * 16;
           if (s_tok[row] >= 0 && col < N) {
             const float u = g.acc[0][i][jj][r];
             const float gv = g.acc[1][i][jj][r];
@@ -873,27 +877,16 @@ __global__ __launch_bounds__(512, 1) void down_stream_kernel(ForwardParams p) {
   int64_t ci = 0;         // compute task index
   int slot_c = 0, slot_i = NSTAGE - 1;
   int nact_c = g.active_blocks([&](int r) { return stream_row_valid(p, c, meta[0], BM, r); });
-  // one K loop per compute task, with or without the padding-block skip
-  // (separate loops: the accumulators are written on one path only)
-  auto kloop = [&](auto full) {
+  for (;;) {
     for (int64_t ckt = 0; ckt < c.nk; ++ckt) {
       wait_vmcnt<(NSTAGE - 2) * TG::MIN_PW>();  // this wave's loads of the stage have landed
       __syncthreads();                          // ... every wave's; the previous stage's reads done
       issue_next(slot_i);
       slot_i = slot_i + 1 == NSTAGE ? 0 : slot_i + 1;
       if (ckt == 0 && ci >= 1) stream_meta_dma<BM>(p, ts, task(ci + 1), meta[(ci + 1) & 1]);
-      if constexpr (decltype(full)::value)
-        g.compute_stage(ring + slot_c * TG::STAGE);
-      else
-        g.compute_stage_partial(ring + slot_c * TG::STAGE, nact_c);
+      g.compute_stage_n(ring + slot_c * TG::STAGE, nact_c);
       slot_c = slot_c + 1 == NSTAGE ? 0 : slot_c + 1;
     }
-  };
-  for (;;) {
-    if (nact_c >= TG::MI)
-      kloop(std::true_type{});
-    else
-      kloop(std::false_type{});
     stream_epilogue(g, p, c, meta[ci & 1]);
     ++ci;
     c = task(ci);
