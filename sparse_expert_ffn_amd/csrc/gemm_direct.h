@@ -212,18 +212,20 @@ struct TileGemmDirect {
     }
   }
 
-  // Issue the LDS-direct loads of K stage kt into the stage buffer `base`.
+  // LDS-direct load number idx (0 <= idx < NPIECE: this wave's A loads, then
+  // its B loads) of K stage kt into the stage buffer `base`.
   // SGPR_FROM_VALU: the caller cannot rule out that the compiler restores the
   // buffer descriptors from VGPR lanes right before (see dma16).
+  static constexpr int NPIECE = A_PW + B_PW;
   template <bool SGPR_FROM_VALU = false>
-  __device__ __forceinline__ void issue_stage(char* base, int kt) {
+  __device__ __forceinline__ void issue_piece(char* base, int kt, int idx) {
     // wave-uniform (scalar) so the buffer resources stay in SGPRs
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int64_t k0 = (int64_t)kt * BK;
-#pragma unroll
-    for (int t = 0; t < A_PW; ++t) {
+    if (idx < A_PW) {
+      const int t = idx;
       const int q = wave + NW * t;
       if (q < A_INSTR) {  // wave-uniform
+        const int64_t k0 = (int64_t)kt * BK;
         const int lane = threadIdx.x & 63;
         const int r = q * (1024 / A_ROWB) + lane / ACH;
         const int c = (lane % ACH) ^ aswz(r);
@@ -231,9 +233,8 @@ struct TileGemmDirect {
                                                                 : kOob;
         dma16<SGPR_FROM_VALU>(rsrc_a, o, base + q * 1024);
       }
-    }
-#pragma unroll
-    for (int t = 0; t < B_PW; ++t) {
+    } else {
+      const int t = idx - A_PW;
       const int q = wave + NW * t;
       const int m = q / (B_MAT / 1024);  // wave-uniform
       const uint32_t o = boff[t] == kOob ? kOob : boff[t] + (uint32_t)kt * b_stage_bytes;
@@ -243,6 +244,13 @@ struct TileGemmDirect {
       }
       dma16<SGPR_FROM_VALU>(rb, o, base + A_LDS + q * 1024);
     }
+  }
+
+  // All LDS-direct loads of K stage kt into the stage buffer `base`.
+  template <bool SGPR_FROM_VALU = false>
+  __device__ __forceinline__ void issue_stage(char* base, int kt) {
+#pragma unroll
+    for (int i = 0; i < NPIECE; ++i) issue_piece<SGPR_FROM_VALU>(base, kt, i);
   }
 
   struct Frags {
@@ -302,8 +310,8 @@ struct TileGemmDirect {
   // the first ADIST A fragments, then alternates the MFMAs of block i with
   // the read of block i + ADIST: ADIST LDS reads stay in flight behind the
   // matrix work.
-  template <int LO, int HI, bool READ_B>
-  __device__ __forceinline__ void compute_range(const char* base) {
+  template <int LO, int HI, bool READ_B, typename Between>
+  __device__ __forceinline__ void compute_range(const char* base, Between between) {
     if constexpr (HI > LO) {
       constexpr int NBLK = HI - LO;
       constexpr int D = ADIST < NBLK ? ADIST : NBLK;
@@ -320,9 +328,14 @@ struct TileGemmDirect {
           mfma_row(LO + i, a[i], fb_[ks].b);
           __builtin_amdgcn_sched_group_barrier(0x008, NB * NI, 0);
           if (i + D < NBLK) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          between(ks * NBLK + i);
         }
       }
     }
+  }
+  template <int LO, int HI, bool READ_B>
+  __device__ __forceinline__ void compute_range(const char* base) {
+    compute_range<LO, HI, READ_B>(base, [](int) {});
   }
 
   // Row blocks [0, nact) of one stage (0 <= nact <= MI): blocks after the
@@ -369,8 +382,16 @@ struct TileGemmDirect {
     for (int kt = 0; kt < nk; ++kt) {
       wait_vmcnt<(NSTAGE - 2) * MIN_PW>();  // this wave's stage-kt loads have landed
       __syncthreads();                      // ... every wave's; stage kt-1 reads done
-      issue_stage(lds + slot_next * STAGE, kt + NSTAGE - 1);
-      compute_range<0, NA, true>(lds + slot * STAGE);
+      // the stage kt+NSTAGE-1 loads go out one at a time between the row
+      // blocks' MFMAs (all of them at once would hold the wave at the
+      // memory issue while its MFMAs wait)
+      char* nxt = lds + slot_next * STAGE;
+      const int knx = kt + NSTAGE - 1;
+      compute_range<0, NA, true>(lds + slot * STAGE, [&](int i) {
+        if (i < NPIECE) issue_piece(nxt, knx, i);
+      });
+#pragma unroll
+      for (int i = NA * KSTEPS; i < NPIECE; ++i) issue_piece(nxt, knx, i);
       slot = slot + 1 == NSTAGE ? 0 : slot + 1;
       slot_next = slot_next + 1 == NSTAGE ? 0 : slot_next + 1;
     }
