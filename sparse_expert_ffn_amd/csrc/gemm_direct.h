@@ -41,8 +41,8 @@ typedef short i16x4_t __attribute__((ext_vector_type(4)));
 typedef int i32x4_t __attribute__((ext_vector_type(4)));
 
 // Schedule knobs (compile time, chosen by measurement):
-//  MOE_PINGPONG   1: the two waves of each SIMD run half a stage apart
-//                 (kloop_pp), so one's LDS reads overlap the other's MFMAs.
+//  MOE_PINGPONG   1: the two waves of each SIMD alternate between reading
+//                 fragments and running MFMAs (kloop_pp).
 //  MOE_MFMA_PRIO  1: raise the wave's issue priority around its MFMA block.
 #ifndef MOE_PINGPONG
 #define MOE_PINGPONG 0
@@ -155,6 +155,7 @@ struct TileGemmDirect {
   i32x4_t rsrc_a;
   i32x4_t rsrc_b[NB];
   uint32_t b_stage_bytes;  // BK * ldb * ES
+  uint32_t a_stage_bytes;  // A bytes from one K stage to the next (see setup)
   int64_t K_;
 
   __device__ __forceinline__ static int bswz(int k) { return (k & 3) | (((k >> 3) & 1) << 2); }
@@ -177,17 +178,24 @@ struct TileGemmDirect {
   }
 
   // A: buffer of a_bytes at a_base, row_off(r) = byte offset of row r or kOob.
+  // a_blocked = false: rows K-contiguous (element k of row r at row_off(r) +
+  // 2k). a_blocked = true: BM rows stored as slabs of 32 columns, slab by
+  // slab (element k of row r at (k / 32) * BM * 64 + r * 64 + 2 (k % 32); the
+  // caller's row_off(r) is then r * 64), so each stage of A is one contiguous
+  // block.
   // B[m]: base of weight matrix m (K x ldb, row-major) with b_bytes[m] bytes;
   // the tile covers its columns n0 .. n0 + BN, of which ncols[m] are valid.
   template <typename RowOff>
   __device__ __forceinline__ void setup(const void* a_base, uint32_t a_bytes, RowOff row_off,
                                         const char* const* B, const uint32_t* b_bytes,
-                                        int64_t ldb, int64_t n0, const int64_t* ncols) {
+                                        int64_t ldb, int64_t n0, const int64_t* ncols,
+                                        bool a_blocked = false) {
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     rsrc_a = make_srd(a_base, a_bytes);
 #pragma unroll
     for (int m = 0; m < NB; ++m) rsrc_b[m] = make_srd(B[m], b_bytes[m]);
+    a_stage_bytes = a_blocked ? (uint32_t)(BK / 32 * BM * 64) : (uint32_t)(BK * ES);
     b_stage_bytes = (uint32_t)(BK * ldb * ES);
 #pragma unroll
     for (int t = 0; t < A_PW; ++t) {
@@ -197,7 +205,7 @@ struct TileGemmDirect {
         const int r = q * (1024 / A_ROWB) + lane / ACH;
         const int c = (lane % ACH) ^ aswz(r);  // logical chunk stored in this lane's slot
         const uint32_t ro = row_off(r);
-        if (ro != kOob) o = ro + c * 16;
+        if (ro != kOob) o = a_blocked ? ro + (c >> 2) * (BM * 64) + (c & 3) * 16 : ro + c * 16;
       }
       aoff[t] = o;
     }
@@ -229,7 +237,7 @@ struct TileGemmDirect {
         const int lane = threadIdx.x & 63;
         const int r = q * (1024 / A_ROWB) + lane / ACH;
         const int c = (lane % ACH) ^ aswz(r);
-        const uint32_t o = (aoff[t] != kOob && k0 + c * 8 < K_) ? aoff[t] + (uint32_t)(k0 * ES)
+        const uint32_t o = (aoff[t] != kOob && k0 + c * 8 < K_) ? aoff[t] + (uint32_t)kt * a_stage_bytes
                                                                 : kOob;
         dma16<SGPR_FROM_VALU>(rsrc_a, o, base + q * 1024);
       }
@@ -397,47 +405,97 @@ struct TileGemmDirect {
     }
   }
 
-  // ---- ping-pong schedule (two waves per SIMD, half a stage apart)
-  // Waves 0 .. NW/2-1 lead, waves NW/2 .. NW-1 (the other wave of each SIMD:
-  // waves are placed on SIMDs round-robin) lag by one barrier. A stage is
-  // two halves with a barrier before each; half h runs the wave's row blocks
-  // [h MI/2, (h+1) MI/2) (half 0 also reads the stage's B fragments, kept in
-  // registers for half 1). Because the laggers pass each barrier one half
-  // behind, on every SIMD one wave waits for its LDS reads while the other's
-  // MFMAs run.
+  // ---- ping-pong schedule (two waves per SIMD alternate roles)
+  // Waves 0 .. NW/2-1 form group 0, waves NW/2 .. NW-1 group 1; waves are
+  // placed on SIMDs round-robin, so each SIMD holds one wave of each group.
+  // The K loop runs in phases separated by workgroup barriers. In each phase
+  // one group runs the MFMAs of a whole stage from fragments already in its
+  // registers while the other group reads the fragments of its next stage
+  // from LDS and issues its share of a later stage's LDS-direct loads; the
+  // groups swap roles every phase. On every SIMD one wave feeds the matrix
+  // core while the other waits on LDS, instead of both doing the same thing
+  // at the same time.
   //
-  // Barrier numbering (leaders: P(kt) = #2kt+1, Q(kt) = #2kt+2; laggers take
-  // one extra barrier first, so their P(kt) = #2kt+2, Q(kt) = #2kt+3):
-  //  - stage kt+1 is read from P(kt+1) = #2kt+3 (leaders) on. Every wave waits
-  //    for its own stage-(kt+1) loads before its Q(kt), which is #2kt+2 or
-  //    #2kt+3: all of them have landed by #2kt+3.
-  //  - stage kt+NSTAGE-1 goes into the slot of stage kt-1 right after the
-  //    issuing wave's Q(kt) (#2kt+2 or later). The last reads of stage kt-1
-  //    are the laggers' second half, which ends at their P(kt) = #2kt+2.
-  //  - the leaders take one barrier after the loop, so both groups leave it
-  //    having passed the same number of barriers.
-  static constexpr bool PP_OK = MOE_PINGPONG && NW == 8 && MI >= 2 && MI % 2 == 0 && NSTAGE >= 3;
+  // Phase q (q = -1 .. 2nk-1; group 0 = G0, group 1 = G1):
+  //   q = 2s:   G0 computes stage s; G1 reads stage s (and, for s >= 1,
+  //             issues its part of stage s-1+NSTAGE);
+  //   q = 2s+1: G0 reads stage s+1 and issues its part of stage s+NSTAGE;
+  //             G1 computes stage s.
+  // The prologue has stages 0 .. NSTAGE-1 in flight, one per slot.
+  //  - stage X is read first by G0 in phase 2X-1; every wave waits for its
+  //    own loads of stage X before the barrier that ends phase 2X-2, so the
+  //    stage is complete and visible when either group reads it;
+  //  - the slot of stage s is read by G0 in phase 2s-1 and by G1 in phase
+  //    2s; its next stage (s+NSTAGE) is loaded from phase 2s+1 on;
+  //  - every wave passes the same barriers (no barrier depends on the group).
+  static constexpr bool PP_OK = MOE_PINGPONG && NW == 8 && MI >= 2 && NSTAGE >= 3;
+  uint4 fa_[PP_OK ? KSTEPS : 1][PP_OK ? MI : 1];  // A fragments of one stage
+
+  template <int NA>
+  __device__ __forceinline__ void pp_read(const char* base) {
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks) {
+      if constexpr (NA > 0) read_frags_b(base, ks, fb_[ks]);
+#pragma unroll
+      for (int i = 0; i < NA; ++i) fa_[ks][i] = read_a(base, ks, i);
+    }
+  }
+
+  template <int NA>
+  __device__ __forceinline__ void pp_compute() {
+#if MOE_MFMA_PRIO
+    __builtin_amdgcn_s_setprio(1);
+#endif
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks)
+#pragma unroll
+      for (int i = 0; i < NA; ++i) mfma_row(i, fa_[ks][i], fb_[ks].b);
+#if MOE_MFMA_PRIO
+    __builtin_amdgcn_s_setprio(0);
+#endif
+  }
 
   template <int NA>
   __device__ __forceinline__ void kloop_pp(char* lds, int nk) {
-    constexpr int HB = MI / 2;
-    constexpr int H0 = NA < HB ? NA : HB;
-    const bool lag = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) >= NW / 2;
-    wait_vmcnt<(NSTAGE - 2) * MIN_PW>();  // this wave's stage-0 loads have landed
-    if (lag) __syncthreads();
-    int slot = 0;                // slot of stage kt
-    int slot_prev = NSTAGE - 1;  // slot of stage kt-1 = slot of stage kt+NSTAGE-1
-    for (int kt = 0; kt < nk; ++kt) {
-      __syncthreads();  // P(kt)
-      compute_range<0, H0, true>(lds + slot * STAGE);
-      wait_vmcnt<(NSTAGE - 3) * MIN_PW>();  // this wave's stage-(kt+1) loads have landed
-      __syncthreads();  // Q(kt)
-      issue_stage(lds + slot_prev * STAGE, kt + NSTAGE - 1);
-      compute_range<HB, NA, false>(lds + slot * STAGE);
-      slot_prev = slot;
-      slot = slot + 1 == NSTAGE ? 0 : slot + 1;
+    const bool g1 = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) >= NW / 2;
+    auto slot_of = [](int st) { return st % NSTAGE; };
+    // a phase boundary: nothing is scheduled across it (the compiler would
+    // otherwise move MFMAs over the barrier into the other phase)
+    auto phase_end = [] {
+      __builtin_amdgcn_sched_barrier(0);
+      __syncthreads();
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    // the prologue issued stages 0 .. NSTAGE-2; the last slot's stage here
+    issue_stage(lds + (NSTAGE - 1) * STAGE, NSTAGE - 1);
+    wait_vmcnt<(NSTAGE - 1) * MIN_PW>();  // this wave's stage-0 loads have landed
+    __syncthreads();
+    // one loop per group (each straight-line; the fragments have a single
+    // writer and a single reader per iteration), with the same barriers
+    if (!g1) {
+      pp_read<NA>(lds);  // phase -1: read stage 0
+      phase_end();
+      for (int s = 0; s < nk; ++s) {
+        pp_compute<NA>();                     // phase 2s
+        wait_vmcnt<(NSTAGE - 2) * MIN_PW>();  // this wave's stage-(s+1) loads have landed
+        phase_end();
+        if (s + 1 < nk) pp_read<NA>(lds + slot_of(s + 1) * STAGE);  // phase 2s+1
+        issue_stage(lds + slot_of(s) * STAGE, s + NSTAGE);
+        phase_end();
+      }
+    } else {
+      phase_end();  // phase -1
+      for (int s = 0; s < nk; ++s) {
+        pp_read<NA>(lds + slot_of(s) * STAGE);  // phase 2s
+        if (s >= 1) issue_stage(lds + slot_of(s - 1) * STAGE, s - 1 + NSTAGE);
+        wait_vmcnt<(NSTAGE - 2) * MIN_PW>();  // this wave's stage-(s+1) loads have landed
+        phase_end();
+        pp_compute<NA>();  // phase 2s+1
+        phase_end();
+      }
     }
-    if (!lag) __syncthreads();
+    // G1's part of stage nk-1+NSTAGE was never issued and nothing waits for
+    // it; the tail past K is zeros either way
   }
 
   // The K loop for this wave's number of active row blocks (one

@@ -313,6 +313,9 @@ moe_status moe_forward(const moe_shape* shape, const void* A, const void* W_up,
   p.Ds = shape->D_shared;
   p.F = shape->S * shape->k;
   p.grid = 0;
+  // bf16 h in 32-column slabs per block (the down kernel's K stages then read
+  // one contiguous block each); the fp32 path and other widths stay row-major
+  p.h_blocked = (shape->dtype == MOE_BF16 && p.D % 32 == 0 && p.Ds % 32 == 0) ? 1 : 0;
   const int dt = shape->dtype;
   const int BM = shape->block_size;
   hipStream_t hs = reinterpret_cast<hipStream_t>(stream);

@@ -100,13 +100,16 @@ struct ForwardParams {
   float* Y;               // slot combine: [F][H] fp32 weighted rows
   float* Ys;              // slot combine: [S][H] fp32 shared-expert rows
   uint8_t* kept;          // slot combine: [F] 1 = assignment has a slot
-  void* h;                // [cap_rows][D]
-  void* hs;               // [round_up(S, BM)][Ds]
+  void* h;                // [cap_rows][D] (layout: h_blocked)
+  void* hs;               // [round_up(S, BM)][Ds] (layout: h_blocked)
   int* counters;          // kCounterInts ints
   int64_t S, H, D, E, k, Ds, F;
   int atomic_combine;     // 1: atomics into Oacc; 0: slots Y / Ys + combine pass
   int sched_quota;        // 1: static per-expert workgroup quota (ablation baseline)
   int out_bf16;           // O is bf16 (else fp32)
+  int h_blocked;          // 1: h and hs hold each BM-row block as slabs of 32 columns
+                          // (row r, column c of block b at b*BM*N + (c/32)*BM*32 + r*32 + c%32)
+                          // so that each down-projection K stage is contiguous; 0: row-major
   int grid;               // persistent workgroups
 };
 

@@ -573,7 +573,11 @@ __global__ __launch_bounds__((tile_threads<T, BM, 2, 2>()), 1) void upgate_kerne
           if (s_tok[row] >= 0 && col < N) {
             const float u = g.acc[0][i][jj][r];
             const float gv = g.acc[1][i][jj][r];
-            out[(size_t)(b * BM + row) * N + col] = from_f32<T>(silu_f32(u) * gv);
+            const size_t o = p.h_blocked
+                                 ? (size_t)b * BM * N + (size_t)(col >> 5) * (BM * 32) + row * 32 +
+                                       (col & 31)
+                                 : (size_t)(b * BM + row) * N + col;
+            out[o] = from_f32<T>(silu_f32(u) * gv);
           }
         }
     }
@@ -661,9 +665,16 @@ __global__ __launch_bounds__((tile_threads<T, BM, kDownStrips, 1>()), 1) void do
     // this m-block's BM rows of h (or hs), K-contiguous
     const char* Ab = reinterpret_cast<const char*>(shared ? p.hs : p.h) +
                      (size_t)b * BM * K * sizeof(T);
-    g.setup(Ab, (uint32_t)(BM * K * sizeof(T)), [&](int r) -> uint32_t {
-      return s_tok[r] >= 0 ? (uint32_t)(r * K * sizeof(T)) : kOob;
-    }, Bm, bb, p.H, n0, nc);
+    if constexpr (is_direct<TG>()) {
+      const bool hb = p.h_blocked;
+      g.setup(Ab, (uint32_t)(BM * K * sizeof(T)), [&](int r) -> uint32_t {
+        return s_tok[r] >= 0 ? (uint32_t)(hb ? r * 64 : r * K * sizeof(T)) : kOob;
+      }, Bm, bb, p.H, n0, nc, hb);
+    } else {
+      g.setup(Ab, (uint32_t)(BM * K * sizeof(T)), [&](int r) -> uint32_t {
+        return s_tok[r] >= 0 ? (uint32_t)(r * K * sizeof(T)) : kOob;
+      }, Bm, bb, p.H, n0, nc);
+    }
     run_mainloop(g, smem, K, [&](int r) { return s_tok[r] >= 0; });
     const int64_t H = p.H;
     if (p.atomic_combine) {
@@ -814,9 +825,11 @@ __device__ __forceinline__ void stream_setup(TG& g, const ForwardParams& p, cons
   }
   const char* Ab = reinterpret_cast<const char*>(k.shared ? p.hs : p.h) +
                    (size_t)k.b * BM * K * sizeof(bf16_t);
+  const bool hb = p.h_blocked;
   g.setup(Ab, (uint32_t)(BM * K * sizeof(bf16_t)), [&](int r) -> uint32_t {
-    return stream_row_valid(p, k, m, BM, r) ? (uint32_t)(r * K * sizeof(bf16_t)) : kOob;
-  }, Bm, bb, H, n0, nc);
+    return stream_row_valid(p, k, m, BM, r) ? (uint32_t)(hb ? r * 64 : r * K * sizeof(bf16_t))
+                                            : kOob;
+  }, Bm, bb, H, n0, nc, hb);
   g.set_k(K);
 }
 
