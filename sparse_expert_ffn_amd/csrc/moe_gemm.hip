@@ -1051,49 +1051,60 @@ hipError_t launch_forward_setup(const ForwardParams& p, hipStream_t st) {
 
 // Slot combine: O[t][:] = sum_{j<k, kept} w[f] * Y[f][:] (f = t*k + j) (+ Ys[t][:]):
 // each product rounded to fp32, summed in slot order in fp32, rounded once
-// into O. 4 columns per thread step.
+// into O.
 template <bool OUT_BF16>
 __global__ __launch_bounds__(256) void combine_kernel(const float* Y, const float* Ys,
                                                       const uint8_t* kept, const float* w,
                                                       void* O, int64_t S, int64_t H,
                                                       int64_t k) {
-  const int64_t h4 = H / 4;
-  const int64_t total = S * h4;
+  // 8 columns per thread step. A token's k slot rows are loaded whether or
+  // not the slot was kept (the rows exist in the workspace; an unkept one
+  // holds stale data that is never added), so the loads do not wait on the
+  // kept flags; the sum is the same as adding only the kept slots, in slot
+  // order.
+  const int64_t h8 = H / 8;
+  const int64_t total = S * h8;
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += stride) {
-    const int64_t t = i / h4;
-    const int64_t c = (i - t * h4) * 4;
-    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    const int64_t t = i / h8;
+    const int64_t c = (i - t * h8) * 8;
+    float a[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     for (int64_t j = 0; j < k; ++j) {
       const int64_t f = t * k + j;
-      if (kept[f]) {
-        const float4 y = *reinterpret_cast<const float4*>(Y + f * H + c);
-        const float wf = w[f];
-        acc.x += __fmul_rn(wf, y.x);  // the product rounded, not fused into the add
-        acc.y += __fmul_rn(wf, y.y);
-        acc.z += __fmul_rn(wf, y.z);
-        acc.w += __fmul_rn(wf, y.w);
+      const float4 y0 = *reinterpret_cast<const float4*>(Y + f * H + c);
+      const float4 y1 = *reinterpret_cast<const float4*>(Y + f * H + c + 4);
+      const bool use = kept[f] != 0;
+      const float wf = w[f];
+      const float y[8] = {y0.x, y0.y, y0.z, y0.w, y1.x, y1.y, y1.z, y1.w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float s = a[e] + __fmul_rn(wf, y[e]);  // the product rounded, not fused
+        a[e] = use ? s : a[e];
       }
     }
     if (Ys != nullptr) {
-      const float4 y = *reinterpret_cast<const float4*>(Ys + t * H + c);
-      acc.x += y.x;
-      acc.y += y.y;
-      acc.z += y.z;
-      acc.w += y.w;
+      const float4 y0 = *reinterpret_cast<const float4*>(Ys + t * H + c);
+      const float4 y1 = *reinterpret_cast<const float4*>(Ys + t * H + c + 4);
+      a[0] += y0.x; a[1] += y0.y; a[2] += y0.z; a[3] += y0.w;
+      a[4] += y1.x; a[5] += y1.y; a[6] += y1.z; a[7] += y1.w;
     }
     if constexpr (OUT_BF16) {
-      const uint32_t w0 = f32_to_bf16(acc.x) | ((uint32_t)f32_to_bf16(acc.y) << 16);
-      const uint32_t w1 = f32_to_bf16(acc.z) | ((uint32_t)f32_to_bf16(acc.w) << 16);
-      *reinterpret_cast<uint2*>(reinterpret_cast<bf16_t*>(O) + t * H + c) = make_uint2(w0, w1);
+      uint32_t q[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        q[e] = f32_to_bf16(a[2 * e]) | ((uint32_t)f32_to_bf16(a[2 * e + 1]) << 16);
+      *reinterpret_cast<uint4*>(reinterpret_cast<bf16_t*>(O) + t * H + c) =
+          make_uint4(q[0], q[1], q[2], q[3]);
     } else {
-      *reinterpret_cast<float4*>(reinterpret_cast<float*>(O) + t * H + c) = acc;
+      float* o = reinterpret_cast<float*>(O) + t * H + c;
+      *reinterpret_cast<float4*>(o) = make_float4(a[0], a[1], a[2], a[3]);
+      *reinterpret_cast<float4*>(o + 4) = make_float4(a[4], a[5], a[6], a[7]);
     }
   }
 }
 
 hipError_t launch_forward_combine(const ForwardParams& p, hipStream_t st) {
-  const int64_t total = p.S * (p.H / 4);
+  const int64_t total = p.S * (p.H / 8);
   if (total == 0) return hipSuccess;
   int64_t blocks = (total + 255) / 256;
   if (blocks > 8192) blocks = 8192;
