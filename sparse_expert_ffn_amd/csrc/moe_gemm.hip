@@ -16,7 +16,9 @@
 //
 // Inside a range the tasks of a group of kGroupBlocks consecutive m-blocks are
 // ordered n-tile-major: tasks running side by side share both the A rows of
-// a few m-blocks and the weight strips of a few n-tiles.
+// a few m-blocks and the weight strips of a few n-tiles. With about one
+// m-block per expert (nothing to share across m-blocks) each m-block's
+// n-tiles run back to back instead.
 #include <algorithm>
 #include <type_traits>
 
@@ -348,13 +350,13 @@ hipError_t launch_gate(const GateParams& p, int dtype, hipStream_t st) {
 // ------------------------------------------------------------ task scheduling
 
 // Task t of a space of nb m-blocks x nn n-tiles -> (m-block b, n-tile j),
-// n-tile-major inside each group of kGroupBlocks consecutive m-blocks.
-__device__ __forceinline__ void decode_task(int64_t t, int64_t nb, int64_t nn, int64_t& b,
-                                            int64_t& j) {
-  const int64_t per = (int64_t)kGroupBlocks * nn;
+// n-tile-major inside each group of gb consecutive m-blocks.
+__device__ __forceinline__ void decode_task(int64_t t, int64_t nb, int64_t nn, int64_t gb,
+                                            int64_t& b, int64_t& j) {
+  const int64_t per = gb * nn;
   const int64_t grp = t / per;
-  const int64_t b0 = grp * kGroupBlocks;
-  const int64_t gsz = min((int64_t)kGroupBlocks, nb - b0);
+  const int64_t b0 = grp * gb;
+  const int64_t gsz = min(gb, nb - b0);
   const int64_t w = t - grp * per;
   j = w / gsz;
   b = b0 + w % gsz;
@@ -423,15 +425,17 @@ __device__ __forceinline__ int64_t first_block(const int32_t* expert_ids, int64_
 
 // Task id of (m-block b, n-tile j) in the queue scheduler's order (the
 // inverse of decode_task).
-__device__ __forceinline__ int64_t encode_task(int64_t b, int64_t j, int64_t nb, int64_t nn) {
-  const int64_t grp = b / kGroupBlocks;
-  const int64_t b0 = grp * kGroupBlocks;
-  const int64_t gsz = min((int64_t)kGroupBlocks, nb - b0);
-  return grp * kGroupBlocks * nn + j * gsz + (b - b0);
+__device__ __forceinline__ int64_t encode_task(int64_t b, int64_t j, int64_t nb, int64_t nn,
+                                               int64_t gb) {
+  const int64_t grp = b / gb;
+  const int64_t b0 = grp * gb;
+  const int64_t gsz = min(gb, nb - b0);
+  return grp * gb * nn + j * gsz + (b - b0);
 }
 
 struct TaskSpace {
   int64_t nb_r, nn_r, nb_s, nn_s, t_r, total;
+  int64_t gb_r;  // routed m-blocks per group (the shared expert's: kGroupBlocks)
 };
 
 __device__ __forceinline__ TaskSpace task_space(const ForwardParams& p, int BM, int BN,
@@ -443,6 +447,11 @@ __device__ __forceinline__ TaskSpace task_space(const ForwardParams& p, int BM, 
   ts.nn_s = (n_shared_cols + BN - 1) / BN;
   ts.t_r = ts.nb_r * ts.nn_r;
   ts.total = ts.t_r + ts.nb_s * ts.nn_s;
+  // About one m-block per expert (decode, many experts): the m-blocks share
+  // no weights, so each m-block's n-tiles run back to back and the XCD's
+  // concurrent tasks stream whole weight rows (measured: dsv3 -2%). Several
+  // m-blocks per expert: groups of kGroupBlocks share each weight strip.
+  ts.gb_r = ts.nb_r <= p.E + p.E / 4 ? 1 : kGroupBlocks;
   return ts;
 }
 
@@ -460,7 +469,7 @@ __device__ __forceinline__ int64_t claim_quota(const ForwardParams& p, const Tas
       }
       const int64_t u = atomicAdd(&ctr[st.e], 1);
       if (u < st.nblk * ts.nn_r)
-        return encode_task(st.b0 + u / ts.nn_r, u % ts.nn_r, ts.nb_r, ts.nn_r);
+        return encode_task(st.b0 + u / ts.nn_r, u % ts.nn_r, ts.nb_r, ts.nn_r, ts.gb_r);
       ++st.e;
       st.b0 = -1;
       continue;
@@ -511,9 +520,9 @@ __global__ __launch_bounds__((tile_threads<T, BM, 2, 2>()), 1) void upgate_kerne
     const bool shared = t >= ts.t_r;
     int64_t b, j;
     if (!shared)
-      decode_task(t, ts.nb_r, ts.nn_r, b, j);
+      decode_task(t, ts.nb_r, ts.nn_r, ts.gb_r, b, j);
     else
-      decode_task(t - ts.t_r, ts.nb_s, ts.nn_s, b, j);
+      decode_task(t - ts.t_r, ts.nb_s, ts.nn_s, kGroupBlocks, b, j);
     if (threadIdx.x < BM) {
       const int r = threadIdx.x;
       int tok;
@@ -618,9 +627,9 @@ __global__ __launch_bounds__((tile_threads<T, BM, kDownStrips, 1>()), 1) void do
     const bool shared = t >= ts.t_r;
     int64_t b, j;
     if (!shared)
-      decode_task(t, ts.nb_r, ts.nn_r, b, j);
+      decode_task(t, ts.nb_r, ts.nn_r, ts.gb_r, b, j);
     else
-      decode_task(t - ts.t_r, ts.nb_s, ts.nn_s, b, j);
+      decode_task(t - ts.t_r, ts.nb_s, ts.nn_s, kGroupBlocks, b, j);
     if (threadIdx.x < BM) {
       const int r = threadIdx.x;
       if (!shared) {
@@ -758,9 +767,9 @@ __device__ __forceinline__ StreamTask stream_task(const TaskSpace& ts, int64_t t
   k.K = k.nk = 0;
   if (t < 0) return k;
   if (!k.shared)
-    decode_task(t, ts.nb_r, ts.nn_r, k.b, k.j);
+    decode_task(t, ts.nb_r, ts.nn_r, ts.gb_r, k.b, k.j);
   else
-    decode_task(t - ts.t_r, ts.nb_s, ts.nn_s, k.b, k.j);
+    decode_task(t - ts.t_r, ts.nb_s, ts.nn_s, kGroupBlocks, k.b, k.j);
   k.K = k.shared ? KS : KR;
   k.nk = (k.K + BK - 1) / BK;
   return k;
