@@ -190,8 +190,10 @@ def main():
     counts = buf.expert_counts.cpu().numpy()
     cnt = layer_counts(wl, counts, bm)
 
-    # HIP events around the two GEMM kernels only, on the stream they run on
-    moe.moe_profile_enable(True, stages=(1, 2))
+    # HIP events around the up/gate kernel only (the roofline kernel), on the
+    # stream it runs on: each bracketed kernel adds two marker packets, which
+    # cost decode-sized steps about 1.5% each
+    moe.moe_profile_enable(True, stages=(1,))
     moe.moe_profile_collect()  # drop anything recorded before the timed region
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
@@ -207,15 +209,16 @@ def main():
     stage_ms, n_calls = moe.moe_profile_collect(4)
     ms = ev0.elapsed_time(ev1) / args.steps
     up_ms = stage_ms[1] / max(n_calls, 1)
-    down_ms = stage_ms[2] / max(n_calls, 1)
-    # setup and combine kernels, timed in a few extra steps after the timed region
-    moe.moe_profile_enable(True, stages=(0, 3))
+    # setup, down and combine kernels, timed in a few extra steps after the
+    # timed region
+    moe.moe_profile_enable(True, stages=(0, 2, 3))
     n_extra = min(args.steps, 10)
     for _ in range(n_extra):
         step()
     torch.cuda.synchronize()
     moe.moe_profile_enable(False)
     small_ms, n_small = moe.moe_profile_collect(4)
+    down_ms = small_ms[2] / max(n_small, 1)
 
     peak = PEAK_BF16_TFLOPS if wl.dtype == wk.BF16 else PEAK_F32_TFLOPS
     up_tflops = cnt["flops_up"] / (up_ms * 1e-3) / 1e12
