@@ -44,6 +44,9 @@ def parse():
     ap.add_argument("--sched", choices=("queue", "quota"), default="queue",
                     help="grouped-GEMM scheduler: per-XCD atomic task queues (default) or "
                          "the static per-expert workgroup quota (ablation baseline)")
+    ap.add_argument("--launch", choices=("two", "one"), default="two",
+                    help="the expert GEMMs as two persistent launches (up/gate, then down) "
+                         "or as one (down tasks wait per m-block for its up/gate tasks)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU work of the oracle baseline sample")
@@ -65,9 +68,12 @@ def layer_counts(wl, counts_e, bm):
     bytes_w = touched * w_expert + 3.0 * wl.H * wl.D_shared * b
     bytes_up = touched * 2.0 * wl.H * wl.D * b + 2.0 * wl.H * wl.D_shared * b + wl.S * wl.H * b
     bytes_io = 2.0 * wl.S * wl.H * b + wl.H * wl.E * b
+    # both expert GEMMs in one kernel: the touched weights, A, and the fp32
+    # slot rows it writes (h stays between its two halves)
+    bytes_experts = bytes_w + wl.S * wl.H * b + 4.0 * wl.H * (kept + (wl.S if wl.D_shared else 0))
     return {"kept": kept, "touched": touched, "flops_gate": f_gate, "flops_up": f_up,
             "flops_down": f_down, "flops": f_gate + f_up + f_down,
-            "bytes": bytes_w + bytes_io, "bytes_up": bytes_up}
+            "bytes": bytes_w + bytes_io, "bytes_up": bytes_up, "bytes_experts": bytes_experts}
 
 
 def measured_traffic(workload, block_size):
@@ -178,7 +184,9 @@ def main():
         Wsg = td(wk.draw_tensor(wl, wk.T_WSGATE, (wl.H, wl.D_shared), ssu))
         Wsd = td(wk.draw_tensor(wl, wk.T_WSDOWN, (wl.D_shared, wl.H), ssd))
     buf = MoEBuffers(wl.S, wl.H, wl.D, wl.E, wl.k, wl.D_shared, wl.capacity, bm,
-                     wl.renormalize, wl.dtype, sched_quota=args.sched == "quota", device=dev)
+                     wl.renormalize, wl.dtype, sched_quota=args.sched == "quota",
+                     fused_launch=args.launch == "one", device=dev)
+    one = args.launch == "one"
     stream = torch.cuda.current_stream()
 
     def step():
@@ -221,22 +229,26 @@ def main():
     down_ms = small_ms[2] / max(n_small, 1)
 
     peak = PEAK_BF16_TFLOPS if wl.dtype == wk.BF16 else PEAK_F32_TFLOPS
-    up_tflops = cnt["flops_up"] / (up_ms * 1e-3) / 1e12
-    up_gbs = cnt["bytes_up"] / (up_ms * 1e-3) / 1e9
-    # the up/gate kernel's bound: its byte floor at the HBM peak vs its flop
-    # floor at the MFMA peak (decode streams weights; prefill is MFMA work)
-    hbm_bound = cnt["bytes_up"] / (PEAK_HBM_GBS * 1e9) > cnt["flops_up"] / (peak * 1e12)
+    # the roofline kernel: up/gate, or with one launch both expert GEMMs
+    k_flops = cnt["flops_up"] + cnt["flops_down"] if one else cnt["flops_up"]
+    k_bytes = cnt["bytes_experts"] if one else cnt["bytes_up"]
+    up_tflops = k_flops / (up_ms * 1e-3) / 1e12
+    up_gbs = k_bytes / (up_ms * 1e-3) / 1e9
+    # the kernel's bound: its byte floor at the HBM peak vs its flop floor at
+    # the MFMA peak (decode streams weights; prefill is MFMA work)
+    hbm_bound = k_bytes / (PEAK_HBM_GBS * 1e9) > k_flops / (peak * 1e12)
     if hbm_bound:
         roof = {"bound": "hbm", "achieved": up_gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": up_gbs / PEAK_HBM_GBS}
     else:
         roof = {"bound": "mfma", "achieved": up_tflops, "peak": peak, "unit": "TFLOP/s",
                 "frac": up_tflops / peak}
-    roof.update({"traffic": measured_traffic(wl.name, bm),
+    roof.update({"traffic": None if one else measured_traffic(wl.name, bm),
                  "traffic_unit": "HBM bytes per launch",
-                 "kernel": "up/gate grouped GEMM + SwiGLU",
-                 "avg_launch_ms": up_ms, "flops_per_launch": cnt["flops_up"],
-                 "bytes_per_launch": cnt["bytes_up"]})
+                 "kernel": ("up/gate + down grouped GEMMs, one launch" if one
+                            else "up/gate grouped GEMM + SwiGLU"),
+                 "avg_launch_ms": up_ms, "flops_per_launch": k_flops,
+                 "bytes_per_launch": k_bytes})
     layer_tflops = cnt["flops"] / (ms * 1e-3) / 1e12
     floor_s = max(cnt["flops"] / (peak * 1e12), cnt["bytes"] / (PEAK_HBM_GBS * 1e9))
     out = {
@@ -254,15 +266,16 @@ def main():
         "data": "synthetic (seeded PCG64 normals, pages' distributions)",
         "config": {"workload": wl.name, "S": wl.S, "H": wl.H, "D": wl.D, "E": wl.E, "k": wl.k,
                    "D_shared": wl.D_shared, "capacity": wl.capacity, "block_size": bm,
-                   "scheduler": args.sched, "parallelism": "single GPU"},
+                   "scheduler": args.sched, "launch": args.launch,
+                   "parallelism": "single GPU"},
         "roofline": roof,
         "layer": {"tflops": layer_tflops, "mfma_frac": layer_tflops / peak,
                   "floor_ms": floor_s * 1e3, "roofline_frac": floor_s / (ms * 1e-3),
                   "gbs": cnt["bytes"] / (ms * 1e-3) / 1e9,
                   "hbm_frac": cnt["bytes"] / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
                   "kept": cnt["kept"],
-                  "touched_experts": cnt["touched"], "down_ms": down_ms,
-                  "down_tflops": cnt["flops_down"] / (down_ms * 1e-3) / 1e12,
+                  "touched_experts": cnt["touched"], "down_ms": None if one else down_ms,
+                  "down_tflops": None if one else cnt["flops_down"] / (down_ms * 1e-3) / 1e12,
                   "setup_ms": small_ms[0] / max(n_small, 1),
                   "combine_ms": small_ms[3] / max(n_small, 1),
                   "wall_s": wall},

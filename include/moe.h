@@ -106,6 +106,15 @@ typedef struct {
  * results; under a skewed routing the hot experts' workgroups queue while the
  * others idle. */
 #define MOE_SCHED_QUOTA 4
+/* flags (bf16 only; not with MOE_SCHED_QUOTA, else MOE_ERR_UNSUPPORTED): run
+ * the up/gate and down GEMMs as one persistent launch (the FlashMoE review's
+ * single-kernel task graph, Algorithm 1) instead of two. Workgroups claim
+ * down tasks once all up/gate tasks are claimed; a down task waits until
+ * every up/gate task of its m-block has published its SwiGLU rows (one
+ * counter per m-block in the workspace). Same tiles, same results, bit for
+ * bit, as the two-launch form. The per-stage timer then reports the one
+ * kernel as stage 1 and nothing as stage 2. */
+#define MOE_FUSED_LAUNCH 8
 
 /*
  * Gate scores and softmax top-k routing.

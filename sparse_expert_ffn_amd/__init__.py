@@ -30,6 +30,7 @@ MOE_BF16 = 1
 MOE_OUTPUT_F32 = 1
 MOE_COMBINE_ATOMIC = 2
 MOE_SCHED_QUOTA = 4  # ablation baseline: static per-expert workgroup quota
+MOE_FUSED_LAUNCH = 8  # up/gate and down GEMMs in one persistent launch (bf16)
 
 STATUS = {0: "MOE_OK", 1: "MOE_ERR_INVALID_ARGUMENT", 2: "MOE_ERR_UNSUPPORTED",
           3: "MOE_ERR_WORKSPACE_TOO_SMALL", 4: "MOE_ERR_HIP"}
@@ -61,9 +62,10 @@ class moe_shape(ctypes.Structure):
 
 def make_shape(S, H, D, E, k, D_shared=0, capacity=0, block_size=128, renormalize=1,
                dtype=MOE_BF16, out_f32=False, atomic_combine=False,
-               sched_quota=False) -> moe_shape:
+               sched_quota=False, fused_launch=False) -> moe_shape:
     flags = ((MOE_OUTPUT_F32 if out_f32 else 0) | (MOE_COMBINE_ATOMIC if atomic_combine else 0)
-             | (MOE_SCHED_QUOTA if sched_quota else 0))
+             | (MOE_SCHED_QUOTA if sched_quota else 0)
+             | (MOE_FUSED_LAUNCH if fused_launch else 0))
     return moe_shape(S, H, D, E, k, D_shared, capacity, block_size, renormalize, dtype, flags)
 
 

@@ -23,7 +23,7 @@ bool fits_buffer(int64_t bytes) { return bytes >= 0 && bytes < ((int64_t)1 << 31
 
 moe_status check_routing_dims(const moe_shape* s) {
   if (s == nullptr) return MOE_ERR_INVALID_ARGUMENT;
-  if ((s->flags & ~(MOE_OUTPUT_F32 | MOE_COMBINE_ATOMIC | MOE_SCHED_QUOTA)) != 0)
+  if ((s->flags & ~(MOE_OUTPUT_F32 | MOE_COMBINE_ATOMIC | MOE_SCHED_QUOTA | MOE_FUSED_LAUNCH)) != 0)
     return MOE_ERR_INVALID_ARGUMENT;
   if (s->dtype != MOE_F32 && s->dtype != MOE_BF16) return MOE_ERR_INVALID_ARGUMENT;
   if (s->S < 0 || s->E < 1 || s->k < 1 || s->k > s->E) return MOE_ERR_INVALID_ARGUMENT;
@@ -48,6 +48,9 @@ moe_status check_forward_dims(const moe_shape* s) {
   if (s->H < 1 || s->D < 1 || s->D_shared < 0) return MOE_ERR_INVALID_ARGUMENT;
   if (s->H % 8 || s->D % 8 || s->D_shared % 8) return MOE_ERR_UNSUPPORTED;
   if (!forward_lds_ok(s->dtype, s->block_size)) return MOE_ERR_UNSUPPORTED;
+  if ((s->flags & MOE_FUSED_LAUNCH) &&
+      (s->dtype != MOE_BF16 || (s->flags & MOE_SCHED_QUOTA)))
+    return MOE_ERR_UNSUPPORTED;
   // the kernels address A, each expert's weight matrices and the SwiGLU rows
   // through 32-bit buffer offsets: each must stay below 2 GiB
   const int64_t es = s->dtype == MOE_BF16 ? 2 : 4;
@@ -82,7 +85,8 @@ bool out_bf16(const moe_shape* s) {
 bool atomic_combine(const moe_shape* s) { return (s->flags & MOE_COMBINE_ATOMIC) != 0; }
 
 struct ForwardLayout {
-  size_t counters, oacc, y, ys, kept, h, hs, total;
+  size_t counters, ready, oacc, y, ys, kept, h, hs, total;
+  int64_t n_ready;
 };
 
 ForwardLayout forward_layout(const moe_shape* s) {
@@ -94,7 +98,10 @@ ForwardLayout forward_layout(const moe_shape* s) {
   const bool atom = atomic_combine(s);
   ForwardLayout L;
   L.counters = 0;
-  L.oacc = round_up(kCounterInts * sizeof(int), kAlignUp);
+  L.ready = round_up(kCounterInts * sizeof(int), kAlignUp);
+  // one readiness counter per routed and per shared m-block (one launch only)
+  L.n_ready = (s->flags & MOE_FUSED_LAUNCH) ? cap_rows / BM + s_rows / BM : 0;
+  L.oacc = L.ready + round_up((size_t)L.n_ready * sizeof(int), kAlignUp);
   // atomic combine: fp32 accumulator unless O itself is fp32
   const size_t oacc_bytes = (atom && out_bf16(s)) ? (size_t)s->S * s->H * sizeof(float) : 0;
   L.y = L.oacc + round_up(oacc_bytes, kAlignUp);
@@ -305,6 +312,9 @@ moe_status moe_forward(const moe_shape* shape, const void* A, const void* W_up,
   p.h = ws + L.h;
   p.hs = ws + L.hs;
   p.counters = reinterpret_cast<int*>(ws + L.counters);
+  p.ready = reinterpret_cast<int*>(ws + L.ready);
+  p.n_ready = L.n_ready;
+  p.fused = (shape->flags & MOE_FUSED_LAUNCH) ? 1 : 0;
   p.S = shape->S;
   p.H = shape->H;
   p.D = shape->D;
@@ -325,10 +335,15 @@ moe_status moe_forward(const moe_shape* shape, const void* A, const void* W_up,
   }
   if (run_stage(0, hs, [&] { return launch_forward_setup(p, hs); }) != hipSuccess)
     return MOE_ERR_HIP;
-  if (run_stage(1, hs, [&] { return launch_forward_upgate(p, dt, BM, hs); }) != hipSuccess)
-    return MOE_ERR_HIP;
-  if (run_stage(2, hs, [&] { return launch_forward_down(p, dt, BM, hs); }) != hipSuccess)
-    return MOE_ERR_HIP;
+  if (p.fused) {
+    if (run_stage(1, hs, [&] { return launch_forward_fused(p, BM, hs); }) != hipSuccess)
+      return MOE_ERR_HIP;
+  } else {
+    if (run_stage(1, hs, [&] { return launch_forward_upgate(p, dt, BM, hs); }) != hipSuccess)
+      return MOE_ERR_HIP;
+    if (run_stage(2, hs, [&] { return launch_forward_down(p, dt, BM, hs); }) != hipSuccess)
+      return MOE_ERR_HIP;
+  }
   if (p.atomic_combine) {
     if (p.out_bf16 &&
         run_stage(3, hs, [&] { return launch_forward_finalize(p, hs); }) != hipSuccess)

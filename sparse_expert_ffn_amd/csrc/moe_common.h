@@ -103,6 +103,9 @@ struct ForwardParams {
   void* h;                // [cap_rows][D] (layout: h_blocked)
   void* hs;               // [round_up(S, BM)][Ds] (layout: h_blocked)
   int* counters;          // kCounterInts ints
+  int* ready;             // one launch: per m-block count of finished up/gate tasks
+                          // (routed blocks, then shared blocks)
+  int64_t n_ready;        // entries of ready
   int64_t S, H, D, E, k, Ds, F;
   int atomic_combine;     // 1: atomics into Oacc; 0: slots Y / Ys + combine pass
   int sched_quota;        // 1: static per-expert workgroup quota (ablation baseline)
@@ -111,6 +114,7 @@ struct ForwardParams {
                           // (row r, column c of block b at b*BM*N + (c/32)*BM*32 + r*32 + c%32)
                           // so that each down-projection K stage is contiguous; 0: row-major
   int grid;               // persistent workgroups
+  int fused;              // 1: up/gate and down in one launch (bf16)
 };
 
 constexpr int kAlignSeg = 512;   // assignments per wave segment in the align kernels
@@ -139,6 +143,7 @@ hipError_t launch_align(const AlignParams& p, hipStream_t st);
 hipError_t launch_forward_setup(const ForwardParams& p, hipStream_t st);
 hipError_t launch_forward_upgate(const ForwardParams& p, int dtype, int BM, hipStream_t st);
 hipError_t launch_forward_down(const ForwardParams& p, int dtype, int BM, hipStream_t st);
+hipError_t launch_forward_fused(const ForwardParams& p, int BM, hipStream_t st);
 hipError_t launch_forward_finalize(const ForwardParams& p, hipStream_t st);
 hipError_t launch_forward_combine(const ForwardParams& p, hipStream_t st);
 int forward_lds_ok(int dtype, int BM);

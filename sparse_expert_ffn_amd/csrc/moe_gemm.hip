@@ -53,14 +53,22 @@ constexpr bool is_direct() {
   return TG::DIRECT;
 }
 
-// Run the K loop of tile core TG. The direct core gets a static LDS ring and
-// skips each wave's row blocks past the last row for which valid(r) holds;
-// the register-staged core uses the dynamic buffer and computes every row.
+// The direct core's static LDS ring: one per tile core type, so kernels that
+// run several GEMMs on one core share it.
+template <typename TG>
+__device__ __forceinline__ char* lds_ring() {
+  __shared__ __align__(16) char ring[TG::LDS_BYTES];
+  return ring;
+}
+
+// Run the K loop of tile core TG. The direct core gets the static LDS ring
+// and skips each wave's row blocks past the last row for which valid(r)
+// holds; the register-staged core uses the dynamic buffer and computes every
+// row.
 template <typename TG, typename Valid>
 __device__ __forceinline__ void run_mainloop(TG& g, char* dyn, int64_t K, Valid valid) {
   if constexpr (is_direct<TG>()) {
-    __shared__ __align__(16) char ring[TG::LDS_BYTES];
-    g.mainloop(ring, K, g.active_blocks(valid));
+    g.mainloop(lds_ring<TG>(), K, g.active_blocks(valid));
   } else {
     g.mainloop(dyn, K);
   }
@@ -499,24 +507,13 @@ constexpr int tile_threads() {
   return TileSel<T, BM, NB, STAGING>::type::THREADS;
 }
 
-template <typename T, int BM, int BN>
-__global__ __launch_bounds__((tile_threads<T, BM, 2, 2>()), 1) void upgate_kernel(ForwardParams p) {
-  using TG = typename TileSel<T, BM, 2, 2>::type;
+// One up/gate task t of the task space ts, run by the whole workgroup.
+// Returns the readiness index of its m-block (b routed, nb_r + b shared).
+template <typename T, int BM, int BN, typename TG>
+__device__ __forceinline__ int64_t upgate_task(const ForwardParams& p, const TaskSpace& ts,
+                                               int64_t t, TG& g, char* smem, int* s_tok) {
   static_assert(TG::BN == BN, "tile width");
-  extern __shared__ __align__(16) char smem[];
-  __shared__ int64_t s_task;
-  __shared__ int s_tok[BM];
-  const TaskSpace ts = task_space(p, BM, BN, p.D, p.Ds);
-  int q = blockIdx.x % kXcds, tried = 0;
-  QuotaState qs = quota_init(p.E);
-  TG g;
-  for (;;) {
-    if (threadIdx.x == 0)
-      s_task = p.sched_quota ? claim_quota(p, ts, p.counters + kQuotaBase, qs)
-                             : claim_task(p.counters, ts.total, q, tried);
-    __syncthreads();
-    const int64_t t = uniform64(s_task);
-    if (t < 0) break;
+  {
     const bool shared = t >= ts.t_r;
     int64_t b, j;
     if (!shared)
@@ -590,6 +587,28 @@ __global__ __launch_bounds__((tile_threads<T, BM, 2, 2>()), 1) void upgate_kerne
           }
         }
     }
+    return shared ? ts.nb_r + b : b;
+  }
+}
+
+template <typename T, int BM, int BN>
+__global__ __launch_bounds__((tile_threads<T, BM, 2, 2>()), 1) void upgate_kernel(ForwardParams p) {
+  using TG = typename TileSel<T, BM, 2, 2>::type;
+  extern __shared__ __align__(16) char smem[];
+  __shared__ int64_t s_task;
+  __shared__ int s_tok[BM];
+  const TaskSpace ts = task_space(p, BM, BN, p.D, p.Ds);
+  int q = blockIdx.x % kXcds, tried = 0;
+  QuotaState qs = quota_init(p.E);
+  TG g;
+  for (;;) {
+    if (threadIdx.x == 0)
+      s_task = p.sched_quota ? claim_quota(p, ts, p.counters + kQuotaBase, qs)
+                             : claim_task(p.counters, ts.total, q, tried);
+    __syncthreads();
+    const int64_t t = uniform64(s_task);
+    if (t < 0) break;
+    upgate_task<T, BM, BN>(p, ts, t, g, smem, s_tok);
   }
 }
 
@@ -601,35 +620,24 @@ __global__ __launch_bounds__((tile_threads<T, BM, 2, 2>()), 1) void upgate_kerne
 // weights run as the tile core's two matrices, sharing the h rows.
 constexpr int kDownStrips = 2;
 
-template <typename T, int BM, int BN>
-__global__ __launch_bounds__((tile_threads<T, BM, kDownStrips, 1>()), 1) void down_kernel(
-    ForwardParams p) {
-  using TG = typename TileSel<T, BM, kDownStrips, 1>::type;
+// One down task t of the task space ts, run by the whole workgroup.
+// before_rows(rb, shared) runs on every thread once the m-block is known and
+// before the barrier that precedes the task's first read of h (rb: the
+// m-block's readiness index, as upgate_task returns it).
+template <typename T, int BM, int BN, typename TG, typename BeforeRows>
+__device__ __forceinline__ void down_task(const ForwardParams& p, const TaskSpace& ts, int64_t t,
+                                          TG& g, char* smem, int* s_tok, int* s_f, float* s_w,
+                                          BeforeRows before_rows) {
   static_assert(TG::BN == BN, "tile width");
   constexpr int NT = kDownStrips * BN;  // columns per task
-  extern __shared__ __align__(16) char smem[];
-  __shared__ int64_t s_task;
-  __shared__ int s_tok[BM];
-  __shared__ int s_f[BM];   // output row: slot f (routed) or token (shared)
-  __shared__ float s_w[BM];
-  const TaskSpace ts = task_space(p, BM, NT, p.H, p.H);
-  int q = blockIdx.x % kXcds, tried = 0;
-  int* counters = p.counters + kXcds;
-  QuotaState qs = quota_init(p.E);
-  TG g;
-  for (;;) {
-    if (threadIdx.x == 0)
-      s_task = p.sched_quota ? claim_quota(p, ts, p.counters + kQuotaBase + kQuotaStride, qs)
-                             : claim_task(counters, ts.total, q, tried);
-    __syncthreads();
-    const int64_t t = uniform64(s_task);
-    if (t < 0) break;
+  {
     const bool shared = t >= ts.t_r;
     int64_t b, j;
     if (!shared)
       decode_task(t, ts.nb_r, ts.nn_r, ts.gb_r, b, j);
     else
       decode_task(t - ts.t_r, ts.nb_s, ts.nn_s, kGroupBlocks, b, j);
+    before_rows(shared ? ts.nb_r + b : b, shared);
     if (threadIdx.x < BM) {
       const int r = threadIdx.x;
       if (!shared) {
@@ -702,6 +710,115 @@ __global__ __launch_bounds__((tile_threads<T, BM, kDownStrips, 1>()), 1) void do
         const int64_t n = n0 + m * BN + col;
         if (f >= 0 && n < H) Yb[(size_t)f * H + n] = v;
       });
+    }
+  }
+}
+
+template <typename T, int BM, int BN>
+__global__ __launch_bounds__((tile_threads<T, BM, kDownStrips, 1>()), 1) void down_kernel(
+    ForwardParams p) {
+  using TG = typename TileSel<T, BM, kDownStrips, 1>::type;
+  extern __shared__ __align__(16) char smem[];
+  __shared__ int64_t s_task;
+  __shared__ int s_tok[BM];
+  __shared__ int s_f[BM];   // output row: slot f (routed) or token (shared)
+  __shared__ float s_w[BM];
+  const TaskSpace ts = task_space(p, BM, kDownStrips * BN, p.H, p.H);
+  int q = blockIdx.x % kXcds, tried = 0;
+  int* counters = p.counters + kXcds;
+  QuotaState qs = quota_init(p.E);
+  TG g;
+  for (;;) {
+    if (threadIdx.x == 0)
+      s_task = p.sched_quota ? claim_quota(p, ts, p.counters + kQuotaBase + kQuotaStride, qs)
+                             : claim_task(counters, ts.total, q, tried);
+    __syncthreads();
+    const int64_t t = uniform64(s_task);
+    if (t < 0) break;
+    down_task<T, BM, BN>(p, ts, t, g, smem, s_tok, s_f, s_w, [](int64_t, bool) {});
+  }
+}
+
+// ------------------------------------------ up/gate and down in one launch
+// The FlashMoE review's single persistent kernel (Algorithm 1 and the task
+// graph of its "Technical details"): one grid runs both GEMMs' tasks. A
+// workgroup first claims up/gate tasks (own XCD's range, then the others);
+// once every up/gate queue is empty it claims down tasks the same way. A down
+// task of m-block b needs all of b's h columns, so it waits until the
+// m-block's readiness counter has counted every up/gate n-tile of b; each
+// up/gate task publishes its h stores (release at device scope) and then
+// adds one to that counter.
+// No wait can deadlock: a workgroup waits only after every up/gate task has
+// been claimed, and a claimed up/gate task runs to its end without waiting
+// (its workgroup is running, whatever the other workgroups do). As a guard
+// the wait is still bounded by the constant-rate clock (kReadyWaitTicks);
+// past it the task reads whatever h holds, so the kernel always ends.
+constexpr uint64_t kReadyWaitTicks = (uint64_t)1 << 28;  // about 2.7 s at 100 MHz
+
+__device__ __forceinline__ void wait_count(const int* ctr, int need) {
+  const uint64_t t0 = wall_clock64();
+  while (__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < need) {
+    __builtin_amdgcn_s_sleep(2);
+    if (wall_clock64() - t0 > kReadyWaitTicks) break;
+  }
+  // one acquire after the spin (not per poll: each acquire invalidates caches)
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+}
+
+template <int BM, int BN>
+__global__ __launch_bounds__((tile_threads<bf16_t, BM, 2, 2>()), 1) void fused_kernel(
+    ForwardParams p) {
+  using TG = typename TileSel<bf16_t, BM, 2, 2>::type;
+  static_assert(std::is_same<TG, typename TileSel<bf16_t, BM, kDownStrips, 1>::type>::value,
+                "one tile core (and one LDS ring) for both GEMMs");
+  extern __shared__ __align__(16) char smem[];
+  __shared__ int64_t s_task;
+  __shared__ int s_tok[BM];
+  __shared__ int s_f[BM];
+  __shared__ float s_w[BM];
+  const TaskSpace tu = task_space(p, BM, BN, p.D, p.Ds);
+  const TaskSpace td = task_space(p, BM, kDownStrips * BN, p.H, p.H);
+  int q = blockIdx.x % kXcds, tried = 0, phase = 0;  // thread 0 only
+  TG g;
+  for (;;) {
+    if (threadIdx.x == 0) {
+      int64_t t = -1;
+      if (phase == 0) {
+        t = claim_task(p.counters, tu.total, q, tried);
+        if (t < 0) {
+          phase = 1;
+          q = blockIdx.x % kXcds;
+          tried = 0;
+        }
+      }
+      if (phase == 1) {
+        t = claim_task(p.counters + kXcds, td.total, q, tried);
+        if (t >= 0) t += tu.total;
+      }
+      s_task = t;
+    }
+    __syncthreads();
+    const int64_t t = uniform64(s_task);
+    if (t < 0) break;
+    if (t < tu.total) {
+      const int64_t rb = upgate_task<bf16_t, BM, BN>(p, tu, t, g, smem, s_tok);
+      // Publish: each wave waits until its h stores have completed (vmcnt
+      // 0: they are in this XCD's L2), then one device-scope release by
+      // thread 0 writes the L2 back and the task is counted. A release fence
+      // in every wave would write the L2 back once per wave: measured 35%
+      // slower at prefill sizes, twice as slow at decode sizes.
+      wait_vmcnt<0>();
+      __syncthreads();
+      if (threadIdx.x == 0) {
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+        __hip_atomic_fetch_add(p.ready + rb, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    } else {
+      down_task<bf16_t, BM, BN>(p, td, t - tu.total, g, smem, s_tok, s_f, s_w,
+                                [&](int64_t rb, bool shared) {
+                                  if (threadIdx.x == 0)
+                                    wait_count(p.ready + rb, (int)(shared ? tu.nn_s : tu.nn_r));
+                                });
     }
   }
 }
@@ -1010,6 +1127,23 @@ static hipError_t dispatch_bm(const ForwardParams& p, int BM, bool up, hipStream
   }
 }
 
+template <int BM>
+static hipError_t launch_fused_t(const ForwardParams& p, hipStream_t st) {
+  return launch_persistent(fused_kernel<BM, upgate_bn<BM>()>, 0, tile_threads<bf16_t, BM, 2, 2>(),
+                           p, st);
+}
+
+hipError_t launch_forward_fused(const ForwardParams& p, int BM, hipStream_t st) {
+  switch (BM) {
+    case 16: return launch_fused_t<16>(p, st);
+    case 32: return launch_fused_t<32>(p, st);
+    case 64: return launch_fused_t<64>(p, st);
+    case 128: return launch_fused_t<128>(p, st);
+    case 256: return launch_fused_t<256>(p, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 hipError_t launch_forward_upgate(const ForwardParams& p, int dtype, int BM, hipStream_t st) {
   return dtype == 1 ? dispatch_bm<bf16_t>(p, BM, true, st) : dispatch_bm<float>(p, BM, true, st);
 }
@@ -1027,7 +1161,8 @@ int forward_lds_ok(int dtype, int BM) {
 // so the whole call can be captured in a HIP graph: the task counters, and
 // either the fp32 accumulator (atomic combine) or the kept flags (slot combine).
 __global__ __launch_bounds__(256) void setup_kernel(float* acc, int64_t n, uint8_t* flags,
-                                                    int64_t nflags, int* counters) {
+                                                    int64_t nflags, int* counters, int* ready,
+                                                    int64_t nready) {
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   const int64_t i0 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (acc != nullptr) {
@@ -1043,6 +1178,7 @@ __global__ __launch_bounds__(256) void setup_kernel(float* acc, int64_t n, uint8
     for (int64_t i = n16 * 16 + i0; i < nflags; i += stride) flags[i] = 0;
   }
   for (int64_t i = i0; i < kCounterInts; i += stride) counters[i] = 0;
+  for (int64_t i = i0; i < nready; i += stride) ready[i] = 0;
 }
 
 hipError_t launch_forward_setup(const ForwardParams& p, hipStream_t st) {
@@ -1054,7 +1190,7 @@ hipError_t launch_forward_setup(const ForwardParams& p, hipStream_t st) {
   if (blocks < 1) blocks = 1;
   if (blocks > 4096) blocks = 4096;
   hipLaunchKernelGGL(setup_kernel, dim3((unsigned)blocks), dim3(256), 0, st, acc, n, flags, nf,
-                     p.counters);
+                     p.counters, p.ready, p.fused ? p.n_ready : (int64_t)0);
   return hipGetLastError();
 }
 

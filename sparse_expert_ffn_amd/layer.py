@@ -15,9 +15,9 @@ from . import (MOE_BF16, make_shape, moe_align_block_size, moe_align_workspace_b
 class MoEBuffers:
     def __init__(self, S, H, D, E, k, D_shared=0, capacity=0, block_size=128, renormalize=1,
                  dtype=MOE_BF16, out_f32=False, atomic_combine=False, sched_quota=False,
-                 device="cuda"):
+                 fused_launch=False, device="cuda"):
         self.shape = make_shape(S, H, D, E, k, D_shared, capacity, block_size, renormalize,
-                                dtype, out_f32, atomic_combine, sched_quota)
+                                dtype, out_f32, atomic_combine, sched_quota, fused_launch)
         self.tdtype = torch.bfloat16 if dtype == MOE_BF16 and not out_f32 else torch.float32
         dev = torch.device(device)
         cap = S * k + E * (block_size - 1)

@@ -79,11 +79,13 @@ def block_size_for(wl):
     return suggest_block_size(wl.S, wl.k, wl.E, wl.capacity, wl.dtype)
 
 
-def buffers(wl, block_size=None, out_f32=False, atomic_combine=False, sched_quota=False):
+def buffers(wl, block_size=None, out_f32=False, atomic_combine=False, sched_quota=False,
+            fused_launch=False):
     bm = block_size or block_size_for(wl)
     return MoEBuffers(wl.S, wl.H, wl.D, wl.E, wl.k, wl.D_shared, wl.capacity, bm,
                       wl.renormalize, wl.dtype, out_f32=out_f32,
-                      atomic_combine=atomic_combine, sched_quota=sched_quota, device=DEV)
+                      atomic_combine=atomic_combine, sched_quota=sched_quota,
+                      fused_launch=fused_launch, device=DEV)
 
 
 class DeviceLayer:

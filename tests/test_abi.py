@@ -87,7 +87,7 @@ def test_gate_topk_validation(lib):
     assert gate(lib, dec, ws=FAKE, wsn=need - 1) == 3   # too small
     assert gate(lib, dec, ws=FAKE + 4, wsn=need) == 2   # misaligned
     s = shape()
-    s.flags = 8                                         # undefined flag bit
+    s.flags = 16                                        # undefined flag bit
     assert gate(lib, s) == 1
 
 
@@ -151,3 +151,13 @@ def test_forward_validation(lib):
     assert fwd(lib, shape(), A=FAKE + 2) == 2
     assert fwd(lib, shape(), ws_bytes=100) == 3
     assert fwd(lib, shape(S=0), A=None, O=None) == 0    # empty call, nothing enqueued
+    # one-launch form: bf16 only, not with the quota scheduler
+    assert fwd(lib, shape(dtype=moe.MOE_F32, fused_launch=True)) == 2
+    assert fwd(lib, shape(fused_launch=True, sched_quota=True)) == 2
+    s = shape()
+    s.flags = 16                                        # undefined flag bit
+    assert fwd(lib, s) == 1
+    assert moe.moe_forward_workspace_bytes(shape(dtype=moe.MOE_F32, fused_launch=True)) == 0
+    # readiness counters: one per routed and per shared m-block, more workspace
+    assert (moe.moe_forward_workspace_bytes(shape(D_shared=64, fused_launch=True))
+            >= moe.moe_forward_workspace_bytes(shape(D_shared=64)))
