@@ -72,7 +72,9 @@ __device__ __forceinline__ i32x4_t make_srd(const void* base, uint32_t bytes) {
 // one-instruction asm block so that the compiler does not add a wait for it in
 // front of later LDS reads of other stage buffers: the K loop orders these
 // loads itself (vmcnt wait on the issuing wave, then a workgroup barrier).
-// The instruction has no register result.
+// The instruction has no register result. NT = true sets the non-temporal
+// hint (data read once: do not keep it in the caches at the expense of data
+// that is reused).
 //
 // The compiler does not look inside the asm, so it does not insert the wait
 // states a vector memory instruction needs after a VALU op wrote one of its
@@ -80,13 +82,20 @@ __device__ __forceinline__ i32x4_t make_srd(const void* base, uint32_t bytes) {
 // from VGPR lanes under SGPR pressure). SGPR_FROM_VALU = true puts them in the
 // asm (s_nop 4); the default form relies on the descriptor being built by
 // scalar code, which a test checks on the compiled kernels.
-template <bool SGPR_FROM_VALU = false>
+template <bool SGPR_FROM_VALU = false, bool NT = false>
 __device__ __forceinline__ void dma16(i32x4_t srd, uint32_t voff, const void* lds_dst) {
   const uint32_t m0v = (uint32_t)reinterpret_cast<uintptr_t>(
       (const __attribute__((address_space(3))) char*)lds_dst);
-  if constexpr (SGPR_FROM_VALU)
+  if constexpr (SGPR_FROM_VALU && NT)
+    asm volatile("s_nop 4\n\tbuffer_load_dwordx4 %0, %1, 0 offen nt lds" ::"v"(voff), "s"(srd),
+                 "{m0}"(m0v)
+                 : "memory");
+  else if constexpr (SGPR_FROM_VALU)
     asm volatile("s_nop 4\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(srd),
                  "{m0}"(m0v)
+                 : "memory");
+  else if constexpr (NT)
+    asm volatile("buffer_load_dwordx4 %0, %1, 0 offen nt lds" ::"v"(voff), "s"(srd), "{m0}"(m0v)
                  : "memory");
   else
     asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(srd), "{m0}"(m0v)
@@ -111,7 +120,10 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-template <int BM_, int NB_, int NW_ = 8, int BK_ = 64, int LDS_BUDGET = 144 * 1024>
+// B_STREAM: the B operand (the weights) is read once per call, no other task
+// reuses it from the caches; its loads carry the non-temporal hint.
+template <int BM_, int NB_, int NW_ = 8, int BK_ = 64, int LDS_BUDGET = 144 * 1024,
+          bool B_STREAM = false>
 struct TileGemmDirect {
   static constexpr bool DIRECT = true;  // the LDS-direct core (vs gemm_tile.h)
   static constexpr int BM = BM_, BN = 128, NB = NB_;
@@ -250,7 +262,7 @@ struct TileGemmDirect {
       if constexpr (NB > 1) {
         if (m == 1) rb = rsrc_b[1];
       }
-      dma16<SGPR_FROM_VALU>(rb, o, base + A_LDS + q * 1024);
+      dma16<SGPR_FROM_VALU, B_STREAM>(rb, o, base + A_LDS + q * 1024);
     }
   }
 

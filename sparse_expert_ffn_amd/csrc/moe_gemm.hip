@@ -30,7 +30,8 @@ namespace moe {
 
 // Tile core of the persistent grouped GEMMs: bf16 loads straight into LDS
 // (gemm_direct.h); fp32 stages through registers (gemm_tile.h).
-template <typename T, int BM, int NB, int STAGING>
+// BS (bf16 core only): the weights are streamed once (non-temporal loads).
+template <typename T, int BM, int NB, int STAGING, bool BS = false>
 struct TileSel {
   using type = TileGemm<T, BM, 128, NB, false, STAGING>;
 };
@@ -43,9 +44,9 @@ template <int BM>
 constexpr int stage_k() {
   return MOE_STAGE_K > 0 ? MOE_STAGE_K : (BM >= 256 ? 32 : 64);
 }
-template <int BM, int NB, int STAGING>
-struct TileSel<bf16_t, BM, NB, STAGING> {
-  using type = TileGemmDirect<BM, NB, 8, stage_k<BM>()>;
+template <int BM, int NB, int STAGING, bool BS>
+struct TileSel<bf16_t, BM, NB, STAGING, BS> {
+  using type = TileGemmDirect<BM, NB, 8, stage_k<BM>(), 144 * 1024, BS>;
 };
 
 template <typename TG>
@@ -591,9 +592,9 @@ __device__ __forceinline__ int64_t upgate_task(const ForwardParams& p, const Tas
   }
 }
 
-template <typename T, int BM, int BN>
+template <typename T, int BM, int BN, bool BS>
 __global__ __launch_bounds__((tile_threads<T, BM, 2, 2>()), 1) void upgate_kernel(ForwardParams p) {
-  using TG = typename TileSel<T, BM, 2, 2>::type;
+  using TG = typename TileSel<T, BM, 2, 2, BS>::type;
   extern __shared__ __align__(16) char smem[];
   __shared__ int64_t s_task;
   __shared__ int s_tok[BM];
@@ -714,10 +715,10 @@ __device__ __forceinline__ void down_task(const ForwardParams& p, const TaskSpac
   }
 }
 
-template <typename T, int BM, int BN>
+template <typename T, int BM, int BN, bool BS>
 __global__ __launch_bounds__((tile_threads<T, BM, kDownStrips, 1>()), 1) void down_kernel(
     ForwardParams p) {
-  using TG = typename TileSel<T, BM, kDownStrips, 1>::type;
+  using TG = typename TileSel<T, BM, kDownStrips, 1, BS>::type;
   extern __shared__ __align__(16) char smem[];
   __shared__ int64_t s_task;
   __shared__ int s_tok[BM];
@@ -765,11 +766,11 @@ __device__ __forceinline__ void wait_count(const int* ctr, int need) {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
 }
 
-template <int BM, int BN>
+template <int BM, int BN, bool BS>
 __global__ __launch_bounds__((tile_threads<bf16_t, BM, 2, 2>()), 1) void fused_kernel(
     ForwardParams p) {
-  using TG = typename TileSel<bf16_t, BM, 2, 2>::type;
-  static_assert(std::is_same<TG, typename TileSel<bf16_t, BM, kDownStrips, 1>::type>::value,
+  using TG = typename TileSel<bf16_t, BM, 2, 2, BS>::type;
+  static_assert(std::is_same<TG, typename TileSel<bf16_t, BM, kDownStrips, 1, BS>::type>::value,
                 "one tile core (and one LDS ring) for both GEMMs");
   extern __shared__ __align__(16) char smem[];
   __shared__ int64_t s_task;
@@ -975,9 +976,9 @@ __device__ __forceinline__ void stream_epilogue(const TG& g, const ForwardParams
   });
 }
 
-template <int BM>
+template <int BM, bool BS>
 __global__ __launch_bounds__(512, 1) void down_stream_kernel(ForwardParams p) {
-  using TG = typename TileSel<bf16_t, BM, kDownStrips, 1>::type;
+  using TG = typename TileSel<bf16_t, BM, kDownStrips, 1, BS>::type;
   static_assert(TG::DIRECT, "the streaming kernel runs on the LDS-direct core");
   constexpr int NSTAGE = TG::NSTAGE;
   __shared__ __align__(16) char ring[TG::LDS_BYTES];
@@ -1094,21 +1095,44 @@ static bool down_stream_ok(const ForwardParams& p) {
          (kmax + TG::BK - 1) / TG::BK <= 16;
 }
 
+// The weights are read once per call when the routing leaves about one
+// m-block per expert: under half a block of assignments per expert on
+// average (decode; DeepSeek-V3's 256 experts at 256-row blocks). The task
+// order then runs each m-block's n-tiles back to back and no task reuses
+// another's weight strip, so the weight loads take the non-temporal hint
+// (measured: decode -9% per step, dsv3 -1%; with several m-blocks per expert
+// sharing each strip in L2, prefill, the hint cost 1-2%). A cache hint only:
+// the results are the same either way.
+static bool weights_streamed(const ForwardParams& p, int BM) {
+  return p.E > 0 && 2 * ((p.F + p.E - 1) / p.E) <= BM;
+}
+
 template <typename T, int BM>
 static hipError_t launch_upgate_t(const ForwardParams& p, hipStream_t st) {
   constexpr int BN = upgate_bn<BM>();
-  return launch_persistent(upgate_kernel<T, BM, BN>, lds_bytes<T, BM, 2, 2>(),
+  if constexpr (sizeof(T) == 2) {
+    if (weights_streamed(p, BM))
+      return launch_persistent(upgate_kernel<T, BM, BN, true>, lds_bytes<T, BM, 2, 2>(),
+                               tile_threads<T, BM, 2, 2>(), p, st);
+  }
+  return launch_persistent(upgate_kernel<T, BM, BN, false>, lds_bytes<T, BM, 2, 2>(),
                            tile_threads<T, BM, 2, 2>(), p, st);
 }
 
 template <typename T, int BM>
 static hipError_t launch_down_t(const ForwardParams& p, hipStream_t st) {
   if constexpr (sizeof(T) == 2) {
+    const bool bs = weights_streamed(p, BM);
     if (down_stream_ok<BM>(p))
-      return launch_persistent(down_stream_kernel<BM>, 0, 512, p, st);
+      return bs ? launch_persistent(down_stream_kernel<BM, true>, 0, 512, p, st)
+                : launch_persistent(down_stream_kernel<BM, false>, 0, 512, p, st);
+    if (bs)
+      return launch_persistent(down_kernel<T, BM, down_bn<BM>(), true>,
+                               lds_bytes<T, BM, kDownStrips, 1>(),
+                               tile_threads<T, BM, kDownStrips, 1>(), p, st);
   }
   constexpr int BN = down_bn<BM>();
-  return launch_persistent(down_kernel<T, BM, BN>, lds_bytes<T, BM, kDownStrips, 1>(),
+  return launch_persistent(down_kernel<T, BM, BN, false>, lds_bytes<T, BM, kDownStrips, 1>(),
                            tile_threads<T, BM, kDownStrips, 1>(), p, st);
 }
 
@@ -1129,8 +1153,11 @@ static hipError_t dispatch_bm(const ForwardParams& p, int BM, bool up, hipStream
 
 template <int BM>
 static hipError_t launch_fused_t(const ForwardParams& p, hipStream_t st) {
-  return launch_persistent(fused_kernel<BM, upgate_bn<BM>()>, 0, tile_threads<bf16_t, BM, 2, 2>(),
-                           p, st);
+  if (weights_streamed(p, BM))
+    return launch_persistent(fused_kernel<BM, upgate_bn<BM>(), true>, 0,
+                             tile_threads<bf16_t, BM, 2, 2>(), p, st);
+  return launch_persistent(fused_kernel<BM, upgate_bn<BM>(), false>, 0,
+                           tile_threads<bf16_t, BM, 2, 2>(), p, st);
 }
 
 hipError_t launch_forward_fused(const ForwardParams& p, int BM, hipStream_t st) {
