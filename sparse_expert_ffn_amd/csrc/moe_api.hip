@@ -315,6 +315,14 @@ moe_status moe_forward(const moe_shape* shape, const void* A, const void* W_up,
   p.ready = reinterpret_cast<int*>(ws + L.ready);
   p.n_ready = L.n_ready;
   p.fused = (shape->flags & MOE_FUSED_LAUNCH) ? 1 : 0;
+  // Slot rows far larger than the 256 MB MALL (DeepSeek-V3 sizes: 0.94 GB)
+  // go to HBM and come back from it anyway: the down kernel stores them and
+  // the combine loads them with the non-temporal hint (measured: down -3%,
+  // combine -15% there). Rows about the MALL's size (prefill, 0.27 GB) are
+  // partly served from it, and the hint measured 8% slower for both.
+  const double slot_bytes =
+      (double)(shape->S * shape->k + (shape->D_shared > 0 ? shape->S : 0)) * shape->H * 4.0;
+  p.slots_nt = (!atomic_combine(shape) && slot_bytes > 512.0 * (1 << 20)) ? 1 : 0;
   p.S = shape->S;
   p.H = shape->H;
   p.D = shape->D;

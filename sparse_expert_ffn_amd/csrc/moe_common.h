@@ -115,6 +115,8 @@ struct ForwardParams {
                           // so that each down-projection K stage is contiguous; 0: row-major
   int grid;               // persistent workgroups
   int fused;              // 1: up/gate and down in one launch (bf16)
+  int slots_nt;           // 1: the slot rows Y / Ys are written and read with the
+                          // non-temporal hint (they far exceed the MALL)
 };
 
 constexpr int kAlignSeg = 512;   // assignments per wave segment in the align kernels

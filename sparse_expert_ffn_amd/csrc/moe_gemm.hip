@@ -624,8 +624,10 @@ constexpr int kDownStrips = 2;
 // One down task t of the task space ts, run by the whole workgroup.
 // before_rows(rb, shared) runs on every thread once the m-block is known and
 // before the barrier that precedes the task's first read of h (rb: the
-// m-block's readiness index, as upgate_task returns it).
-template <typename T, int BM, int BN, typename TG, typename BeforeRows>
+// m-block's readiness index, as upgate_task returns it). SLOT_NT: honour
+// p.slots_nt (a second copy of the slot epilogue; the one-launch kernel
+// leaves it out, its SGPR budget has no room for it).
+template <typename T, int BM, int BN, bool SLOT_NT, typename TG, typename BeforeRows>
 __device__ __forceinline__ void down_task(const ForwardParams& p, const TaskSpace& ts, int64_t t,
                                           TG& g, char* smem, int* s_tok, int* s_f, float* s_w,
                                           BeforeRows before_rows) {
@@ -706,11 +708,18 @@ __device__ __forceinline__ void down_task(const ForwardParams& p, const TaskSpac
       // the row into its own slot: routed -> Y[f], shared -> Ys[token]; the
       // combine applies the router weight
       float* Yb = shared ? p.Ys : p.Y;
-      g.for_each([&](int m, int row, int col, float v) {
-        const int f = s_f[row];
-        const int64_t n = n0 + m * BN + col;
-        if (f >= 0 && n < H) Yb[(size_t)f * H + n] = v;
-      });
+      if (SLOT_NT && p.slots_nt)
+        g.for_each([&](int m, int row, int col, float v) {
+          const int f = s_f[row];
+          const int64_t n = n0 + m * BN + col;
+          if (f >= 0 && n < H) __builtin_nontemporal_store(v, Yb + (size_t)f * H + n);
+        });
+      else
+        g.for_each([&](int m, int row, int col, float v) {
+          const int f = s_f[row];
+          const int64_t n = n0 + m * BN + col;
+          if (f >= 0 && n < H) Yb[(size_t)f * H + n] = v;
+        });
     }
   }
 }
@@ -736,7 +745,7 @@ __global__ __launch_bounds__((tile_threads<T, BM, kDownStrips, 1>()), 1) void do
     __syncthreads();
     const int64_t t = uniform64(s_task);
     if (t < 0) break;
-    down_task<T, BM, BN>(p, ts, t, g, smem, s_tok, s_f, s_w, [](int64_t, bool) {});
+    down_task<T, BM, BN, true>(p, ts, t, g, smem, s_tok, s_f, s_w, [](int64_t, bool) {});
   }
 }
 
@@ -815,11 +824,10 @@ __global__ __launch_bounds__((tile_threads<bf16_t, BM, 2, 2>()), 1) void fused_k
         __hip_atomic_fetch_add(p.ready + rb, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
     } else {
-      down_task<bf16_t, BM, BN>(p, td, t - tu.total, g, smem, s_tok, s_f, s_w,
-                                [&](int64_t rb, bool shared) {
-                                  if (threadIdx.x == 0)
-                                    wait_count(p.ready + rb, (int)(shared ? tu.nn_s : tu.nn_r));
-                                });
+      down_task<bf16_t, BM, BN, false>(
+          p, td, t - tu.total, g, smem, s_tok, s_f, s_w, [&](int64_t rb, bool shared) {
+            if (threadIdx.x == 0) wait_count(p.ready + rb, (int)(shared ? tu.nn_s : tu.nn_r));
+          });
     }
   }
 }
@@ -1297,11 +1305,7 @@ hipError_t launch_forward_combine(const ForwardParams& p, hipStream_t st) {
   int64_t blocks = (total + 255) / 256;
   if (blocks > 8192) blocks = 8192;
   const float* Ys = p.Ds > 0 ? p.Ys : nullptr;
-  // Slot rows far larger than the 256 MB MALL (DeepSeek-V3 sizes: 0.94 GB)
-  // come from HBM anyway: non-temporal loads (measured -15% for that
-  // combine). Rows about the MALL's size (prefill, 0.27 GB) are partly served
-  // from it, and the hint measured 8% slower there.
-  const bool nt = (double)(p.F + (Ys ? p.S : 0)) * p.H * sizeof(float) > 512.0 * (1 << 20);
+  const bool nt = p.slots_nt != 0;
   auto go = [&](auto kernel) {
     hipLaunchKernelGGL(kernel, dim3((unsigned)blocks), dim3(256), 0, st, p.Y, Ys, p.kept,
                        p.topk_w, p.O, p.S, p.H, p.k);
