@@ -119,3 +119,26 @@ def test_fused_fullsize_same_output(name):
     for o in ones:
         assert np.all(np.isfinite(o))
         assert np.array_equal(two, o)
+
+
+@pytest.mark.parametrize("name,S,bm", [("prefill_skew", 300, 128), ("dsv3", 40, 256)])
+def test_fused_atomic_combine(orc, name, S, bm):
+    """One launch with the atomic combine (fp32 accumulator, order not fixed):
+    to the parity bar against the oracle."""
+    wl = wk.WORKLOADS[name].with_tokens(S)
+    log(f"[fused atomic {name} S={S} bm={bm}]")
+    li = wk.draw_layer(wl)
+    G = orc.gate_logits(li.A, li.Wr, li.bias)
+    L = DeviceLayer(wl, li)
+    buf = buffers(wl, bm, out_f32=True, atomic_combine=True, fused_launch=True)
+    buf.forward_ws.fill_(0xFF)
+    buf.route(logits_in=dev(G))
+    buf.O.fill_(float("nan"))
+    out = host(L.forward(buf)).copy()
+    torch.cuda.synchronize()
+    assert np.all(np.isfinite(out))
+    ref = orc.layer(li.A, li.Wr, li.bias, li.W_up, li.W_gate, li.W_down, wl.k,
+                    renormalize=wl.renormalize, capacity=wl.capacity, Ws_up=li.Ws_up,
+                    Ws_gate=li.Ws_gate, Ws_down=li.Ws_down, logits=G)
+    err, tol = parity(wl, out, ref["O"])
+    assert err <= tol
