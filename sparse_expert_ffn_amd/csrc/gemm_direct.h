@@ -537,8 +537,13 @@ struct TileGemmDirect {
     K_ = K;
     const int nk = (int)((K + BK - 1) / BK);
     if (nk <= 0) return;
-    wait_vmcnt<0>();  // nothing of an earlier tile still writing LDS
-    __syncthreads();
+    // No wait for this wave's earlier memory operations here: an earlier
+    // tile's loads all landed before its mainloop returned, and what may
+    // still be in flight are an epilogue's global stores. vmcnt retires in
+    // issue order, so the first stage's wait below covers them, and their
+    // latency overlaps the first stages' loads (measured: up/gate -1% at
+    // prefill sizes).
+    __syncthreads();  // every wave is done with the ring
 #pragma unroll
     for (int s = 0; s + 1 < NSTAGE; ++s) issue_stage(lds + s * STAGE, s);
     kloop_n(lds, nk, nact);
