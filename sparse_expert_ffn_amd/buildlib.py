@@ -24,17 +24,30 @@ def sources():
     return sorted(glob.glob(os.path.join(PKG, "csrc", "*.hip")))
 
 
+def _code_only(text: str) -> str:
+    """C/C++ source with comments removed and whitespace runs collapsed to one
+    space (string literals kept as they are)."""
+    import re
+    string = r'"(?:\\.|[^"\\\n])*"'
+    keep = lambda m: m.group(0) if m.group(0).startswith('"') else " "
+    text = re.sub(string + r'|//[^\n]*|/\*.*?\*/', keep, text, flags=re.S)
+    return re.sub(string + r'|\s+', keep, text).strip()
+
+
 def source_digest() -> str:
-    """SHA-256 over what determines the compiled kernels: the HIP sources
-    and headers under csrc/ and the compiler flags. Measurement records
-    (hardware counters) carry it, so that a record taken on other kernels is
-    recognised as stale."""
+    """SHA-256 over what determines the compiled kernels: the code of the HIP
+    sources and headers under csrc/ and of the public header (comments and
+    layout left out, so a comment edit keeps the digest) and the compiler
+    flags. Measurement records (hardware counters) carry it, so that a record
+    taken on other kernels is recognised as stale."""
     import hashlib
     h = hashlib.sha256()
-    for f in sorted(glob.glob(os.path.join(PKG, "csrc", "*"))):
+    files = sorted(glob.glob(os.path.join(PKG, "csrc", "*"))) + \
+        sorted(glob.glob(os.path.join(ROOT, "include", "*.h")))
+    for f in files:
         h.update(os.path.relpath(f, ROOT).encode())
-        with open(f, "rb") as fh:
-            h.update(fh.read())
+        with open(f, encoding="utf-8") as fh:
+            h.update(_code_only(fh.read()).encode())
     h.update(" ".join(HIPCC_FLAGS).encode())
     return h.hexdigest()
 

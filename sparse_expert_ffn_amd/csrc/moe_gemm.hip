@@ -1,7 +1,9 @@
-// GEMM kernels of the MoE layer: gate scores, and the two persistent grouped
-// GEMMs of the expert FFN (up/gate with a SwiGLU epilogue, down with the
-// router-weighted combine epilogue), plus the accumulator setup and the
-// final output cast.
+// GEMM kernels of the MoE layer: gate scores (with the top-k fused, or split
+// along H), the two persistent grouped GEMMs of the expert FFN (up/gate with
+// a SwiGLU epilogue; down writing each kept row to its fp32 slot, or adding
+// it with atomics), the streaming down kernel for decode-sized tiles, both
+// GEMMs in one launch (MOE_FUSED_LAUNCH), the setup fill, the ordered slot
+// combine and the output cast.
 //
 // Persistent scheduling (Weave review, sections 2.1-2.2 and 5.1): the work of
 // a grouped GEMM is cut into tile tasks (m-block of BM sorted rows, n-tile of
