@@ -47,6 +47,10 @@ def parse():
     ap.add_argument("--launch", choices=("two", "one"), default="two",
                     help="the expert GEMMs as two persistent launches (up/gate, then down) "
                          "or as one (down tasks wait per m-block for its up/gate tasks)")
+    ap.add_argument("--weight-copies", type=int, default=1,
+                    help="rotate the steps over this many copies of the expert weights (a "
+                         "cold-cache figure when one copy of the touched weights fits the "
+                         "256 MB MALL)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU work of the oracle baseline sample")
@@ -183,14 +187,22 @@ def main():
         Wsu = td(wk.draw_tensor(wl, wk.T_WSUP, (wl.H, wl.D_shared), ssu))
         Wsg = td(wk.draw_tensor(wl, wk.T_WSGATE, (wl.H, wl.D_shared), ssu))
         Wsd = td(wk.draw_tensor(wl, wk.T_WSDOWN, (wl.D_shared, wl.H), ssd))
+    n_copies = max(1, args.weight_copies)
+    copies = [(Wu, Wg, Wd, Wsu, Wsg, Wsd)]
+    for _ in range(n_copies - 1):  # same values, other addresses
+        copies.append(tuple(None if x is None else x.clone() for x in copies[0]))
     buf = MoEBuffers(wl.S, wl.H, wl.D, wl.E, wl.k, wl.D_shared, wl.capacity, bm,
                      wl.renormalize, wl.dtype, sched_quota=args.sched == "quota",
                      fused_launch=args.launch == "one", device=dev)
     one = args.launch == "one"
     stream = torch.cuda.current_stream()
 
+    n_step = [0]
+
     def step():
-        buf.run(A_d, Wr_d, Wu, Wg, Wd, Wsu, Wsg, Wsd, router_bias=b_d, stream=stream)
+        w = copies[n_step[0] % n_copies]
+        n_step[0] += 1
+        buf.run(A_d, Wr_d, *w, router_bias=b_d, stream=stream)
 
     for _ in range(args.warmup):
         step()
@@ -227,6 +239,16 @@ def main():
     moe.moe_profile_enable(False)
     small_ms, n_small = moe.moe_profile_collect(4)
     down_ms = small_ms[2] / max(n_small, 1)
+    # per-step times (an event pair per step), for the median; after the timed
+    # region, which holds no per-step markers
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(min(args.steps, 16))]
+    for e0, e1 in evs:
+        e0.record(stream)
+        step()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    med_ms = float(np.median([e0.elapsed_time(e1) for e0, e1 in evs])) if evs else None
 
     peak = PEAK_BF16_TFLOPS if wl.dtype == wk.BF16 else PEAK_F32_TFLOPS
     # the roofline kernel: up/gate, or with one launch both expert GEMMs
@@ -267,6 +289,7 @@ def main():
         "config": {"workload": wl.name, "S": wl.S, "H": wl.H, "D": wl.D, "E": wl.E, "k": wl.k,
                    "D_shared": wl.D_shared, "capacity": wl.capacity, "block_size": bm,
                    "scheduler": args.sched, "launch": args.launch,
+                   "weight_copies": n_copies,
                    "parallelism": "single GPU"},
         "roofline": roof,
         "layer": {"tflops": layer_tflops, "mfma_frac": layer_tflops / peak,
@@ -278,7 +301,7 @@ def main():
                   "down_tflops": None if one else cnt["flops_down"] / (down_ms * 1e-3) / 1e12,
                   "setup_ms": small_ms[0] / max(n_small, 1),
                   "combine_ms": small_ms[3] / max(n_small, 1),
-                  "wall_s": wall},
+                  "median_ms_per_step": med_ms, "wall_s": wall},
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
