@@ -190,24 +190,25 @@ struct TileGemmDirect {
   }
 
   // A: buffer of a_bytes at a_base, row_off(r) = byte offset of row r or kOob.
-  // a_blocked = false: rows K-contiguous (element k of row r at row_off(r) +
-  // 2k). a_blocked = true: BM rows stored as slabs of 32 columns, slab by
-  // slab (element k of row r at (k / 32) * BM * 64 + r * 64 + 2 (k % 32); the
-  // caller's row_off(r) is then r * 64), so each stage of A is one contiguous
-  // block.
+  // a_slab_rows = 0: rows K-contiguous (element k of row r at row_off(r) +
+  // 2k). a_slab_rows = R > 0: a block of R rows stored as slabs of 32
+  // columns, slab by slab (element k of block row r at (k / 32) * R * 64 +
+  // r * 64 + 2 (k % 32); the caller's row_off(r) is then the row's r * 64),
+  // so each stage of A is one contiguous block. R is the tile's BM, or
+  // larger when the tile covers part of a block's rows.
   // B[m]: base of weight matrix m (K x ldb, row-major) with b_bytes[m] bytes;
   // the tile covers its columns n0 .. n0 + BN, of which ncols[m] are valid.
   template <typename RowOff>
   __device__ __forceinline__ void setup(const void* a_base, uint32_t a_bytes, RowOff row_off,
                                         const char* const* B, const uint32_t* b_bytes,
                                         int64_t ldb, int64_t n0, const int64_t* ncols,
-                                        bool a_blocked = false) {
+                                        int a_slab_rows = 0) {
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     rsrc_a = make_srd(a_base, a_bytes);
 #pragma unroll
     for (int m = 0; m < NB; ++m) rsrc_b[m] = make_srd(B[m], b_bytes[m]);
-    a_stage_bytes = a_blocked ? (uint32_t)(BK / 32 * BM * 64) : (uint32_t)(BK * ES);
+    a_stage_bytes = a_slab_rows ? (uint32_t)(BK / 32 * a_slab_rows * 64) : (uint32_t)(BK * ES);
     b_stage_bytes = (uint32_t)(BK * ldb * ES);
 #pragma unroll
     for (int t = 0; t < A_PW; ++t) {
@@ -217,7 +218,8 @@ struct TileGemmDirect {
         const int r = q * (1024 / A_ROWB) + lane / ACH;
         const int c = (lane % ACH) ^ aswz(r);  // logical chunk stored in this lane's slot
         const uint32_t ro = row_off(r);
-        if (ro != kOob) o = a_blocked ? ro + (c >> 2) * (BM * 64) + (c & 3) * 16 : ro + c * 16;
+        if (ro != kOob)
+          o = a_slab_rows ? ro + (c >> 2) * (a_slab_rows * 64) + (c & 3) * 16 : ro + c * 16;
       }
       aoff[t] = o;
     }

@@ -56,12 +56,20 @@ constexpr bool is_direct() {
   return TG::DIRECT;
 }
 
-// The direct core's static LDS ring: one per tile core type, so kernels that
-// run several GEMMs on one core share it.
+// The direct cores' static LDS ring: one buffer for every core type, so a
+// kernel that runs tiles of several shapes (whole and half tiles, or both
+// GEMMs) holds a single ring.
+constexpr int kRingBytes = 144 * 1024;
+
+__device__ __forceinline__ char* lds_ring_bytes() {
+  __shared__ __align__(16) char ring[kRingBytes];
+  return ring;
+}
+
 template <typename TG>
 __device__ __forceinline__ char* lds_ring() {
-  __shared__ __align__(16) char ring[TG::LDS_BYTES];
-  return ring;
+  static_assert(TG::LDS_BYTES <= kRingBytes, "ring size");
+  return lds_ring_bytes();
 }
 
 // Run the K loop of tile core TG. The direct core gets the static LDS ring
@@ -396,6 +404,58 @@ __device__ __forceinline__ int64_t claim_task(int* counters, int64_t total, int&
   return -1;
 }
 
+// Long-tail splitting (the Weave review's tail handling, section 5.1). Tasks
+// cost about the same, so when a queue's n tasks are not a multiple of its R
+// workgroups, n mod R of them form a last round that only some workgroups
+// run while the others wait for the kernel's end (measured: 13% of the
+// up/gate kernel's workgroup time idle at prefill_skew, about 1,080 tasks on
+// 256 workgroups). Those last n mod R tasks of each queue are claimed as two
+// halves, rows [0, BM/2) and [BM/2, BM) of the tile, each run by a whole
+// workgroup on the BM/2-row tile core, so a half takes about half a task.
+// The half core adds the same 32-wide K chunks in the same order into each
+// output element as the whole-tile core, so the result is the same, bit for
+// bit. Claimed ids are (task << 2) | part: part 0 = whole tile, 1 = the first
+// half of the rows, 2 = the second. R = workgroups per XCD; split = false
+// keeps every task whole.
+__device__ __forceinline__ int64_t claim_task_split(int* counters, int64_t total, int64_t R,
+                                                    bool split, int& q, int& tried) {
+  while (tried < kXcds) {
+    const int64_t lo = total * q / kXcds;
+    const int64_t n = total * (q + 1) / kXcds - lo;
+    if (n > 0) {
+      const int64_t k = split ? n % R : 0;  // tasks cut in two
+      const int c = atomicAdd(&counters[q], 1);
+      if (c < n + k) {
+        const int64_t whole = n - k;
+        if (c < whole) return (lo + c) << 2;
+        const int64_t v = c - whole;
+        return ((lo + whole + v / 2) << 2) | (1 + (v & 1));
+      }
+    }
+    q = (q + 1) % kXcds;
+    ++tried;
+  }
+  return -1;
+}
+
+// Workgroups per XCD of this grid.
+__device__ __forceinline__ int64_t wgs_per_xcd() {
+  return gridDim.x >= kXcds ? gridDim.x / kXcds : 1;
+}
+
+// The half-tile core of a persistent kernel with BM-row tiles: the LDS-direct
+// core at BM/2 rows, where BM/2 still gives each SIMD one wave of each row
+// group (bf16, BM >= 64); void where tasks are not split.
+template <typename T, int BM, int NB, int STAGING, bool BS>
+struct HalfSel {
+  using type = void;
+};
+template <int BM, int NB, int STAGING, bool BS>
+struct HalfSel<bf16_t, BM, NB, STAGING, BS> {
+  using type = std::conditional_t<(BM >= 64),
+                                  typename TileSel<bf16_t, BM / 2, NB, STAGING, BS>::type, void>;
+};
+
 // ---------------------------------------------------- quota scheduler
 // Ablation baseline (the Weave review's comparator, sections 1.2-1.3: a fixed
 // number of SMs per expert): workgroup g serves only the experts
@@ -510,12 +570,16 @@ constexpr int tile_threads() {
   return TileSel<T, BM, NB, STAGING>::type::THREADS;
 }
 
-// One up/gate task t of the task space ts, run by the whole workgroup.
-// Returns the readiness index of its m-block (b routed, nb_r + b shared).
-template <typename T, int BM, int BN, typename TG>
+// One up/gate task t of the task space ts (m-blocks of BMB rows), run by
+// the whole workgroup on tile core TG: a whole block (TG::BM = BMB, row0 = 0)
+// or the rows row0 .. row0 + TG::BM of it. Returns the readiness index of its
+// m-block (b routed, nb_r + b shared).
+template <typename T, int BMB, int BN, typename TG>
 __device__ __forceinline__ int64_t upgate_task(const ForwardParams& p, const TaskSpace& ts,
-                                               int64_t t, TG& g, char* smem, int* s_tok) {
+                                               int64_t t, int row0, TG& g, char* smem,
+                                               int* s_tok) {
   static_assert(TG::BN == BN, "tile width");
+  constexpr int BM = TG::BM;  // tile rows
   {
     const bool shared = t >= ts.t_r;
     int64_t b, j;
@@ -527,13 +591,13 @@ __device__ __forceinline__ int64_t upgate_task(const ForwardParams& p, const Tas
       const int r = threadIdx.x;
       int tok;
       if (!shared) {
-        const int f = p.sorted_ids[b * BM + r];
+        const int f = p.sorted_ids[b * BMB + row0 + r];
         tok = f < p.F ? (int)(f / p.k) : -1;
         // slot combine: the first n-tile's task of a block marks its kept
         // assignments (the flags were cleared by the setup kernel)
         if (!p.atomic_combine && j == 0 && f < p.F) p.kept[f] = 1;
       } else {
-        const int64_t s = b * BM + r;
+        const int64_t s = b * BMB + row0 + r;
         tok = s < p.S ? (int)s : -1;
       }
       s_tok[r] = tok;
@@ -582,10 +646,11 @@ __device__ __forceinline__ int64_t upgate_task(const ForwardParams& p, const Tas
           if (s_tok[row] >= 0 && col < N) {
             const float u = g.acc[0][i][jj][r];
             const float gv = g.acc[1][i][jj][r];
+            const int brow = row0 + row;  // row in the block
             const size_t o = p.h_blocked
-                                 ? (size_t)b * BM * N + (size_t)(col >> 5) * (BM * 32) + row * 32 +
-                                       (col & 31)
-                                 : (size_t)(b * BM + row) * N + col;
+                                 ? (size_t)b * BMB * N + (size_t)(col >> 5) * (BMB * 32) +
+                                       brow * 32 + (col & 31)
+                                 : (size_t)(b * BMB + brow) * N + col;
             out[o] = from_f32<T>(silu_f32(u) * gv);
           }
         }
@@ -603,15 +668,31 @@ __global__ __launch_bounds__((tile_threads<T, BM, 2, 2>()), 1) void upgate_kerne
   const TaskSpace ts = task_space(p, BM, BN, p.D, p.Ds);
   int q = blockIdx.x % kXcds, tried = 0;
   QuotaState qs = quota_init(p.E);
+  using TH = typename HalfSel<T, BM, 2, 2, BS>::type;
+  constexpr bool kHalves = !std::is_void<TH>::value;
+  const bool split = kHalves && !p.sched_quota;
   TG g;
   for (;;) {
-    if (threadIdx.x == 0)
-      s_task = p.sched_quota ? claim_quota(p, ts, p.counters + kQuotaBase, qs)
-                             : claim_task(p.counters, ts.total, q, tried);
+    if (threadIdx.x == 0) {
+      if (p.sched_quota) {
+        const int64_t t = claim_quota(p, ts, p.counters + kQuotaBase, qs);
+        s_task = t < 0 ? -1 : t << 2;
+      } else {
+        s_task = claim_task_split(p.counters, ts.total, wgs_per_xcd(), split, q, tried);
+      }
+    }
     __syncthreads();
-    const int64_t t = uniform64(s_task);
-    if (t < 0) break;
-    upgate_task<T, BM, BN>(p, ts, t, g, smem, s_tok);
+    const int64_t c = uniform64(s_task);
+    if (c < 0) break;
+    const int part = (int)(c & 3);
+    if constexpr (kHalves) {
+      if (part != 0) {
+        TH gh;
+        upgate_task<T, BM, BN>(p, ts, c >> 2, (part - 1) * (BM / 2), gh, smem, s_tok);
+        continue;
+      }
+    }
+    upgate_task<T, BM, BN>(p, ts, c >> 2, 0, g, smem, s_tok);
   }
 }
 
@@ -629,11 +710,14 @@ constexpr int kDownStrips = 2;
 // m-block's readiness index, as upgate_task returns it). SLOT_NT: honour
 // p.slots_nt (a second copy of the slot epilogue; the one-launch kernel
 // leaves it out, its SGPR budget has no room for it).
-template <typename T, int BM, int BN, bool SLOT_NT, typename TG, typename BeforeRows>
+// As upgate_task, the tile is a whole m-block of BMB rows or the rows row0 ..
+// row0 + TG::BM of it.
+template <typename T, int BMB, int BN, bool SLOT_NT, typename TG, typename BeforeRows>
 __device__ __forceinline__ void down_task(const ForwardParams& p, const TaskSpace& ts, int64_t t,
-                                          TG& g, char* smem, int* s_tok, int* s_f, float* s_w,
-                                          BeforeRows before_rows) {
+                                          int row0, TG& g, char* smem, int* s_tok, int* s_f,
+                                          float* s_w, BeforeRows before_rows) {
   static_assert(TG::BN == BN, "tile width");
+  constexpr int BM = TG::BM;            // tile rows
   constexpr int NT = kDownStrips * BN;  // columns per task
   {
     const bool shared = t >= ts.t_r;
@@ -646,7 +730,7 @@ __device__ __forceinline__ void down_task(const ForwardParams& p, const TaskSpac
     if (threadIdx.x < BM) {
       const int r = threadIdx.x;
       if (!shared) {
-        const int f = p.sorted_ids[b * BM + r];
+        const int f = p.sorted_ids[b * BMB + row0 + r];
         if (f < p.F) {
           s_tok[r] = (int)(f / p.k);
           s_f[r] = f;
@@ -657,7 +741,7 @@ __device__ __forceinline__ void down_task(const ForwardParams& p, const TaskSpac
           s_w[r] = 0.f;
         }
       } else {
-        const int64_t s = b * BM + r;
+        const int64_t s = b * BMB + row0 + r;
         s_tok[r] = s < p.S ? (int)s : -1;
         s_f[r] = s_tok[r];
         s_w[r] = 1.f;
@@ -684,17 +768,19 @@ __device__ __forceinline__ void down_task(const ForwardParams& p, const TaskSpac
       bb[m] = wbytes - (uint32_t)(m * BN * sizeof(T));
       nc[m] = p.H - n0 - m * BN;
     }
-    // this m-block's BM rows of h (or hs), K-contiguous
+    // this m-block's BMB rows of h (or hs); the tile's row r is block row
+    // row0 + r
     const char* Ab = reinterpret_cast<const char*>(shared ? p.hs : p.h) +
-                     (size_t)b * BM * K * sizeof(T);
+                     (size_t)b * BMB * K * sizeof(T);
     if constexpr (is_direct<TG>()) {
       const bool hb = p.h_blocked;
-      g.setup(Ab, (uint32_t)(BM * K * sizeof(T)), [&](int r) -> uint32_t {
-        return s_tok[r] >= 0 ? (uint32_t)(hb ? r * 64 : r * K * sizeof(T)) : kOob;
-      }, Bm, bb, p.H, n0, nc, hb);
+      g.setup(Ab, (uint32_t)(BMB * K * sizeof(T)), [&](int r) -> uint32_t {
+        const int br = row0 + r;
+        return s_tok[r] >= 0 ? (uint32_t)(hb ? br * 64 : br * K * sizeof(T)) : kOob;
+      }, Bm, bb, p.H, n0, nc, hb ? BMB : 0);
     } else {
-      g.setup(Ab, (uint32_t)(BM * K * sizeof(T)), [&](int r) -> uint32_t {
-        return s_tok[r] >= 0 ? (uint32_t)(r * K * sizeof(T)) : kOob;
+      g.setup(Ab, (uint32_t)(BMB * K * sizeof(T)), [&](int r) -> uint32_t {
+        return s_tok[r] >= 0 ? (uint32_t)((row0 + r) * K * sizeof(T)) : kOob;
       }, Bm, bb, p.H, n0, nc);
     }
     run_mainloop(g, smem, K, [&](int r) { return s_tok[r] >= 0; });
@@ -741,13 +827,21 @@ __global__ __launch_bounds__((tile_threads<T, BM, kDownStrips, 1>()), 1) void do
   QuotaState qs = quota_init(p.E);
   TG g;
   for (;;) {
-    if (threadIdx.x == 0)
-      s_task = p.sched_quota ? claim_quota(p, ts, p.counters + kQuotaBase + kQuotaStride, qs)
-                             : claim_task(counters, ts.total, q, tried);
+    if (threadIdx.x == 0) {
+      if (p.sched_quota) {
+        const int64_t t = claim_quota(p, ts, p.counters + kQuotaBase + kQuotaStride, qs);
+        s_task = t < 0 ? -1 : t << 2;
+      } else {
+        // whole tiles only: split into halves, the down tasks measured no
+        // faster, and the half-tile code slowed the whole-tile path (prefill
+        // down +3 to +5%)
+        s_task = claim_task_split(counters, ts.total, wgs_per_xcd(), false, q, tried);
+      }
+    }
     __syncthreads();
-    const int64_t t = uniform64(s_task);
-    if (t < 0) break;
-    down_task<T, BM, BN, true>(p, ts, t, g, smem, s_tok, s_f, s_w, [](int64_t, bool) {});
+    const int64_t c = uniform64(s_task);
+    if (c < 0) break;
+    down_task<T, BM, BN, true>(p, ts, c >> 2, 0, g, smem, s_tok, s_f, s_w, [](int64_t, bool) {});
   }
 }
 
@@ -813,7 +907,7 @@ __global__ __launch_bounds__((tile_threads<bf16_t, BM, 2, 2>()), 1) void fused_k
     const int64_t t = uniform64(s_task);
     if (t < 0) break;
     if (t < tu.total) {
-      const int64_t rb = upgate_task<bf16_t, BM, BN>(p, tu, t, g, smem, s_tok);
+      const int64_t rb = upgate_task<bf16_t, BM, BN>(p, tu, t, 0, g, smem, s_tok);
       // Publish: each wave waits until its h stores have completed (vmcnt
       // 0: they are in this XCD's L2), then one device-scope release by
       // thread 0 writes the L2 back and the task is counted. A release fence
@@ -827,7 +921,7 @@ __global__ __launch_bounds__((tile_threads<bf16_t, BM, 2, 2>()), 1) void fused_k
       }
     } else {
       down_task<bf16_t, BM, BN, false>(
-          p, td, t - tu.total, g, smem, s_tok, s_f, s_w, [&](int64_t rb, bool shared) {
+          p, td, t - tu.total, 0, g, smem, s_tok, s_f, s_w, [&](int64_t rb, bool shared) {
             if (threadIdx.x == 0) wait_count(p.ready + rb, (int)(shared ? tu.nn_s : tu.nn_r));
           });
     }
@@ -966,7 +1060,7 @@ __device__ __forceinline__ void stream_setup(TG& g, const ForwardParams& p, cons
   g.setup(Ab, (uint32_t)(BM * K * sizeof(bf16_t)), [&](int r) -> uint32_t {
     return stream_row_valid(p, k, m, BM, r) ? (uint32_t)(hb ? r * 64 : r * K * sizeof(bf16_t))
                                             : kOob;
-  }, Bm, bb, H, n0, nc, hb);
+  }, Bm, bb, H, n0, nc, hb ? BM : 0);
   g.set_k(K);
 }
 
