@@ -159,6 +159,9 @@ static hipError_t launch_gate_direct(const GateParams& p, hipStream_t st) {
 // workgroup computes the scores of BMG tokens for all E <= NB * 128 experts
 // on the LDS-direct core, stages the fp32 score tile (bias added) in LDS,
 // writes it to G coalesced, and each wave ranks its tokens from LDS.
+// Largest k whose weights the fused gate computes in one pass per wave.
+constexpr int kTopkBatchK = 8;
+
 template <int BMG, int NB>
 __global__ __launch_bounds__(512, 1) void gate_topk_kernel(GateParams gp, TopkParams tp) {
   using TG = TileGemmDirect<BMG, NB, 8, 64, 120 * 1024>;
@@ -192,9 +195,29 @@ __global__ __launch_bounds__(512, 1) void gate_topk_kernel(GateParams gp, TopkPa
   for (int i = threadIdx.x; i < rows * E; i += 512) gp.G[(size_t)m0 * E + i] = tile[i];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  for (int r = wave; r < rows; r += 8) {
-    const int64_t s = m0 + r;
-    topk_one(tile + r * E, E, tp.k, tp.renormalize, tp.ids + s * tp.k, tp.w + s * tp.k, lane);
+  if (tp.renormalize && tp.k <= kTopkBatchK) {
+    // choices token by token, then the weights of all the wave's tokens in one
+    // pass (topk_weights_renorm)
+    constexpr int NT = BMG / 8;  // tokens per wave
+    __shared__ float s_sel[8][NT * kTopkBatchK];
+    __shared__ double s_e[8][NT * kTopkBatchK];
+    const int k = (int)tp.k;
+    int nt = 0;
+    for (int r = wave; r < rows; r += 8, ++nt) {
+      float my_sel, top;
+      int my_id;
+      topk_select(tile + r * E, (int)E, k, lane, my_sel, my_id, top);
+      if (lane < k) {
+        tp.ids[(m0 + r) * k + lane] = my_id;
+        s_sel[wave][nt * k + lane] = my_sel;
+      }
+    }
+    topk_weights_renorm(s_sel[wave], s_e[wave], nt, k, m0 + wave, 8, tp.w, lane);
+  } else {
+    for (int r = wave; r < rows; r += 8) {
+      const int64_t s = m0 + r;
+      topk_one(tile + r * E, E, tp.k, tp.renormalize, tp.ids + s * tp.k, tp.w + s * tp.k, lane);
+    }
   }
 }
 

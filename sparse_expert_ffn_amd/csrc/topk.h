@@ -52,12 +52,13 @@ __device__ __forceinline__ double readlane_f64(double x, int l) {
   return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
 }
 
-// One token: g = its E scores (global or LDS), ids / w = its k outputs
-// (k <= 64), NPL >= ceil(E / 64) scores per lane. Every lane of the wave
-// calls it.
+// The k choices of one token: g = its E scores (global or LDS), NPL >=
+// ceil(E / 64) scores per lane, k <= 64. Every lane of the wave calls it;
+// lane j < k gets the j-th choice's score and expert, every lane the top
+// score m0.
 template <int NPL, typename GPtr>
-__device__ __forceinline__ void topk_one_n(GPtr g, int E, int k, int renormalize, int32_t* ids,
-                                           float* w, int lane) {
+__device__ __forceinline__ void topk_select_n(GPtr g, int E, int k, int lane, float& my_sel,
+                                              int& my_id, float& m0) {
   float v[NPL];
   uint32_t live = 0;  // bit i: expert lane + 64 i exists and is not taken
 #pragma unroll
@@ -67,9 +68,9 @@ __device__ __forceinline__ void topk_one_n(GPtr g, int E, int k, int renormalize
     v[i] = (x != x) ? -INFINITY : x;
     if (e < E) live |= 1u << i;
   }
-  float my_sel = 0.f;  // lane j: score of the j-th choice
-  int my_id = 0;       // lane j: expert of the j-th choice
-  float m0 = 0.f;
+  my_sel = 0.f;  // lane j: score of the j-th choice
+  my_id = 0;     // lane j: expert of the j-th choice
+  m0 = 0.f;
   for (int j = 0; j < k; ++j) {
     float lm = -INFINITY;
 #pragma unroll
@@ -92,6 +93,17 @@ __device__ __forceinline__ void topk_one_n(GPtr g, int E, int k, int renormalize
     }
     if (j == 0) m0 = M;
   }
+}
+
+// One token: g = its E scores (global or LDS), ids / w = its k outputs
+// (k <= 64), NPL >= ceil(E / 64) scores per lane. Every lane of the wave
+// calls it.
+template <int NPL, typename GPtr>
+__device__ __forceinline__ void topk_one_n(GPtr g, int E, int k, int renormalize, int32_t* ids,
+                                           float* w, int lane) {
+  float my_sel, m0;
+  int my_id;
+  topk_select_n<NPL>(g, E, k, lane, my_sel, my_id, m0);
   const double m = (double)m0;
   if (renormalize) {
     // lane j < k computes exp(G_j - G_0); the denominator adds them in slot
@@ -118,6 +130,49 @@ __device__ __forceinline__ void topk_one_n(GPtr g, int E, int k, int renormalize
       ids[lane] = my_id;
       w[lane] = (float)(exp((double)my_sel - m) / den);
     }
+  }
+}
+
+// topk_select_n dispatched on the scores per lane (E <= 1024).
+template <typename GPtr>
+__device__ __forceinline__ void topk_select(GPtr g, int E, int k, int lane, float& my_sel,
+                                            int& my_id, float& m0) {
+  if (E <= 64)
+    topk_select_n<1>(g, E, k, lane, my_sel, my_id, m0);
+  else if (E <= 128)
+    topk_select_n<2>(g, E, k, lane, my_sel, my_id, m0);
+  else if (E <= 256)
+    topk_select_n<4>(g, E, k, lane, my_sel, my_id, m0);
+  else if (E <= 512)
+    topk_select_n<8>(g, E, k, lane, my_sel, my_id, m0);
+  else
+    topk_select_n<16>(g, E, k, lane, my_sel, my_id, m0);
+}
+
+// Renormalised router weights of nt tokens, token t being s0 + t * stride
+// (one wave): sel = their chosen scores, k per token in slot order, in LDS;
+// e = LDS room for nt * k doubles; w = the [S][k] weights. The same arithmetic as topk_one_n's renormalised weights
+// (exp(G_j - G_0) in double, the denominator added in slot order, the
+// quotient rounded once), but with the exponentials of all nt tokens spread
+// over the lanes instead of k lanes per token: the double exp is the
+// costly part, so one pass over nt * k lanes replaces nt passes.
+__device__ __forceinline__ void topk_weights_renorm(const float* sel, double* e, int nt, int k,
+                                                    int64_t s0, int64_t stride, float* w,
+                                                    int lane) {
+  const int n = nt * k;
+  for (int p = lane; p < n; p += 64) {
+    const int t = p / k;
+    e[p] = exp((double)sel[p] - (double)sel[t * k]);
+  }
+  // other lanes' exponentials are read below: wait for this wave's LDS
+  // writes (one wave, so no workgroup barrier)
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  __builtin_amdgcn_wave_barrier();
+  for (int p = lane; p < n; p += 64) {
+    const int t = p / k;
+    double den = 0.0;
+    for (int j = 0; j < k; ++j) den += e[t * k + j];
+    w[(s0 + t * stride) * k + (p - t * k)] = (float)(e[p] / den);
   }
 }
 
