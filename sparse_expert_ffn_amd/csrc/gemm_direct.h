@@ -12,8 +12,8 @@
 //    Zero rows, rows past K and columns past N use out-of-range offsets: the
 //    hardware writes zeros.
 //  - A in LDS: BM rows of 2*BK bytes, 16-byte chunk c of row r stored in slot
-//    c ^ key(r) (see aswz): the 16 rows one operand read touches land in 16
-//    different 16-byte bank windows.
+//    c ^ key(r) (see aswz), the key chosen by measurement so the fragment
+//    reads (ds_read_b128) are free of bank conflicts.
 //  - B in LDS: each matrix as [BK k-rows][BN columns], N-contiguous as in
 //    memory (256 bytes per row); its 32-byte column pairs are XOR-swizzled by
 //    g(k) = (k & 3) | ((k >> 3) & 1) << 2 so the 16 k-rows one transposed read
@@ -171,13 +171,18 @@ struct TileGemmDirect {
   int64_t K_;
 
   __device__ __forceinline__ static int bswz(int k) { return (k & 3) | (((k >> 3) & 1) << 2); }
-  // A chunk swizzle: the 16 rows of an operand read hit 16 different 16-byte
-  // bank windows (8 chunks per 128-byte row, or 4 per 64-byte row)
+  // A chunk swizzle (8 chunks per 128-byte row, or 4 per 64-byte row). Chosen
+  // by measurement, with an LDS probe of exactly the fragment-read pattern on
+  // 256 workgroups: these keys sustain 234 B/clk per CU; the keys that spread
+  // one read's 16 rows over 16 different 16-byte bank windows ((r & 7) ^
+  // ((r >> 3) & 1) and (r >> 2) & 3) ran at 128 B/clk, half of the LDS
+  // cycles stalled on bank conflicts (the hardware does not serve a read's
+  // 64 lanes as four groups of 16 consecutive lanes).
   __device__ __forceinline__ static int aswz(int r) {
     if constexpr (ACH == 8)
-      return (r & 7) ^ ((r >> 3) & 1);
+      return (r >> 1) & 7;
     else
-      return (r >> 2) & 3;
+      return ((r >> 2) & 1) << 1;
   }
 
   __device__ __forceinline__ void zero_acc() {
