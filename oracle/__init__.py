@@ -23,7 +23,7 @@ _PLANT_DIR = os.path.join(_HERE, "_build")
 
 # Deliberately wrong variants used only by the pin self-test.
 PLANTS = ("TIE_HIGH", "WEIGHT_NO_EXP", "CAP_OFF_BY_ONE", "ALIGN_REVERSED",
-          "SILU_ON_GATE", "DOWN_TRANSPOSED", "WEIGHT_SLOT0", "DROP_SHARED")
+          "SILU_ON_GATE", "DOWN_TRANSPOSED", "WEIGHT_SLOT0", "DROP_SHARED", "ROW_INDEX")
 
 F32 = 0
 BF16 = 1

@@ -243,7 +243,11 @@ void oracle_layer_rows(int64_t H, int64_t D, int64_t E, int64_t k, int64_t Ds, i
     double* y = O + (size_t)i * H;
     for (int64_t n = 0; n < H; ++n) y[n] = 0.0;
     for (int64_t j = 0; j < k; ++j) {
+#ifdef ORACLE_PLANT_ROW_INDEX
+      size_t f = (size_t)i * k + j;
+#else
       size_t f = (size_t)t * k + j;
+#endif
       if (kept && !kept[f]) continue;
       int64_t e = ids[f];
 #ifdef ORACLE_PLANT_WEIGHT_SLOT0

@@ -139,6 +139,38 @@ def check_logits_matmul(orc):
         assert np.array_equal(Gb, G + bias), "router bias must be an fp32 add to the scores"
 
 
+def check_router_bias(orc):
+    """The router bias is added to the fp32 scores before ranking. Two closed
+    forms of that reading: a bias equal for every expert shifts all scores
+    alike, so the choice and the renormalised weights stay those of the
+    softmax of the unbiased scores; a bias far above the score spread on one
+    expert puts that expert in every token's first slot, and the remaining
+    slots follow the unbiased ranking (stable argsort) of the other experts."""
+    A = _rand((64, 32), 1.0, wk.F32, [5, 0])
+    Wr = _rand((32, 16), 0.05, wk.F32, [5, 1])
+    G = orc.gate_logits(A, Wr)
+    k = 4
+    ids, w = orc.topk_softmax(G, k, 1)
+    # 0.25 is exact in fp32 and small next to the scores' ulp range: the
+    # shifted scores are exact, so the ranking is unchanged
+    Gc = orc.gate_logits(A, Wr, np.full(16, 0.25, dtype=np.float32))
+    assert np.array_equal(Gc, (G.astype(np.float64) + 0.25).astype(np.float32))
+    ids_c, w_c = orc.topk_softmax(Gc, k, 1)
+    assert np.array_equal(ids_c, ids), "an equal bias on every expert changes no choice"
+    sel = np.take_along_axis(G.astype(np.float64), ids, axis=1)
+    ref = torch.softmax(torch.from_numpy(sel), dim=1).numpy()
+    _close(w_c, ref, 1.2e-7, "renormalised weights under an equal bias")
+    hot = 11
+    b = np.zeros(16, dtype=np.float32)
+    b[hot] = 1000.0
+    ids_h, _ = orc.topk_softmax(orc.gate_logits(A, Wr, b), k, 1)
+    assert np.all(ids_h[:, 0] == hot), "a dominant bias puts its expert in slot 0"
+    rest = np.delete(G.astype(np.float64), hot, axis=1)
+    order = np.argsort(-rest, axis=1, kind="stable")[:, : k - 1]
+    order = order + (order >= hot)
+    assert np.array_equal(ids_h[:, 1:], order), "other slots follow the unbiased ranking"
+
+
 def check_topk_library(orc):
     rng = np.random.default_rng(3)
     for E, k in ((8, 2), (24, 5), (64, 8), (5, 5)):
@@ -307,6 +339,22 @@ def check_shared_only(orc):
     _close(O, ref.numpy(), 1e-12, "shared expert alone is a plain FFN with weight 1")
 
 
+def check_layer_rows_subset(orc):
+    """Rows of a listed token subset, in a shuffled order with repeats: row i
+    of the result is token tokens[i]'s output, with its own routing, capacity
+    flags and shared expert (dense brute force, and the full run's rows)."""
+    for dtype in (wk.F32, wk.BF16):
+        L = _tiny_layer(dtype, S=31, H=12, D=10, E=5, k=2, Ds=6, seed=14)
+        out = _layer(orc, L, 2, capacity=9)
+        assert out["kept"] is not None and out["kept"].sum() < 31 * 2
+        p = np.array([30, 3, 17, 3, 0, 22, 9], dtype=np.int64)
+        rows = orc.layer_rows(L["A"], L["W_up"], L["W_gate"], L["W_down"], out["ids"],
+                              out["w"], out["kept"], p, L["Ws_up"], L["Ws_gate"], L["Ws_down"])
+        ref = _dense_reference(L, out["ids"], out["w"], out["kept"])
+        _close(rows, ref[p], 1e-12, f"token subset rows vs dense brute force dtype={dtype}")
+        assert np.array_equal(rows, out["O"][p]), "token subset rows vs the full run"
+
+
 def check_weights_sum_one_layer(orc):
     """Identical experts: with weights summing to 1, O equals one expert's FFN."""
     L = _tiny_layer(wk.F32, S=12, H=8, D=6, E=4, k=3, seed=13)
@@ -323,4 +371,5 @@ CHECKS = [check_golden_layer, check_golden_align, check_golden_topk, check_logit
           check_topk_library, check_topk_invariants, check_align_bruteforce,
           check_capacity_mask, check_layer_dense, check_plain_ffn, check_down_scaling,
           check_expert_permutation, check_token_permutation, check_capacity_limits,
-          check_zero_expert, check_shared_only, check_weights_sum_one_layer]
+          check_zero_expert, check_shared_only, check_weights_sum_one_layer,
+          check_router_bias, check_layer_rows_subset]
