@@ -11,10 +11,15 @@ from sparse_expert_ffn_amd.layer import MoEBuffers, suggest_block_size
 
 DEV = "cuda:0"
 
-# Parity bar: fp32 max |g - o| / max(|o|, RMS(o)) <= 1e-4;
+# Parity bar: fp32 max |g - o| / max(|o|, RMS(o)) <= 1e-4 over every element,
+#               and the plain max |g - o| / |o| <= 1e-4 over the elements with
+#               |o| >= RMS(o) / 10 (below that the plain ratio measures the
+#               cancellation in o, not the kernels: an element 1e6 times
+#               smaller than its neighbours has no meaningful relative error);
 #             bf16 max |g - o| / RMS(o) <= 2e-2 (fp32 accumulation).
 TOL_F32 = 1e-4
 TOL_BF16 = 2e-2
+PLAIN_FLOOR = 0.1
 
 
 def dev(a, device=DEV):
@@ -47,6 +52,16 @@ def err_f32(g, o):
     return float(np.max(np.abs(g - o) / np.maximum(np.abs(o), r)))
 
 
+def err_f32_plain(g, o, floor=PLAIN_FLOOR):
+    """max |g - o| / |o| over the elements with |o| >= floor * RMS(o)."""
+    g = np.asarray(g, dtype=np.float64)
+    o = np.asarray(o, dtype=np.float64)
+    sel = np.abs(o) >= floor * rms(o)
+    if not np.any(sel):
+        return 0.0
+    return float(np.max(np.abs(g[sel] - o[sel]) / np.abs(o[sel])))
+
+
 def err_bf16(g, o):
     g = np.asarray(g, dtype=np.float64)
     o = np.asarray(o, dtype=np.float64)
@@ -59,7 +74,7 @@ def parity(wl, g, o):
     """(error, tolerance) of the parity bar for this workload's dtype. In bf16
     mode ``g`` is the fp32-accumulated output (written as fp32)."""
     if wl.dtype == wk.F32:
-        return err_f32(g, o), TOL_F32
+        return max(err_f32(g, o), err_f32_plain(g, o)), TOL_F32
     return err_bf16(g, o), TOL_BF16
 
 

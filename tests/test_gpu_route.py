@@ -107,3 +107,41 @@ def test_fused_gate_topk_consistent(orc, name, S):
     ids_o, w_o = orc.topk_softmax(G, wl.k, wl.renormalize)
     assert np.array_equal(buf.topk_ids.cpu().numpy(), ids_o)
     assert np.array_equal(buf.topk_weights.cpu().numpy().view(np.uint32), w_o.view(np.uint32))
+
+
+# Gate-score GEMM variants reached when the fused gate + top-k does not apply:
+# bf16 with E > 256 (E % 8 == 0: the LDS-direct gate GEMM, three row-tile
+# sizes by S), bf16 or fp32 with E % 8 != 0 (the register-staged GEMM with
+# ragged columns), fp32 with E % 8 == 0; each followed by the separate top-k
+# kernel. H = 200 leaves a K tail after three 64-wide stages.
+GEMM_CASES = [(wk.BF16, 600, 8, 1), (wk.BF16, 600, 8, 300), (wk.BF16, 600, 8, 1500),
+              (wk.BF16, 600, 8, 3300), (wk.BF16, 1000, 32, 77), (wk.BF16, 1020, 6, 150),
+              (wk.BF16, 12, 3, 300), (wk.BF16, 12, 3, 1), (wk.F32, 12, 3, 300),
+              (wk.F32, 5, 2, 77), (wk.F32, 64, 4, 200)]
+
+
+@pytest.mark.parametrize("dtype,E,k,S", GEMM_CASES)
+def test_gate_gemm_variants(orc, dtype, E, k, S):
+    H = 200
+    rng = np.random.default_rng([E, S, dtype])
+    A = rng.standard_normal((S, H)).astype(np.float32)
+    Wr = (rng.standard_normal((H, E)) / np.sqrt(H)).astype(np.float32)
+    bias = (rng.standard_normal(E) * 0.1).astype(np.float32)
+    if dtype == wk.BF16:
+        A, Wr = wk.f32_to_bf16_bits(A), wk.f32_to_bf16_bits(Wr)
+    G_o = orc.gate_logits(A, Wr, bias)
+    shape = moe.make_shape(S, H, 8, E, k, block_size=16, dtype=dtype)
+    ws_n = moe.moe_gate_workspace_bytes(shape)
+    ws = torch.empty(max(ws_n, 1), dtype=torch.uint8, device=DEV) if ws_n else None
+    G = torch.empty((S, E), dtype=torch.float32, device=DEV)
+    ids = torch.empty((S, k), dtype=torch.int32, device=DEV)
+    w = torch.empty((S, k), dtype=torch.float32, device=DEV)
+    moe.moe_gate_topk(shape, dev(A), dev(Wr), dev(bias), None, G, ids, w, ws)
+    torch.cuda.synchronize()
+    Gh = G.cpu().numpy()
+    err = float(np.max(np.abs(Gh.astype(np.float64) - G_o)) / rms(G_o))
+    assert err <= 1e-4, f"gate scores max err / RMS = {err:.3e}"
+    # routing of the GPU's own scores: the oracle's top-k of them, bit for bit
+    ids_o, w_o = orc.topk_softmax(Gh, k, 1)
+    assert np.array_equal(ids.cpu().numpy(), ids_o)
+    assert np.array_equal(w.cpu().numpy().view(np.uint32), w_o.view(np.uint32))
