@@ -51,6 +51,9 @@ def parse():
                     help="rotate the steps over this many copies of the expert weights (a "
                          "cold-cache figure when one copy of the touched weights fits the "
                          "256 MB MALL)")
+    ap.add_argument("--other", default="decode,prefill_skew",
+                    help="comma-separated workloads timed after the headline one with the "
+                         "same step loop (GPU timing only, in other_workloads); '' for none")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU work of the oracle baseline sample")
@@ -110,6 +113,47 @@ def copy_calibration():
     print(json.dumps({"copy_calibration_bytes": n, "copies": 3}))
 
 
+def host_info():
+    """Host CPU as this process sees it: logical CPUs, the ones it may run
+    on, and the model name."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except AttributeError:
+        usable = os.cpu_count()
+    return {"nproc": os.cpu_count(), "usable_cpus": usable, "cpu_model": model}
+
+
+def gpu_info(moe, torch):
+    """The GPU as the HIP runtime reports it."""
+    cus, mhz, name = moe.moe_device_query()
+    props = torch.cuda.get_device_properties(torch.cuda.current_device())
+    return {"name": name, "arch": getattr(props, "gcnArchName", None), "compute_units": cus,
+            "peak_clock_mhz": mhz, "hbm_gib": round(props.total_memory / 2 ** 30, 1)}
+
+
+def routing_stats(buf, wl):
+    """Histogram figures of one step's routing: rows per expert before and
+    after the capacity clip, empty experts, dropped assignments."""
+    ids = buf.topk_ids.cpu().numpy().reshape(-1)
+    routed = np.bincount(ids, minlength=wl.E)
+    kept = buf.expert_counts.cpu().numpy()
+    mean = wl.S * wl.k / wl.E
+    return {"assignments": int(wl.S * wl.k), "kept": int(kept.sum()),
+            "dropped": int(wl.S * wl.k - kept.sum()), "empty_experts": int((routed == 0).sum()),
+            "max_rows_per_expert": int(routed.max()), "mean_rows_per_expert": mean,
+            "max_over_mean": float(routed.max() / mean) if mean else None,
+            "max_kept_rows": int(kept.max()), "capacity": wl.capacity}
+
+
 def cpu_baseline(wl, target_s):
     """The oracle as it stands, on a bounded sample of the same workload
     (first S' tokens' worth: the same layer at S' tokens), whole layer."""
@@ -130,33 +174,20 @@ def cpu_baseline(wl, target_s):
     t0 = one(S0)
     S1 = int(min(wl.S, max(S0, S0 * target_s / max(t0, 1e-3))))
     t1 = one(S1) if S1 != S0 else t0
+    h = host_info()
     return {"value": S1 / t1, "unit": "tokens/s", "cores": orc.num_threads(), "kind": "oracle",
             "sample": f"{wl.name} layer at S={S1} tokens (same H, D, E, k, distributions; "
                       f"capacity recomputed for S), gate+top-k+capacity+experts+combine, "
-                      f"{t1:.1f} s"}
+                      f"{t1:.1f} s",
+            "nproc": h["nproc"], "usable_cpus": h["usable_cpus"], "cpu_model": h["cpu_model"]}
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              "(the multi-GPU expert-parallel path is not built)", file=sys.stderr)
-        sys.exit(2)
-    import torch
-    if args.copy_calibration:
-        copy_calibration()
-        return
-
-    import sparse_expert_ffn_amd as moe
+def setup_workload(wl, args, torch, moe, dev="cuda"):
+    """Resident device inputs and buffers of one workload; returns step()."""
     from sparse_expert_ffn_amd import workloads as wk
     from sparse_expert_ffn_amd.layer import MoEBuffers, suggest_block_size
 
-    moe.load_library()
-    wl = wk.WORKLOADS[args.workload]
-    if args.tokens > 0:
-        wl = wl.with_tokens(args.tokens)
     bm = args.block_size or suggest_block_size(wl.S, wl.k, wl.E, wl.capacity, wl.dtype)
-    dev = "cuda"
 
     def td(a):
         if a is None:
@@ -194,9 +225,7 @@ def main():
     buf = MoEBuffers(wl.S, wl.H, wl.D, wl.E, wl.k, wl.D_shared, wl.capacity, bm,
                      wl.renormalize, wl.dtype, sched_quota=args.sched == "quota",
                      fused_launch=args.launch == "one", device=dev)
-    one = args.launch == "one"
     stream = torch.cuda.current_stream()
-
     n_step = [0]
 
     def step():
@@ -204,11 +233,22 @@ def main():
         n_step[0] += 1
         buf.run(A_d, Wr_d, *w, router_bias=b_d, stream=stream)
 
-    for _ in range(args.warmup):
+    return step, buf, bm, stream, n_copies
+
+
+def measure(wl, args, steps, warmup, torch, moe, full=True):
+    """Time `steps` passes of the layer after `warmup` untimed ones; the
+    roofline kernel (up/gate) is timed by HIP events on its own stream inside
+    the timed region. Returns the record (the headline fields when full)."""
+    from sparse_expert_ffn_amd import workloads as wk
+    step, buf, bm, stream, n_copies = setup_workload(wl, args, torch, moe)
+    one = args.launch == "one"
+    for _ in range(warmup):
         step()
     torch.cuda.synchronize()
     counts = buf.expert_counts.cpu().numpy()
     cnt = layer_counts(wl, counts, bm)
+    routing = routing_stats(buf, wl)
 
     # HIP events around the up/gate kernel only (the roofline kernel), on the
     # stream it runs on: each bracketed kernel adds two marker packets, which
@@ -220,19 +260,19 @@ def main():
     torch.cuda.synchronize()
     w0 = time.perf_counter()
     ev0.record(stream)
-    for _ in range(args.steps):
+    for _ in range(steps):
         step()
     ev1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - w0
     moe.moe_profile_enable(False)
     stage_ms, n_calls = moe.moe_profile_collect(4)
-    ms = ev0.elapsed_time(ev1) / args.steps
+    ms = ev0.elapsed_time(ev1) / steps
     up_ms = stage_ms[1] / max(n_calls, 1)
     # setup, down and combine kernels, timed in a few extra steps after the
     # timed region
     moe.moe_profile_enable(True, stages=(0, 2, 3))
-    n_extra = min(args.steps, 10)
+    n_extra = min(steps, 10)
     for _ in range(n_extra):
         step()
     torch.cuda.synchronize()
@@ -242,13 +282,14 @@ def main():
     # per-step times (an event pair per step), for the median; after the timed
     # region, which holds no per-step markers
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(min(args.steps, 16))]
+           for _ in range(min(steps, 16))]
     for e0, e1 in evs:
         e0.record(stream)
         step()
         e1.record(stream)
     torch.cuda.synchronize()
     med_ms = float(np.median([e0.elapsed_time(e1) for e0, e1 in evs])) if evs else None
+    status = moe.forward_status(buf.forward_ws)
 
     peak = PEAK_BF16_TFLOPS if wl.dtype == wk.BF16 else PEAK_F32_TFLOPS
     # the roofline kernel: up/gate, or with one launch both expert GEMMs
@@ -273,36 +314,86 @@ def main():
                  "bytes_per_launch": k_bytes})
     layer_tflops = cnt["flops"] / (ms * 1e-3) / 1e12
     floor_s = max(cnt["flops"] / (peak * 1e12), cnt["bytes"] / (PEAK_HBM_GBS * 1e9))
+    layer_bound = "hbm" if cnt["bytes"] / (PEAK_HBM_GBS * 1e9) > cnt["flops"] / (peak * 1e12) \
+        else "mfma"
+    layer = {"tflops": layer_tflops, "mfma_frac": layer_tflops / peak,
+             "bound": layer_bound, "floor_ms": floor_s * 1e3,
+             "roofline_frac": floor_s / (ms * 1e-3),
+             "gbs": cnt["bytes"] / (ms * 1e-3) / 1e9,
+             "hbm_frac": cnt["bytes"] / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+             "kept": cnt["kept"],
+             "touched_experts": cnt["touched"], "down_ms": None if one else down_ms,
+             "down_tflops": None if one else cnt["flops_down"] / (down_ms * 1e-3) / 1e12,
+             "setup_ms": small_ms[0] / max(n_small, 1),
+             "combine_ms": small_ms[3] / max(n_small, 1),
+             "median_ms_per_step": med_ms, "wall_s": wall, "status_word": status}
+    config = {"workload": wl.name, "S": wl.S, "H": wl.H, "D": wl.D, "E": wl.E, "k": wl.k,
+              "D_shared": wl.D_shared, "capacity": wl.capacity, "block_size": bm,
+              "scheduler": args.sched, "launch": args.launch, "weight_copies": n_copies,
+              "parallelism": "single GPU"}
+    rec = {"ms_per_step": ms, "value": wl.S / (ms * 1e-3), "config": config, "roofline": roof,
+           "layer": layer, "routing": routing, "steps": steps, "warmup": warmup,
+           "dtype": "bf16" if wl.dtype == wk.BF16 else "f32"}
+    del buf
+    torch.cuda.empty_cache()
+    return rec
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the multi-GPU expert-parallel path is not built)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if args.copy_calibration:
+        copy_calibration()
+        return
+
+    import sparse_expert_ffn_amd as moe
+    from sparse_expert_ffn_amd import workloads as wk
+
+    moe.load_library()
+    wl = wk.WORKLOADS[args.workload]
+    if args.tokens > 0:
+        wl = wl.with_tokens(args.tokens)
+    head = measure(wl, args, args.steps, args.warmup, torch, moe)
+    others = {}
+    for name in [n for n in args.other.split(",") if n and n != wl.name]:
+        o = measure(wk.WORKLOADS[name], args, min(args.steps, 20), min(args.warmup, 10), torch,
+                    moe)
+        others[name] = {"ms_per_step": o["ms_per_step"], "tokens_per_s": o["value"],
+                        "steps": o["steps"], "warmup": o["warmup"], "config": o["config"],
+                        "roofline": {k: o["roofline"][k] for k in
+                                     ("bound", "achieved", "peak", "unit", "frac", "kernel",
+                                      "avg_launch_ms")},
+                        "layer": {k: o["layer"][k] for k in
+                                  ("bound", "floor_ms", "roofline_frac", "tflops", "mfma_frac",
+                                   "gbs", "hbm_frac", "down_ms", "combine_ms",
+                                   "median_ms_per_step", "status_word")},
+                        "routing": o["routing"]}
     out = {
         "metric": "MoE layer tokens/s + % bf16 MFMA peak (prefill) / % HBM BW (decode)",
-        "value": wl.S / (ms * 1e-3),
+        "value": head["value"],
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": ms,
+        "ms_per_step": head["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if wl.dtype == wk.BF16 else "f32",
+        "dtype": head["dtype"],
         "data": "synthetic (seeded PCG64 normals, pages' distributions)",
-        "config": {"workload": wl.name, "S": wl.S, "H": wl.H, "D": wl.D, "E": wl.E, "k": wl.k,
-                   "D_shared": wl.D_shared, "capacity": wl.capacity, "block_size": bm,
-                   "scheduler": args.sched, "launch": args.launch,
-                   "weight_copies": n_copies,
-                   "parallelism": "single GPU"},
-        "roofline": roof,
-        "layer": {"tflops": layer_tflops, "mfma_frac": layer_tflops / peak,
-                  "floor_ms": floor_s * 1e3, "roofline_frac": floor_s / (ms * 1e-3),
-                  "gbs": cnt["bytes"] / (ms * 1e-3) / 1e9,
-                  "hbm_frac": cnt["bytes"] / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
-                  "kept": cnt["kept"],
-                  "touched_experts": cnt["touched"], "down_ms": None if one else down_ms,
-                  "down_tflops": None if one else cnt["flops_down"] / (down_ms * 1e-3) / 1e12,
-                  "setup_ms": small_ms[0] / max(n_small, 1),
-                  "combine_ms": small_ms[3] / max(n_small, 1),
-                  "median_ms_per_step": med_ms, "wall_s": wall},
+        "config": head["config"],
+        "roofline": head["roofline"],
+        "layer": head["layer"],
+        "routing": head["routing"],
+        "gpu": gpu_info(moe, torch),
+        "host": host_info(),
     }
+    if others:
+        out["other_workloads"] = others
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
     print(json.dumps(out), flush=True)

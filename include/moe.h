@@ -116,6 +116,21 @@ typedef struct {
  * kernel as stage 1 and nothing as stage 2. */
 #define MOE_FUSED_LAUNCH 8
 
+/* The call's status word: an int32 at this byte offset of the moe_forward
+ * workspace. Every moe_forward call sets it to 0 before its GEMMs run; once
+ * the call's work has finished on the stream, a nonzero value reports a
+ * failure inside the kernels that the host could not see when it enqueued
+ * them (bits below). Read it after synchronising the stream; it stays as the
+ * last call left it until the next call on that workspace.
+ *   MOE_STATUS_READY_TIMEOUT: with MOE_FUSED_LAUNCH, a down task stopped
+ *     waiting for its m-block's SwiGLU rows (the wait is bounded at about
+ *     2.7 s of the GPU's constant-rate clock so that the kernel always ends;
+ *     it never runs that long unless the GPU is shared or preempted). The
+ *     task wrote NaN to the output rows it covers instead of computing them,
+ *     so O holds NaN there. The two-launch path never sets it. */
+#define MOE_FORWARD_STATUS_OFFSET 128
+#define MOE_STATUS_READY_TIMEOUT 1
+
 /*
  * Gate scores and softmax top-k routing.
  *
@@ -254,6 +269,31 @@ const char* moe_status_string(moe_status status);
  * number of calls recorded in *n_calls, and forgets them. Not thread-safe.
  */
 moe_status moe_profile_enable(int stage_mask);
+/*
+ * Per-task timing records of the persistent GEMM kernels (measurement aid;
+ * the Weave review, section 5.2, notes that external profilers perturb
+ * persistent kernels, so the kernels stamp themselves). Only libraries built
+ * with -DMOE_TRACE=1 record; others return MOE_ERR_UNSUPPORTED. After
+ * moe_trace_attach(buffer, bytes), every moe_forward call's up/gate and down
+ * kernels append one 48-byte record per task to `buffer` (device memory,
+ * 64-byte aligned, owned by the caller, which must keep it alive while
+ * calls run): uint32 kernel (1 up/gate, 2 down, 3 / 4 the one-launch
+ * kernel's up/gate / down tasks), uint32 workgroup, int64 task (claimed id
+ * << 2 | row-half part; -1: the workgroup found no task left), then four
+ * uint64 stamps of the GPU's 100 MHz constant clock: the claim's result, the
+ * K loop's start, its end, the epilogue's stores issued (for task -1 all four
+ * are its exit time). The buffer's first uint64 counts the records (records
+ * past the buffer's room are dropped but counted); records start at byte 64.
+ * The caller zeroes the buffer before the calls it wants recorded.
+ * moe_trace_attach(NULL, 0) stops recording. Not thread-safe.
+ */
+moe_status moe_trace_attach(void* buffer, size_t bytes);
+
+/* The current HIP device's compute-unit count, peak engine clock in kHz and
+ * marketing name (NUL-terminated, cut to name_bytes), as the runtime reports
+ * them; any output may be NULL. Measurement aid: benchmark records state the
+ * hardware they ran on. MOE_ERR_HIP when no device is usable. */
+moe_status moe_device_query(int* cu_count, int* max_clock_khz, char* name, size_t name_bytes);
 moe_status moe_profile_collect(float* stage_ms, int max_stages, int* n_calls);
 
 #ifdef __cplusplus

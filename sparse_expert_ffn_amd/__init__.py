@@ -18,7 +18,10 @@ __all__ = ["MOE_F32", "MOE_BF16", "MoeError", "moe_shape", "make_shape", "load_l
            "moe_gate_workspace_bytes", "moe_gate_topk", "moe_align_workspace_bytes",
            "moe_align_block_size",
            "moe_forward_workspace_bytes", "moe_forward", "moe_status_string",
-           "moe_profile_enable", "moe_profile_collect", "build", "LIB_PATH", "STATUS"]
+           "moe_profile_enable", "moe_profile_collect", "moe_device_query", "moe_trace_attach",
+           "forward_status",
+           "build",
+           "LIB_PATH", "STATUS", "MOE_FORWARD_STATUS_OFFSET", "MOE_STATUS_READY_TIMEOUT"]
 
 # SPARSE_EXPERT_FFN_LIB: load the library from another path (e.g. a build
 # with different compile-time tile settings)
@@ -31,6 +34,9 @@ MOE_OUTPUT_F32 = 1
 MOE_COMBINE_ATOMIC = 2
 MOE_SCHED_QUOTA = 4  # ablation baseline: static per-expert workgroup quota
 MOE_FUSED_LAUNCH = 8  # up/gate and down GEMMs in one persistent launch (bf16)
+# byte offset of the int32 status word in the moe_forward workspace, and its bits
+MOE_FORWARD_STATUS_OFFSET = 128
+MOE_STATUS_READY_TIMEOUT = 1
 
 STATUS = {0: "MOE_OK", 1: "MOE_ERR_INVALID_ARGUMENT", 2: "MOE_ERR_UNSUPPORTED",
           3: "MOE_ERR_WORKSPACE_TOO_SMALL", 4: "MOE_ERR_HIP"}
@@ -39,7 +45,7 @@ STATUS = {0: "MOE_OK", 1: "MOE_ERR_INVALID_ARGUMENT", 2: "MOE_ERR_UNSUPPORTED",
 EXPORTS = ("moe_gate_workspace_bytes", "moe_gate_topk", "moe_align_workspace_bytes",
            "moe_align_block_size",
            "moe_forward_workspace_bytes", "moe_forward", "moe_status_string",
-           "moe_profile_enable", "moe_profile_collect")
+           "moe_profile_enable", "moe_profile_collect", "moe_device_query", "moe_trace_attach")
 
 
 class MoeError(RuntimeError):
@@ -72,12 +78,13 @@ def make_shape(S, H, D, E, k, D_shared=0, capacity=0, block_size=128, renormaliz
 _LIB = None
 
 
-def build(verbose: bool = False) -> str:
-    """Compile libmoe.so for gfx950 in-tree (hipcc)."""
+def build(verbose: bool = False) -> list:
+    """Compile libmoe.so and its timing-record variant libmoe_trace.so for
+    gfx950 in-tree (hipcc)."""
     from . import buildlib as _b
     global _LIB
     _LIB = None
-    return _b.build(verbose=verbose)
+    return _b.build_all(verbose=verbose)
 
 
 def load_library(path: str | None = None) -> ctypes.CDLL:
@@ -105,8 +112,11 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.moe_profile_enable.argtypes = [ctypes.c_int]
     lib.moe_profile_collect.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_int,
                                         ctypes.POINTER(ctypes.c_int)]
+    lib.moe_device_query.argtypes = [ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_int),
+                                     ctypes.c_char_p, sz]
+    lib.moe_trace_attach.argtypes = [vp, sz]
     for name in ("moe_gate_topk", "moe_align_block_size", "moe_forward", "moe_profile_enable",
-                 "moe_profile_collect"):
+                 "moe_profile_collect", "moe_device_query", "moe_trace_attach"):
         getattr(lib, name).restype = ctypes.c_int
     del i64
     if path is None:
@@ -221,3 +231,33 @@ def moe_profile_collect(n_stages: int = 4):
     _check("moe_profile_collect", load_library().moe_profile_collect(buf, n_stages,
                                                                      ctypes.byref(n)))
     return [float(x) for x in buf], int(n.value)
+
+
+def forward_status(workspace) -> int:
+    """The status word moe_forward left in ``workspace`` (a device uint8
+    tensor; read after the stream has finished the call): 0, or
+    MOE_STATUS_* bits."""
+    w = workspace[MOE_FORWARD_STATUS_OFFSET:MOE_FORWARD_STATUS_OFFSET + 4]
+    return int(w.cpu().view(dtype=__import__("torch").int32).item())
+
+
+def moe_device_query():
+    """(compute units, peak engine clock in MHz, device name) of the current
+    HIP device, as the runtime reports them."""
+    cus = ctypes.c_int(0)
+    khz = ctypes.c_int(0)
+    name = ctypes.create_string_buffer(256)
+    _check("moe_device_query", load_library().moe_device_query(
+        ctypes.byref(cus), ctypes.byref(khz), name, 256))
+    return int(cus.value), khz.value / 1000.0, name.value.decode(errors="replace")
+
+
+def moe_trace_attach(buffer, check=True) -> int:
+    """Record per-task timing into ``buffer`` (a 64-byte aligned device uint8
+    tensor; None stops). MOE_ERR_UNSUPPORTED unless the loaded library was
+    built with MOE_TRACE (``buildlib.build_trace()``)."""
+    a, n = (None, 0) if buffer is None else _ws(buffer)
+    code = load_library().moe_trace_attach(a, n)
+    if check:
+        _check("moe_trace_attach", code)
+    return code

@@ -9,6 +9,9 @@ import sys
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 LIB = os.path.join(PKG, "libmoe.so")  # the build() target (not SPARSE_EXPERT_FFN_LIB)
+# the same library with per-task timing records in the persistent kernels
+TRACE_LIB = os.path.join(PKG, "libmoe_trace.so")
+TRACE_FLAGS = ["-DMOE_TRACE=1"]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [
@@ -69,5 +72,17 @@ def build(verbose: bool = False, extra: list[str] | None = None, out: str = LIB)
     return out
 
 
+def build_trace(verbose: bool = False) -> str:
+    return build(verbose=verbose, extra=TRACE_FLAGS, out=TRACE_LIB)
+
+
+def build_all(verbose: bool = False) -> list[str]:
+    """The library and its timing-record variant, compiled side by side."""
+    from concurrent.futures import ThreadPoolExecutor
+    with ThreadPoolExecutor(2) as ex:
+        futs = [ex.submit(build, verbose), ex.submit(build_trace, verbose)]
+        return [f.result() for f in futs]
+
+
 if __name__ == "__main__":
-    print(build(verbose=True))
+    print(build_all(verbose=True))

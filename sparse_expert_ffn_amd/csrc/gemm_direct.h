@@ -122,8 +122,12 @@ __device__ __forceinline__ void wait_vmcnt() {
 
 // B_STREAM: the B operand (the weights) is read once per call, no other task
 // reuses it from the caches; its loads carry the non-temporal hint.
+// VALU_SGPR: every LDS-direct load takes the wait-state form of dma16 (for
+// kernels whose SGPR pressure makes the compiler restore the buffer
+// descriptors from VGPR lanes next to the loads; the asm hazard test finds
+// the sites).
 template <int BM_, int NB_, int NW_ = 8, int BK_ = 64, int LDS_BUDGET = 144 * 1024,
-          bool B_STREAM = false>
+          bool B_STREAM = false, bool VALU_SGPR = false>
 struct TileGemmDirect {
   static constexpr bool DIRECT = true;  // the LDS-direct core (vs gemm_tile.h)
   static constexpr int BM = BM_, BN = 128, NB = NB_;
@@ -244,7 +248,7 @@ struct TileGemmDirect {
   // SGPR_FROM_VALU: the caller cannot rule out that the compiler restores the
   // buffer descriptors from VGPR lanes right before (see dma16).
   static constexpr int NPIECE = A_PW + B_PW;
-  template <bool SGPR_FROM_VALU = false>
+  template <bool SGPR_FROM_VALU = VALU_SGPR>
   __device__ __forceinline__ void issue_piece(char* base, int kt, int idx) {
     // wave-uniform (scalar) so the buffer resources stay in SGPRs
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -274,7 +278,7 @@ struct TileGemmDirect {
   }
 
   // All LDS-direct loads of K stage kt into the stage buffer `base`.
-  template <bool SGPR_FROM_VALU = false>
+  template <bool SGPR_FROM_VALU = VALU_SGPR>
   __device__ __forceinline__ void issue_stage(char* base, int kt) {
 #pragma unroll
     for (int i = 0; i < NPIECE; ++i) issue_piece<SGPR_FROM_VALU>(base, kt, i);

@@ -121,6 +121,10 @@ struct ProfileRecord {
   hipEvent_t start, stop;
 };
 
+// per-task timing records (libraries built with MOE_TRACE)
+void* g_trace = nullptr;
+int64_t g_trace_cap = 0;
+
 std::mutex g_prof_mu;
 bool g_prof_on = false;
 unsigned g_prof_mask = 0;  // bit s: time stage s
@@ -154,6 +158,112 @@ hipError_t run_stage(int stage, hipStream_t st, F launch) {
   if (e != hipSuccess) return e;
   g_prof.push_back(r);
   return hipSuccess;
+}
+
+// moe_forward on a given workspace; timing = false records no stage events.
+moe_status forward_impl(const moe_shape* shape, const void* A, const void* W_up,
+                        const void* W_gate, const void* W_down, const void* Ws_up,
+                        const void* Ws_gate, const void* Ws_down, const float* topk_weights,
+                        const int32_t* sorted_ids, const int32_t* expert_ids,
+                        const int32_t* num_tokens_post_padded, void* O, void* workspace,
+                        size_t workspace_bytes, void* stream, bool timing) {
+  moe_status st = check_forward_dims(shape);
+  if (st != MOE_OK) return st;
+  const bool has_shared = shape->D_shared > 0;
+  if ((Ws_up != nullptr) != has_shared || (Ws_gate != nullptr) != has_shared ||
+      (Ws_down != nullptr) != has_shared)
+    return MOE_ERR_INVALID_ARGUMENT;
+  if (shape->S == 0) return MOE_OK;
+  if (A == nullptr || W_up == nullptr || W_gate == nullptr || W_down == nullptr ||
+      topk_weights == nullptr || sorted_ids == nullptr || expert_ids == nullptr ||
+      num_tokens_post_padded == nullptr || O == nullptr || workspace == nullptr)
+    return MOE_ERR_INVALID_ARGUMENT;
+  const void* vec_ptrs[] = {A, W_up, W_gate, W_down, O, workspace};
+  for (const void* q : vec_ptrs)
+    if (!aligned16(q)) return MOE_ERR_UNSUPPORTED;
+  if (has_shared && (!aligned16(Ws_up) || !aligned16(Ws_gate) || !aligned16(Ws_down)))
+    return MOE_ERR_UNSUPPORTED;
+  const ForwardLayout L = forward_layout(shape);
+  if (workspace_bytes < L.total) return MOE_ERR_WORKSPACE_TOO_SMALL;
+
+  char* ws = static_cast<char*>(workspace);
+  ForwardParams p;
+  p.A = A;
+  p.Wu = W_up;
+  p.Wg = W_gate;
+  p.Wd = W_down;
+  p.Wsu = Ws_up;
+  p.Wsg = Ws_gate;
+  p.Wsd = Ws_down;
+  p.topk_w = topk_weights;
+  p.sorted_ids = sorted_ids;
+  p.expert_ids = expert_ids;
+  p.ntpp = num_tokens_post_padded;
+  p.O = O;
+  p.atomic_combine = atomic_combine(shape) ? 1 : 0;
+  p.out_bf16 = out_bf16(shape) ? 1 : 0;
+  p.sched_quota = (shape->flags & MOE_SCHED_QUOTA) ? 1 : 0;
+  p.Oacc = (p.atomic_combine && p.out_bf16) ? reinterpret_cast<float*>(ws + L.oacc)
+                                            : reinterpret_cast<float*>(O);
+  p.Y = reinterpret_cast<float*>(ws + L.y);
+  p.Ys = reinterpret_cast<float*>(ws + L.ys);
+  p.kept = reinterpret_cast<uint8_t*>(ws + L.kept);
+  p.h = ws + L.h;
+  p.hs = ws + L.hs;
+  p.counters = reinterpret_cast<int*>(ws + L.counters);
+  p.ready = reinterpret_cast<int*>(ws + L.ready);
+  p.n_ready = L.n_ready;
+  p.fused = (shape->flags & MOE_FUSED_LAUNCH) ? 1 : 0;
+  // Slot rows far larger than the 256 MB MALL (DeepSeek-V3 sizes: 0.94 GB)
+  // go to HBM and come back from it anyway: the down kernel stores them and
+  // the combine loads them with the non-temporal hint (measured: down -3%,
+  // combine -15% there). Rows about the MALL's size (prefill, 0.27 GB) are
+  // partly served from it, and the hint measured 8% slower for both.
+  const double slot_bytes =
+      (double)(shape->S * shape->k + (shape->D_shared > 0 ? shape->S : 0)) * shape->H * 4.0;
+  p.slots_nt = (!atomic_combine(shape) && slot_bytes > 512.0 * (1 << 20)) ? 1 : 0;
+  p.S = shape->S;
+  p.H = shape->H;
+  p.D = shape->D;
+  p.E = shape->E;
+  p.k = shape->k;
+  p.Ds = shape->D_shared;
+  p.F = shape->S * shape->k;
+  p.grid = 0;
+  p.trace = g_trace;
+  p.trace_cap = g_trace_cap;
+  // bf16 h in 32-column slabs per block (the down kernel's K stages then read
+  // one contiguous block each); the fp32 path and other widths stay row-major
+  p.h_blocked = (shape->dtype == MOE_BF16 && p.D % 32 == 0 && p.Ds % 32 == 0) ? 1 : 0;
+  const int dt = shape->dtype;
+  const int BM = shape->block_size;
+  hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+  if (timing && g_prof_on) {
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    ++g_prof_calls;
+  }
+  auto run_stage = [&](int stage, hipStream_t st, auto launch) {
+    return timing ? ::run_stage(stage, st, launch) : launch();
+  };
+  if (run_stage(0, hs, [&] { return launch_forward_setup(p, hs); }) != hipSuccess)
+    return MOE_ERR_HIP;
+  if (p.fused) {
+    if (run_stage(1, hs, [&] { return launch_forward_fused(p, BM, hs); }) != hipSuccess)
+      return MOE_ERR_HIP;
+  } else {
+    if (run_stage(1, hs, [&] { return launch_forward_upgate(p, dt, BM, hs); }) != hipSuccess)
+      return MOE_ERR_HIP;
+    if (run_stage(2, hs, [&] { return launch_forward_down(p, dt, BM, hs); }) != hipSuccess)
+      return MOE_ERR_HIP;
+  }
+  if (p.atomic_combine) {
+    if (p.out_bf16 &&
+        run_stage(3, hs, [&] { return launch_forward_finalize(p, hs); }) != hipSuccess)
+      return MOE_ERR_HIP;
+  } else if (run_stage(3, hs, [&] { return launch_forward_combine(p, hs); }) != hipSuccess) {
+    return MOE_ERR_HIP;
+  }
+  return MOE_OK;
 }
 
 }  // namespace
@@ -268,96 +378,42 @@ moe_status moe_forward(const moe_shape* shape, const void* A, const void* W_up,
                        const int32_t* sorted_ids, const int32_t* expert_ids,
                        const int32_t* num_tokens_post_padded, void* O, void* workspace,
                        size_t workspace_bytes, void* stream) {
-  moe_status st = check_forward_dims(shape);
-  if (st != MOE_OK) return st;
-  const bool has_shared = shape->D_shared > 0;
-  if ((Ws_up != nullptr) != has_shared || (Ws_gate != nullptr) != has_shared ||
-      (Ws_down != nullptr) != has_shared)
-    return MOE_ERR_INVALID_ARGUMENT;
-  if (shape->S == 0) return MOE_OK;
-  if (A == nullptr || W_up == nullptr || W_gate == nullptr || W_down == nullptr ||
-      topk_weights == nullptr || sorted_ids == nullptr || expert_ids == nullptr ||
-      num_tokens_post_padded == nullptr || O == nullptr || workspace == nullptr)
-    return MOE_ERR_INVALID_ARGUMENT;
-  const void* vec_ptrs[] = {A, W_up, W_gate, W_down, O, workspace};
-  for (const void* q : vec_ptrs)
-    if (!aligned16(q)) return MOE_ERR_UNSUPPORTED;
-  if (has_shared && (!aligned16(Ws_up) || !aligned16(Ws_gate) || !aligned16(Ws_down)))
-    return MOE_ERR_UNSUPPORTED;
-  const ForwardLayout L = forward_layout(shape);
-  if (workspace_bytes < L.total) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  return forward_impl(shape, A, W_up, W_gate, W_down, Ws_up, Ws_gate, Ws_down, topk_weights,
+                      sorted_ids, expert_ids, num_tokens_post_padded, O, workspace,
+                      workspace_bytes, stream, true);
+}
 
-  char* ws = static_cast<char*>(workspace);
-  ForwardParams p;
-  p.A = A;
-  p.Wu = W_up;
-  p.Wg = W_gate;
-  p.Wd = W_down;
-  p.Wsu = Ws_up;
-  p.Wsg = Ws_gate;
-  p.Wsd = Ws_down;
-  p.topk_w = topk_weights;
-  p.sorted_ids = sorted_ids;
-  p.expert_ids = expert_ids;
-  p.ntpp = num_tokens_post_padded;
-  p.O = O;
-  p.atomic_combine = atomic_combine(shape) ? 1 : 0;
-  p.out_bf16 = out_bf16(shape) ? 1 : 0;
-  p.sched_quota = (shape->flags & MOE_SCHED_QUOTA) ? 1 : 0;
-  p.Oacc = (p.atomic_combine && p.out_bf16) ? reinterpret_cast<float*>(ws + L.oacc)
-                                            : reinterpret_cast<float*>(O);
-  p.Y = reinterpret_cast<float*>(ws + L.y);
-  p.Ys = reinterpret_cast<float*>(ws + L.ys);
-  p.kept = reinterpret_cast<uint8_t*>(ws + L.kept);
-  p.h = ws + L.h;
-  p.hs = ws + L.hs;
-  p.counters = reinterpret_cast<int*>(ws + L.counters);
-  p.ready = reinterpret_cast<int*>(ws + L.ready);
-  p.n_ready = L.n_ready;
-  p.fused = (shape->flags & MOE_FUSED_LAUNCH) ? 1 : 0;
-  // Slot rows far larger than the 256 MB MALL (DeepSeek-V3 sizes: 0.94 GB)
-  // go to HBM and come back from it anyway: the down kernel stores them and
-  // the combine loads them with the non-temporal hint (measured: down -3%,
-  // combine -15% there). Rows about the MALL's size (prefill, 0.27 GB) are
-  // partly served from it, and the hint measured 8% slower for both.
-  const double slot_bytes =
-      (double)(shape->S * shape->k + (shape->D_shared > 0 ? shape->S : 0)) * shape->H * 4.0;
-  p.slots_nt = (!atomic_combine(shape) && slot_bytes > 512.0 * (1 << 20)) ? 1 : 0;
-  p.S = shape->S;
-  p.H = shape->H;
-  p.D = shape->D;
-  p.E = shape->E;
-  p.k = shape->k;
-  p.Ds = shape->D_shared;
-  p.F = shape->S * shape->k;
-  p.grid = 0;
-  // bf16 h in 32-column slabs per block (the down kernel's K stages then read
-  // one contiguous block each); the fp32 path and other widths stay row-major
-  p.h_blocked = (shape->dtype == MOE_BF16 && p.D % 32 == 0 && p.Ds % 32 == 0) ? 1 : 0;
-  const int dt = shape->dtype;
-  const int BM = shape->block_size;
-  hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
-  if (g_prof_on) {
-    std::lock_guard<std::mutex> lk(g_prof_mu);
-    ++g_prof_calls;
+moe_status moe_trace_attach(void* buffer, size_t bytes) {
+  if (!MOE_TRACE) return MOE_ERR_UNSUPPORTED;
+  if (buffer == nullptr) {
+    g_trace = nullptr;
+    g_trace_cap = 0;
+    return MOE_OK;
   }
-  if (run_stage(0, hs, [&] { return launch_forward_setup(p, hs); }) != hipSuccess)
+  if (bytes < (size_t)kTraceHeaderBytes || (reinterpret_cast<uintptr_t>(buffer) & 63) != 0)
+    return MOE_ERR_INVALID_ARGUMENT;
+  g_trace = buffer;
+  g_trace_cap = (int64_t)((bytes - kTraceHeaderBytes) / kTraceRecBytes);
+  return MOE_OK;
+}
+
+moe_status moe_device_query(int* cu_count, int* max_clock_khz, char* name, size_t name_bytes) {
+  if (name != nullptr && name_bytes == 0) return MOE_ERR_INVALID_ARGUMENT;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return MOE_ERR_HIP;
+  if (cu_count != nullptr &&
+      hipDeviceGetAttribute(cu_count, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
     return MOE_ERR_HIP;
-  if (p.fused) {
-    if (run_stage(1, hs, [&] { return launch_forward_fused(p, BM, hs); }) != hipSuccess)
-      return MOE_ERR_HIP;
-  } else {
-    if (run_stage(1, hs, [&] { return launch_forward_upgate(p, dt, BM, hs); }) != hipSuccess)
-      return MOE_ERR_HIP;
-    if (run_stage(2, hs, [&] { return launch_forward_down(p, dt, BM, hs); }) != hipSuccess)
-      return MOE_ERR_HIP;
-  }
-  if (p.atomic_combine) {
-    if (p.out_bf16 &&
-        run_stage(3, hs, [&] { return launch_forward_finalize(p, hs); }) != hipSuccess)
-      return MOE_ERR_HIP;
-  } else if (run_stage(3, hs, [&] { return launch_forward_combine(p, hs); }) != hipSuccess) {
+  if (max_clock_khz != nullptr &&
+      hipDeviceGetAttribute(max_clock_khz, hipDeviceAttributeClockRate, dev) != hipSuccess)
     return MOE_ERR_HIP;
+  if (name != nullptr) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return MOE_ERR_HIP;
+    size_t i = 0;
+    for (; i + 1 < name_bytes && i < sizeof(prop.name) && prop.name[i] != 0; ++i)
+      name[i] = prop.name[i];
+    name[i] = 0;
   }
   return MOE_OK;
 }

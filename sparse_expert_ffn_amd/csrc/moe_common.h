@@ -19,6 +19,11 @@ constexpr int kXcds = 8;          // MI355X: 8 XCDs, workgroups dispatched round
 constexpr int kQuotaBase = 64;
 constexpr int kQuotaStride = 1024 + 16;
 constexpr int kCounterInts = kQuotaBase + 2 * kQuotaStride;
+// The call's status word, an int inside the counter block (so cleared by
+// every call's setup kernel) at the byte offset the public header names
+// (MOE_FORWARD_STATUS_OFFSET); bits as MOE_STATUS_* there.
+constexpr int kStatusWord = 32;
+constexpr int kStatusReadyTimeout = 1;
 
 __device__ __forceinline__ float bf16_to_f32(bf16_t x) {
   return __uint_as_float(((uint32_t)x) << 16);
@@ -117,7 +122,30 @@ struct ForwardParams {
   int fused;              // 1: up/gate and down in one launch (bf16)
   int slots_nt;           // 1: the slot rows Y / Ys are written and read with the
                           // non-temporal hint (they far exceed the MALL)
+  void* trace;            // per-task timing records (libraries built with MOE_TRACE), or null
+  int64_t trace_cap;      // records that fit the trace buffer
 };
+
+// Per-task timing records of the persistent GEMM kernels (compile with
+// -DMOE_TRACE=1). The trace buffer starts with a 64-byte header whose first
+// uint64 counts the records written (an atomic cursor); records of
+// kTraceRecBytes follow. Times are the GPU's constant 100 MHz clock.
+#ifndef MOE_TRACE
+#define MOE_TRACE 0
+#endif
+struct TraceRec {
+  uint32_t kernel;      // kTraceUpgate, kTraceDown, kTraceFusedUp, kTraceFusedDown
+  uint32_t workgroup;
+  int64_t task;         // claimed task id << 2 | part (part 1, 2: row halves); -1: the
+                        // workgroup found no task left (t_claim is then its exit time)
+  uint64_t t_claim;     // the claim's result arrived
+  uint64_t t_rows;      // row metadata in LDS, tile set up: the K loop starts
+  uint64_t t_kloop;     // the K loop ended: the epilogue starts
+  uint64_t t_end;       // the epilogue's stores were issued
+};
+constexpr int kTraceHeaderBytes = 64;
+constexpr int kTraceRecBytes = (int)sizeof(TraceRec);
+enum { kTraceUpgate = 1, kTraceDown = 2, kTraceFusedUp = 3, kTraceFusedDown = 4 };
 
 constexpr int kAlignSeg = 512;   // assignments per wave segment in the align kernels
 #ifndef MOE_ALIGN_SMALL_F

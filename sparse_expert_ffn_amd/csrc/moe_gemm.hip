@@ -72,17 +72,54 @@ __device__ __forceinline__ char* lds_ring() {
   return lds_ring_bytes();
 }
 
+// ------------------------------------------------------- per-task timing
+// With MOE_TRACE, thread 0 of a persistent kernel stamps each task's phases
+// into LDS and writes one TraceRec per task to the caller's trace buffer;
+// without it these are empty.
+__device__ __forceinline__ uint64_t* trace_stamps() {
+  __shared__ uint64_t s[4];
+  return s;
+}
+__device__ __forceinline__ void trace_stamp(int i) {
+  if constexpr (MOE_TRACE) {
+    if (threadIdx.x == 0) trace_stamps()[i] = wall_clock64();
+  }
+}
+__device__ __forceinline__ void trace_record(const ForwardParams& p, uint32_t kernel,
+                                             int64_t task) {
+  if constexpr (MOE_TRACE) {
+    if (threadIdx.x != 0 || p.trace == nullptr) return;
+    uint64_t* s = trace_stamps();
+    const uint64_t now = wall_clock64();
+    if (task < 0) s[0] = now;
+    unsigned long long* cur = reinterpret_cast<unsigned long long*>(p.trace);
+    const unsigned long long i = atomicAdd(cur, 1ull);
+    if ((int64_t)i >= p.trace_cap) return;
+    TraceRec* r = reinterpret_cast<TraceRec*>(reinterpret_cast<char*>(p.trace) +
+                                              kTraceHeaderBytes + i * kTraceRecBytes);
+    r->kernel = kernel;
+    r->workgroup = blockIdx.x;
+    r->task = task;
+    r->t_claim = s[0];
+    r->t_rows = task < 0 ? now : s[1];
+    r->t_kloop = task < 0 ? now : s[2];
+    r->t_end = now;
+  }
+}
+
 // Run the K loop of tile core TG. The direct core gets the static LDS ring
 // and skips each wave's row blocks past the last row for which valid(r)
 // holds; the register-staged core uses the dynamic buffer and computes every
 // row.
 template <typename TG, typename Valid>
 __device__ __forceinline__ void run_mainloop(TG& g, char* dyn, int64_t K, Valid valid) {
+  trace_stamp(1);
   if constexpr (is_direct<TG>()) {
     g.mainloop(lds_ring<TG>(), K, g.active_blocks(valid));
   } else {
     g.mainloop(dyn, K);
   }
+  trace_stamp(2);
 }
 
 constexpr int kGroupBlocks = 4;
@@ -704,18 +741,24 @@ __global__ __launch_bounds__((tile_threads<T, BM, 2, 2>()), 1) void upgate_kerne
         s_task = claim_task_split(p.counters, ts.total, wgs_per_xcd(), split, q, tried);
       }
     }
+    trace_stamp(0);
     __syncthreads();
     const int64_t c = uniform64(s_task);
-    if (c < 0) break;
+    if (c < 0) {
+      trace_record(p, kTraceUpgate, -1);
+      break;
+    }
     const int part = (int)(c & 3);
     if constexpr (kHalves) {
       if (part != 0) {
         TH gh;
         upgate_task<T, BM, BN>(p, ts, c >> 2, (part - 1) * (BM / 2), gh, smem, s_tok);
+        trace_record(p, kTraceUpgate, c);
         continue;
       }
     }
     upgate_task<T, BM, BN>(p, ts, c >> 2, 0, g, smem, s_tok);
+    trace_record(p, kTraceUpgate, c);
   }
 }
 
@@ -735,7 +778,10 @@ constexpr int kDownStrips = 2;
 // leaves it out, its SGPR budget has no room for it).
 // As upgate_task, the tile is a whole m-block of BMB rows or the rows row0 ..
 // row0 + TG::BM of it.
-template <typename T, int BMB, int BN, bool SLOT_NT, typename TG, typename BeforeRows>
+// WAITS: before_rows may give up a bounded wait for the m-block's SwiGLU
+// rows (it then returns true on thread 0): the task writes NaN to its output
+// rows instead of its product with whatever h held.
+template <typename T, int BMB, int BN, bool SLOT_NT, bool WAITS, typename TG, typename BeforeRows>
 __device__ __forceinline__ void down_task(const ForwardParams& p, const TaskSpace& ts, int64_t t,
                                           int row0, TG& g, char* smem, int* s_tok, int* s_f,
                                           float* s_w, BeforeRows before_rows) {
@@ -749,7 +795,9 @@ __device__ __forceinline__ void down_task(const ForwardParams& p, const TaskSpac
       decode_task(t, ts.nb_r, ts.nn_r, ts.gb_r, b, j);
     else
       decode_task(t - ts.t_r, ts.nb_s, ts.nn_s, kGroupBlocks, b, j);
-    before_rows(shared ? ts.nb_r + b : b, shared);
+    __shared__ int s_gave_up;
+    const bool gave_up = before_rows(shared ? ts.nb_r + b : b, shared);
+    if (WAITS && threadIdx.x == 0) s_gave_up = gave_up ? 1 : 0;
     if (threadIdx.x < BM) {
       const int r = threadIdx.x;
       if (!shared) {
@@ -808,6 +856,23 @@ __device__ __forceinline__ void down_task(const ForwardParams& p, const TaskSpac
     }
     run_mainloop(g, smem, K, [&](int r) { return s_tok[r] >= 0; });
     const int64_t H = p.H;
+    if (WAITS && s_gave_up) {
+      // the rows this task would have computed from unpublished h: NaN
+      const float nan = __builtin_nanf("");
+      if (p.atomic_combine)
+        g.for_each([&](int m, int row, int col, float) {
+          const int tok = s_tok[row];
+          const int64_t n = n0 + m * BN + col;
+          if (tok >= 0 && n < H) atomicAdd(p.Oacc + (size_t)tok * H + n, nan);
+        });
+      else
+        g.for_each([&](int m, int row, int col, float) {
+          const int f = s_f[row];
+          const int64_t n = n0 + m * BN + col;
+          if (f >= 0 && n < H) (shared ? p.Ys : p.Y)[(size_t)f * H + n] = nan;
+        });
+      return;
+    }
     if (p.atomic_combine) {
       float* O = p.Oacc;
       g.for_each([&](int m, int row, int col, float v) {
@@ -861,10 +926,16 @@ __global__ __launch_bounds__((tile_threads<T, BM, kDownStrips, 1>()), 1) void do
         s_task = claim_task_split(counters, ts.total, wgs_per_xcd(), false, q, tried);
       }
     }
+    trace_stamp(0);
     __syncthreads();
     const int64_t c = uniform64(s_task);
-    if (c < 0) break;
-    down_task<T, BM, BN, true>(p, ts, c >> 2, 0, g, smem, s_tok, s_f, s_w, [](int64_t, bool) {});
+    if (c < 0) {
+      trace_record(p, kTraceDown, -1);
+      break;
+    }
+    down_task<T, BM, BN, true, false>(p, ts, c >> 2, 0, g, smem, s_tok, s_f, s_w,
+                                      [](int64_t, bool) { return false; });
+    trace_record(p, kTraceDown, c);
   }
 }
 
@@ -880,26 +951,40 @@ __global__ __launch_bounds__((tile_threads<T, BM, kDownStrips, 1>()), 1) void do
 // No wait can deadlock: a workgroup waits only after every up/gate task has
 // been claimed, and a claimed up/gate task runs to its end without waiting
 // (its workgroup is running, whatever the other workgroups do). As a guard
-// the wait is still bounded by the constant-rate clock (kReadyWaitTicks);
-// past it the task reads whatever h holds, so the kernel always ends.
+// the wait is still bounded by the constant-rate clock (kReadyWaitTicks), so
+// the kernel always ends. A task that gives up sets the call's status word
+// (counters[kStatusWord], cleared by the setup kernel) and writes NaN to its
+// output rows: a wrong result is never silent.
 constexpr uint64_t kReadyWaitTicks = (uint64_t)1 << 28;  // about 2.7 s at 100 MHz
 
-__device__ __forceinline__ void wait_count(const int* ctr, int need) {
+// true when the count reached `need`, false when the wait gave up
+__device__ __forceinline__ bool wait_count(const int* ctr, int need) {
   const uint64_t t0 = wall_clock64();
+  bool ok = true;
   while (__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < need) {
     __builtin_amdgcn_s_sleep(2);
-    if (wall_clock64() - t0 > kReadyWaitTicks) break;
+    if (wall_clock64() - t0 > kReadyWaitTicks) {
+      ok = false;
+      break;
+    }
   }
   // one acquire after the spin (not per poll: each acquire invalidates caches)
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  return ok;
 }
+
+// The one-launch kernel's tile core: the persistent kernels' core in the
+// wait-state form of its loads (both GEMMs' task code in one kernel leaves the
+// compiler short of SGPRs; it restores descriptors from VGPR lanes right
+// before loads).
+template <int BM, bool BS>
+using FusedTile = TileGemmDirect<BM, 2, 8, stage_k<BM>(), 144 * 1024, BS, true>;
 
 template <int BM, int BN, bool BS>
 __global__ __launch_bounds__((tile_threads<bf16_t, BM, 2, 2>()), 1) void fused_kernel(
     ForwardParams p) {
-  using TG = typename TileSel<bf16_t, BM, 2, 2, BS>::type;
-  static_assert(std::is_same<TG, typename TileSel<bf16_t, BM, kDownStrips, 1, BS>::type>::value,
-                "one tile core (and one LDS ring) for both GEMMs");
+  using TG = FusedTile<BM, BS>;
+  static_assert(kDownStrips == 2, "one tile core (and one LDS ring) for both GEMMs");
   extern __shared__ __align__(16) char smem[];
   __shared__ int64_t s_task;
   __shared__ int s_tok[BM];
@@ -926,9 +1011,13 @@ __global__ __launch_bounds__((tile_threads<bf16_t, BM, 2, 2>()), 1) void fused_k
       }
       s_task = t;
     }
+    trace_stamp(0);
     __syncthreads();
     const int64_t t = uniform64(s_task);
-    if (t < 0) break;
+    if (t < 0) {
+      trace_record(p, kTraceFusedDown, -1);
+      break;
+    }
     if (t < tu.total) {
       const int64_t rb = upgate_task<bf16_t, BM, BN>(p, tu, t, 0, g, smem, s_tok);
       // Publish: each wave waits until its h stores have completed (vmcnt
@@ -942,11 +1031,17 @@ __global__ __launch_bounds__((tile_threads<bf16_t, BM, 2, 2>()), 1) void fused_k
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
         __hip_atomic_fetch_add(p.ready + rb, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
+      trace_record(p, kTraceFusedUp, t << 2);
     } else {
-      down_task<bf16_t, BM, BN, false>(
+      // (the task's t_rows stamp follows the wait for its m-block's h rows)
+      down_task<bf16_t, BM, BN, false, true>(
           p, td, t - tu.total, 0, g, smem, s_tok, s_f, s_w, [&](int64_t rb, bool shared) {
-            if (threadIdx.x == 0) wait_count(p.ready + rb, (int)(shared ? tu.nn_s : tu.nn_r));
+            if (threadIdx.x != 0) return false;
+            if (wait_count(p.ready + rb, (int)(shared ? tu.nn_s : tu.nn_r))) return false;
+            atomicOr(p.counters + kStatusWord, kStatusReadyTimeout);
+            return true;
           });
+      trace_record(p, kTraceFusedDown, (t - tu.total) << 2);
     }
   }
 }

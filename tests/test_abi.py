@@ -161,3 +161,27 @@ def test_forward_validation(lib):
     # readiness counters: one per routed and per shared m-block, more workspace
     assert (moe.moe_forward_workspace_bytes(shape(D_shared=64, fused_launch=True))
             >= moe.moe_forward_workspace_bytes(shape(D_shared=64)))
+
+
+def _header_macros():
+    text = open(HEADER).read()
+    return {m: int(v) for m, v in re.findall(r"#define\s+(MOE_\w+)\s+(\d+)", text)}
+
+
+def test_forward_status_word_layout(lib):
+    """The status word's offset and bits in include/moe.h match the binding and
+    the library's counter block (cleared by every call), and every valid
+    shape's workspace covers it."""
+    macros = _header_macros()
+    off = macros["MOE_FORWARD_STATUS_OFFSET"]
+    assert off == moe.MOE_FORWARD_STATUS_OFFSET and off % 4 == 0
+    assert macros["MOE_STATUS_READY_TIMEOUT"] == moe.MOE_STATUS_READY_TIMEOUT
+    common = open(os.path.join(ROOT, "sparse_expert_ffn_amd", "csrc", "moe_common.h")).read()
+    word = int(re.search(r"kStatusWord\s*=\s*(\d+)", common).group(1))
+    timeout = int(re.search(r"kStatusReadyTimeout\s*=\s*(\d+)", common).group(1))
+    queues = int(re.search(r"kQuotaBase\s*=\s*(\d+)", common).group(1))
+    assert word * 4 == off and timeout == moe.MOE_STATUS_READY_TIMEOUT
+    assert 16 <= word < queues, "inside the counter block, clear of the task queues"
+    for kw in (dict(), dict(S=1, E=1, k=1), dict(dtype=moe.MOE_F32, block_size=128),
+               dict(fused_launch=True), dict(atomic_combine=True)):
+        assert moe.moe_forward_workspace_bytes(shape(**kw)) >= off + 4, kw

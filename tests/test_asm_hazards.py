@@ -26,46 +26,97 @@ def _sgprs(text):
     return regs
 
 
+def _blocks(body: str):
+    """Basic blocks of one kernel's assembly: [(label or None, [instruction])]."""
+    blocks = [[None, []]]
+    for line in body.split("\n"):
+        t = line.strip()
+        if re.match(r"^[.\w$]+:", t):  # a label (.LBB0_1: and the like)
+            blocks.append([t.split(":")[0], []])
+            continue
+        t = t.split(";")[0].strip()
+        if not t or t.startswith("."):
+            continue
+        blocks[-1][1].append(t)
+        op = t.split()[0]
+        if op in ("s_branch", "s_endpgm", "s_setpc_b64") or op.startswith("s_cbranch"):
+            blocks.append([None, []])  # a branch ends its block
+    return blocks
+
+
+def _effect(t: str):
+    """(wait states the instruction takes, SGPRs it writes if it is a VALU op)."""
+    op = t.split()[0]
+    n = 1
+    mm = re.match(r"s_nop\s+(\d+)", t)
+    if mm:
+        n = int(mm.group(1)) + 1
+    written = set()
+    if op.startswith("v_"):
+        operands = t[len(op):].split(",")
+        if operands and re.match(r"\s*s(\[|\d)", operands[0]):
+            written = _sgprs(operands[0])
+    return n, written
+
+
+def _kernel_hazards(kernel: str, body: str):
+    blocks = _blocks(body)
+    index = {lab: i for i, (lab, _) in enumerate(blocks) if lab}
+    preds = {i: set() for i in range(len(blocks))}
+    for i, (_, ins) in enumerate(blocks):
+        for t in ins:
+            op = t.split()[0]
+            if op == "s_branch" or op.startswith("s_cbranch"):
+                target = t.split()[1]
+                if target in index:
+                    preds[index[target]].add(i)
+        last = ins[-1].split()[0] if ins else None
+        if last not in ("s_branch", "s_endpgm", "s_setpc_b64") and i + 1 < len(blocks):
+            preds[i + 1].add(i)
+
+    def fewest(bi, end, srd, budget, seen):
+        """Fewest wait states between a VALU write of srd and instruction
+        `end` of block bi over every path into it, or None if none within
+        budget."""
+        ins = blocks[bi][1]
+        w = 0
+        for k in range(end - 1, -1, -1):
+            n, written = _effect(ins[k])
+            if written & srd:
+                return w
+            w += n
+            if w >= budget:
+                return None
+        best = None
+        for p in preds[bi]:
+            if (p, budget - w) in seen:
+                continue
+            seen.add((p, budget - w))
+            r = fewest(p, len(blocks[p][1]), srd, budget - w, seen)
+            if r is not None and (best is None or r + w < best):
+                best = r + w
+        return best
+
+    found = []
+    for bi, (_, ins) in enumerate(blocks):
+        for k, t in enumerate(ins):
+            if t.startswith("buffer_load") and re.search(r"\slds\b", t) and "," in t:
+                r = fewest(bi, k, _sgprs(t.split(",")[1]), WAIT_STATES, set())
+                if r is not None and r < WAIT_STATES:
+                    found.append((kernel, r, t))
+    return found
+
+
 def lds_load_hazards(asm: str):
     """(kernel, wait states, load) for every LDS-direct buffer load reading an
-    SGPR written by a VALU op fewer than WAIT_STATES wait states before, in
-    straight-line code (history restarts at each label)."""
+    SGPR written by a VALU op fewer than WAIT_STATES wait states before, over
+    every path into the load: straight-line code, code that falls through
+    into a label, and branches (forward and loop back-edges) to it."""
     found = []
-    kernel = None
-    hist = []  # (wait states the instruction takes, SGPRs written by a VALU op)
-    for line in asm.split("\n"):
-        m = re.match(r"^(_Z\S+):", line)
-        if m:
-            kernel, hist = m.group(1), []
-            continue
-        t = line.strip()
-        if not t or t.startswith((";", ".")):
-            continue
-        if t.endswith(":"):
-            hist = []
-            continue
-        op = t.split()[0]
-        if op.startswith("buffer_load") and re.search(r"\slds\b", t):
-            srd = _sgprs(t.split(",")[1]) if "," in t else set()
-            waits = 0
-            for n, written in reversed(hist):
-                if written & srd:
-                    if waits < WAIT_STATES:
-                        found.append((kernel, waits, t))
-                    break
-                waits += n
-                if waits >= WAIT_STATES:
-                    break
-        n = 1
-        mm = re.match(r"s_nop\s+(\d+)", t)
-        if mm:
-            n = int(mm.group(1)) + 1
-        written = set()
-        if op.startswith("v_"):
-            operands = t[len(op):].split(",")
-            if operands and re.match(r"\s*s(\[|\d)", operands[0]):
-                written = _sgprs(operands[0])
-        hist.append((n, written))
+    heads = list(re.finditer(r"^(_Z\S+):", asm, re.M))
+    for n, m in enumerate(heads):
+        end = heads[n + 1].start() if n + 1 < len(heads) else len(asm)
+        found += _kernel_hazards(m.group(1), asm[m.end():end])
     return found
 
 
@@ -82,13 +133,62 @@ def test_scanner_catches_the_pattern():
     assert len(found) == 1 and found[0][1] == 0
 
 
+def test_scanner_follows_fall_through():
+    """A VALU write of an SGPR at the end of one block, then a label that the
+    code falls through into, then the load: still a hazard. After an
+    unconditional branch the label starts a new path."""
+    asm = """_Zk:
+\tv_readfirstlane_b32 s8, v3
+.LBB0_1:
+\tbuffer_load_dwordx4 v4, s[8:11], 0 offen lds
+\ts_branch .LBB0_3
+\tv_readfirstlane_b32 s12, v3
+\ts_branch .LBB0_1
+.LBB0_2:
+\tbuffer_load_dwordx4 v4, s[12:15], 0 offen lds
+.LBB0_3:
+\ts_endpgm
+"""
+    found = lds_load_hazards(asm)
+    assert len(found) == 1 and "s[8:11]" in found[0][2] and found[0][1] == 0
+
+
+def test_scanner_follows_branches_and_back_edges():
+    """A loop whose last instructions write the descriptor with a VALU op and
+    branch back to a load at the loop head; a forward branch from right after
+    such a write to a load."""
+    asm = """_Zk:
+\ts_mov_b32 s4, 0
+.LBB0_1:
+\tbuffer_load_dwordx4 v4, s[4:7], 0 offen lds
+\ts_nop 7
+\tv_readlane_b32 s5, v9, 1
+\ts_cbranch_scc1 .LBB0_1
+\tv_readfirstlane_b32 s12, v3
+\ts_cbranch_vccz .LBB0_3
+\ts_nop 7
+\ts_branch .LBB0_4
+.LBB0_3:
+\tbuffer_load_dwordx4 v4, s[12:15], 0 offen lds
+.LBB0_4:
+\ts_endpgm
+"""
+    found = sorted(lds_load_hazards(asm), key=lambda f: f[2])
+    assert [(w, t.split(",")[1].strip()) for _, w, t in found] == [(1, "s[12:15]"),
+                                                                    (1, "s[4:7]")]
+
+
 @pytest.mark.skipif(shutil.which(os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")) is None,
                     reason="hipcc not available")
-def test_gemm_kernels_have_no_valu_sgpr_hazard(tmp_path):
+@pytest.mark.parametrize("variant", ["plain", "trace"])
+def test_gemm_kernels_have_no_valu_sgpr_hazard(tmp_path, variant):
+    """Both library builds: the plain one and the one with timing records."""
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
     src = os.path.join(buildlib.PKG, "csrc", "moe_gemm.hip")
     out = tmp_path / "moe_gemm.s"
     flags = [f for f in buildlib.HIPCC_FLAGS if f not in ("-shared", "-fPIC")]
+    if variant == "trace":
+        flags += buildlib.TRACE_FLAGS
     cmd = [hipcc, *flags, "-I", os.path.join(buildlib.ROOT, "include"), "-I",
            os.path.join(buildlib.PKG, "csrc"), "-S", "--cuda-device-only", src, "-o", str(out)]
     r = subprocess.run(cmd, capture_output=True, text=True)

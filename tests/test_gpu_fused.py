@@ -11,6 +11,7 @@ import pytest
 import torch
 
 import oracle
+import sparse_expert_ffn_amd as moe
 from sparse_expert_ffn_amd import workloads as wk
 from tests.gpu_util import DeviceLayer, buffers, dev, host, parity
 
@@ -44,6 +45,8 @@ def _outputs(wl, li, G, bm, calls=1):
         for _ in range(calls if fused else 1):
             buf.O.fill_(float("nan"))
             res.append(host(L.forward(buf)).copy())
+            # no down task gave up its bounded wait for the SwiGLU rows
+            assert moe.forward_status(buf.forward_ws) == 0
     torch.cuda.synchronize()
     return res[0], res[1:]
 
@@ -136,6 +139,7 @@ def test_fused_atomic_combine(orc, name, S, bm):
     buf.O.fill_(float("nan"))
     out = host(L.forward(buf)).copy()
     torch.cuda.synchronize()
+    assert moe.forward_status(buf.forward_ws) == 0
     assert np.all(np.isfinite(out))
     ref = orc.layer(li.A, li.Wr, li.bias, li.W_up, li.W_gate, li.W_down, wl.k,
                     renormalize=wl.renormalize, capacity=wl.capacity, Ws_up=li.Ws_up,
