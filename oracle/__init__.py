@@ -23,7 +23,9 @@ _PLANT_DIR = os.path.join(_HERE, "_build")
 
 # Deliberately wrong variants used only by the pin self-test.
 PLANTS = ("TIE_HIGH", "WEIGHT_NO_EXP", "CAP_OFF_BY_ONE", "ALIGN_REVERSED",
-          "SILU_ON_GATE", "DOWN_TRANSPOSED", "WEIGHT_SLOT0", "DROP_SHARED", "ROW_INDEX")
+          "SILU_ON_GATE", "DOWN_TRANSPOSED", "WEIGHT_SLOT0", "DROP_SHARED", "ROW_INDEX",
+          "E4M3_TIES_AWAY", "E4M3_NO_SATURATE", "MX_EMAX7", "MX_WEIGHT_UNSCALED",
+          "MX_NO_H_QUANT")
 
 F32 = 0
 BF16 = 1
@@ -72,6 +74,14 @@ class Oracle:
                                         _p, _p, _p, _p, _p, _p, _p,
                                         _p, _p, _p, _i64, _p, _p]
         L.oracle_num_threads.restype = ctypes.c_int
+        L.oracle_e4m3_values.argtypes = [_i64, _p, _p]
+        L.oracle_e4m3_encode_array.argtypes = [_i64, _p, _p]
+        L.oracle_mx_quantize_rows.argtypes = [_i64, _i64, ctypes.c_int, _p, _p, _p]
+        L.oracle_mx_quantize_cols.argtypes = [_i64, _i64, ctypes.c_int, _p, _p, _p]
+        L.oracle_layer_rows_mx.argtypes = [_i64] * 5 + [_p] * 14 + [_p, _p, _p, _i64, _p, _p]
+        for f in (L.oracle_e4m3_values, L.oracle_e4m3_encode_array, L.oracle_mx_quantize_rows,
+                  L.oracle_mx_quantize_cols, L.oracle_layer_rows_mx):
+            f.restype = None
         for f in (L.oracle_gate_logits, L.oracle_topk_softmax, L.oracle_capacity_mask,
                   L.oracle_align, L.oracle_layer_rows):
             f.restype = None
@@ -167,6 +177,83 @@ class Oracle:
         self.lib.oracle_layer_rows(H, D, E, k, Ds, self._dtype_of(A), P(A), P(W_up), P(W_gate),
                                    P(W_down), P(Ws_up), P(Ws_gate), P(Ws_down), P(ids), P(w),
                                    P(kept), tokens.size, P(tokens), P(O))
+        return O
+
+    # ------------------------------------------------------------- MXFP8
+    def e4m3_values(self, codes) -> np.ndarray:
+        """float64 values of E4M3 codes (uint8 array)."""
+        c = np.ascontiguousarray(codes, dtype=np.uint8)
+        out = np.empty(c.shape, dtype=np.float64)
+        self.lib.oracle_e4m3_values(c.size, self._ptr(c), self._ptr(out))
+        return out
+
+    def e4m3_encode(self, x) -> np.ndarray:
+        """Nearest E4M3 codes of float64 values (ties to even, saturating)."""
+        x = np.ascontiguousarray(x, dtype=np.float64)
+        out = np.empty(x.shape, dtype=np.uint8)
+        self.lib.oracle_e4m3_encode_array(x.size, self._ptr(x), self._ptr(out))
+        return out
+
+    def mx_quantize_rows(self, X):
+        """MX blocks along the last axis of X [..][K]: (codes [..][K] uint8,
+        scales [..][K/32] uint8)."""
+        X = np.ascontiguousarray(X)
+        K = X.shape[-1]
+        assert K % 32 == 0
+        R = X.size // K
+        codes = np.empty(X.shape, dtype=np.uint8)
+        scales = np.empty(X.shape[:-1] + (K // 32,), dtype=np.uint8)
+        self.lib.oracle_mx_quantize_rows(R, K, self._dtype_of(X), self._ptr(X),
+                                         self._ptr(codes), self._ptr(scales))
+        return codes, scales
+
+    def mx_quantize_cols(self, W):
+        """MX blocks along axis -2 of W [..][K][N] (each column's K values in
+        blocks of 32): (codes [..][K][N], scales [..][K/32][N])."""
+        W = np.ascontiguousarray(W)
+        K, N = W.shape[-2:]
+        assert K % 32 == 0
+        lead = W.shape[:-2]
+        codes = np.empty(W.shape, dtype=np.uint8)
+        scales = np.empty(lead + (K // 32, N), dtype=np.uint8)
+        Wf = W.reshape((-1, K, N))
+        cf = codes.reshape((-1, K, N))
+        sf = scales.reshape((-1, K // 32, N))
+        for i in range(Wf.shape[0]):
+            wi = np.ascontiguousarray(Wf[i])
+            ci = np.empty((K, N), dtype=np.uint8)
+            si = np.empty((K // 32, N), dtype=np.uint8)
+            self.lib.oracle_mx_quantize_cols(K, N, self._dtype_of(wi), self._ptr(wi),
+                                             self._ptr(ci), self._ptr(si))
+            cf[i] = ci
+            sf[i] = si
+        return codes, scales
+
+    def layer_rows_mx(self, Aq, As, Wu, Wg, Wd, ids, w, kept=None, tokens=None,
+                      Wsu=None, Wsg=None, Wsd=None) -> np.ndarray:
+        """O rows [n][H] (float64) of the MXFP8 layer. Aq/As: the token rows'
+        codes and scales; Wu, Wg, Wd, Wsu, Wsg, Wsd: (codes, scales) pairs in
+        the layouts of mx_quantize_cols applied to W_up, W_gate [E][H][D],
+        W_down [E][D][H] and the shared [H][Ds], [H][Ds], [Ds][H]."""
+        S, H = Aq.shape
+        E, _, D = Wu[0].shape
+        k = ids.shape[1]
+        Ds = 0 if Wsu is None else Wsu[0].shape[1]
+        if tokens is None:
+            tokens = np.arange(S, dtype=np.int64)
+        tokens = np.ascontiguousarray(tokens, dtype=np.int64)
+        ids = np.ascontiguousarray(ids, dtype=np.int32)
+        w = np.ascontiguousarray(w, dtype=np.float32)
+        if kept is not None:
+            kept = np.ascontiguousarray(kept, dtype=np.uint8)
+        c = lambda x: None if x is None else np.ascontiguousarray(x, dtype=np.uint8)
+        arrs = [c(Aq), c(As), c(Wu[0]), c(Wu[1]), c(Wg[0]), c(Wg[1]), c(Wd[0]), c(Wd[1])]
+        sh = [None] * 6 if Wsu is None else [c(Wsu[0]), c(Wsu[1]), c(Wsg[0]), c(Wsg[1]),
+                                             c(Wsd[0]), c(Wsd[1])]
+        O = np.empty((tokens.size, H), dtype=np.float64)
+        P = self._ptr
+        self.lib.oracle_layer_rows_mx(H, D, E, k, Ds, *[P(a) for a in arrs + sh], P(ids), P(w),
+                                      P(kept), tokens.size, P(tokens), P(O))
         return O
 
     # ---------------------------------------------------------- whole layer

@@ -48,6 +48,11 @@
  * library's score tensor is fp32); the router weights are computed in double
  * and rounded once to fp32; the expert FFN and the combine stay in double.
  *
+ * MXFP8 mode (the functions at the end): the same layer with FP8 E4M3
+ * operands in MX blocks of 32 sharing an E8M0 scale, quantised by the OCP
+ * Microscaling rule; products of the dequantised values accumulate in double
+ * and the SwiGLU rows are requantised before the down projection.
+ *
  * ORACLE_PLANT_* macros build deliberately wrong variants for the pin
  * self-test only (each must be caught by at least one pin).
  */
@@ -261,6 +266,201 @@ void oracle_layer_rows(int64_t H, int64_t D, int64_t E, int64_t k, int64_t Ds, i
 #ifndef ORACLE_PLANT_DROP_SHARED
     if (Ds > 0) ffn_accumulate(H, Ds, dtype, A, (size_t)t * H, Ws_up, Ws_gate, Ws_down, 0, 0, 1.0, y);
 #endif
+  }
+}
+
+/* ------------------------------------------------------------------ MXFP8
+ * MXFP8 expert weights and activations (the Mixture-of-Kittens page names
+ * MXFP8 as the low-precision format of its MoE kernels; the format is the OCP
+ * Microscaling (MX) specification's): blocks of 32 consecutive values along
+ * the reduction dimension share one E8M0 scale 2^(x - 127); each value is an
+ * FP8 E4M3 number (1 sign, 4 exponent bits with bias 7, 3 mantissa bits;
+ * subnormals below 2^-6; largest magnitude 448; no infinities; S.1111.111 is
+ * NaN). A block's scale is 2^(floor(log2(max |v|)) - 8), 8 being the E4M3
+ * exponent of its largest binade, clamped to 2^-127 .. 2^127 (2^-127 for an
+ * all-zero block); each element is v / scale rounded to the nearest E4M3
+ * value, ties to the even code, magnitudes past 448 saturating to 448. */
+
+/* The value of an E4M3 code. */
+double oracle_e4m3_value(uint8_t c) {
+  const int s = c >> 7, e = (c >> 3) & 15, m = c & 7;
+  if (e == 15 && m == 7) return NAN;
+  /* normal: (1 + m/8) 2^(e-7) = (8 + m) 2^(e-10); subnormal: (m/8) 2^-6 = m 2^-9 */
+  const double v = e ? ldexp(8.0 + m, e - 10) : ldexp((double)m, -9);
+  return s ? -v : v;
+}
+
+/* The E4M3 code nearest to x (ties to the even code; |x| >= 448 gives +-448;
+ * a result of zero keeps x's sign). */
+uint8_t oracle_e4m3_encode(double x) {
+  const uint8_t sign = signbit(x) ? 0x80 : 0;
+  double a = fabs(x);
+#ifdef ORACLE_PLANT_E4M3_NO_SATURATE
+  if (a >= 480.0) return sign | 0x7F;
+#endif
+  if (a >= 448.0) return sign | 0x7E;
+  if (a == 0.0) return sign;
+  int e2;
+  frexp(a, &e2);
+  const int E = e2 - 1;                    /* a in [2^E, 2^(E+1)) */
+  const int step = E < -6 ? -9 : E - 3;    /* spacing of E4M3 values around a */
+#ifdef ORACLE_PLANT_E4M3_TIES_AWAY
+  const double q = round(ldexp(a, -step));
+#else
+  const double q = nearbyint(ldexp(a, -step));  /* default rounding: ties to even */
+#endif
+  if (E < -6) return sign | (uint8_t)q;   /* subnormal m = q (q = 8 is 2^-6, code 0x08) */
+  if (q >= 16.0) return sign | (uint8_t)((E + 8) << 3);   /* rounded up to 2^(E+1) */
+  return sign | (uint8_t)(((E + 7) << 3) | ((int)q - 8));
+}
+
+/* Element-wise forms of the two above, over n codes or values. */
+void oracle_e4m3_values(int64_t n, const uint8_t* c, double* out) {
+  for (int64_t i = 0; i < n; ++i) out[i] = oracle_e4m3_value(c[i]);
+}
+void oracle_e4m3_encode_array(int64_t n, const double* x, uint8_t* out) {
+  for (int64_t i = 0; i < n; ++i) out[i] = oracle_e4m3_encode(x[i]);
+}
+
+/* Scale exponent of a block whose largest magnitude is amax. */
+static int mx_scale_exp(double amax) {
+  if (amax == 0.0) return -127;
+  int e2;
+  frexp(amax, &e2);
+#ifdef ORACLE_PLANT_MX_EMAX7
+  int se = (e2 - 1) - 7;
+#else
+  int se = (e2 - 1) - 8;
+#endif
+  return se < -127 ? -127 : (se > 127 ? 127 : se);
+}
+
+/* MX blocks along the rows of a [R][K] matrix (K a multiple of 32):
+ * codes [R][K], scales [R][K/32]. */
+void oracle_mx_quantize_rows(int64_t R, int64_t K, int dtype, const void* V, uint8_t* codes,
+                             uint8_t* scales) {
+#pragma omp parallel for schedule(static)
+  for (int64_t r = 0; r < R; ++r)
+    for (int64_t b = 0; b < K / 32; ++b) {
+      double amax = 0.0;
+      for (int64_t i = 0; i < 32; ++i) {
+        const double v = fabs(elem(V, dtype, (size_t)r * K + b * 32 + i));
+        if (v > amax) amax = v;
+      }
+      const int se = mx_scale_exp(amax);
+      scales[(size_t)r * (K / 32) + b] = (uint8_t)(se + 127);
+      for (int64_t i = 0; i < 32; ++i)
+        codes[(size_t)r * K + b * 32 + i] =
+            oracle_e4m3_encode(ldexp(elem(V, dtype, (size_t)r * K + b * 32 + i), -se));
+    }
+}
+
+/* MX blocks along the columns of a [K][N] matrix (K a multiple of 32): block
+ * b of column n holds rows 32b .. 32b + 31. codes [K][N], scales [K/32][N]. */
+void oracle_mx_quantize_cols(int64_t K, int64_t N, int dtype, const void* V, uint8_t* codes,
+                             uint8_t* scales) {
+#pragma omp parallel for schedule(static)
+  for (int64_t n = 0; n < N; ++n)
+    for (int64_t b = 0; b < K / 32; ++b) {
+      double amax = 0.0;
+      for (int64_t i = 0; i < 32; ++i) {
+        const double v = fabs(elem(V, dtype, (size_t)(b * 32 + i) * N + n));
+        if (v > amax) amax = v;
+      }
+      const int se = mx_scale_exp(amax);
+      scales[(size_t)b * N + n] = (uint8_t)(se + 127);
+      for (int64_t i = 0; i < 32; ++i)
+        codes[(size_t)(b * 32 + i) * N + n] =
+            oracle_e4m3_encode(ldexp(elem(V, dtype, (size_t)(b * 32 + i) * N + n), -se));
+    }
+}
+
+/* The value an MX element stands for: its code's value times its block's scale. */
+static double mx_value(const uint8_t* codes, const uint8_t* scales, size_t i, size_t si) {
+  return ldexp(oracle_e4m3_value(codes[i]), (int)scales[si] - 127);
+}
+
+/* y[H] += scale * W_down^T q(SwiGLU(W_up^T a, W_gate^T a)) for one token with
+ * MXFP8 operands: the token's row (codes a_q[H], scales a_s[H/32]); W_up,
+ * W_gate [H][Dx] with scales [H/32][Dx]; W_down [Dx][H] with scales
+ * [Dx/32][H]. u and g are exact sums of the dequantised products (double),
+ * rounded to fp32 as the GPU holds them; the SwiGLU value is rounded to fp32
+ * and q() quantises the Dx of them to MX blocks of 32 (the down projection's
+ * reduction runs over Dx) before the down projection. */
+static void ffn_accumulate_mx(int64_t H, int64_t Dx, const uint8_t* a_q, const uint8_t* a_s,
+                              const uint8_t* wu_q, const uint8_t* wu_s, const uint8_t* wg_q,
+                              const uint8_t* wg_s, const uint8_t* wd_q, const uint8_t* wd_s,
+                              double scale, double* y) {
+  double* u = (double*)calloc((size_t)Dx, sizeof(double));
+  double* g = (double*)calloc((size_t)Dx, sizeof(double));
+  float* hv = (float*)malloc((size_t)Dx * sizeof(float));
+  uint8_t* h_q = (uint8_t*)malloc((size_t)Dx);
+  uint8_t* h_s = (uint8_t*)malloc((size_t)(Dx / 32));
+  for (int64_t h = 0; h < H; ++h) {
+    const double a = mx_value(a_q, a_s, (size_t)h, (size_t)(h / 32));
+    for (int64_t d = 0; d < Dx; ++d) {
+#ifdef ORACLE_PLANT_MX_WEIGHT_UNSCALED
+      u[d] += a * oracle_e4m3_value(wu_q[(size_t)h * Dx + d]);
+#else
+      u[d] += a * mx_value(wu_q, wu_s, (size_t)h * Dx + d, (size_t)(h / 32) * Dx + d);
+#endif
+      g[d] += a * mx_value(wg_q, wg_s, (size_t)h * Dx + d, (size_t)(h / 32) * Dx + d);
+    }
+  }
+  for (int64_t d = 0; d < Dx; ++d) {
+    const float u32 = (float)u[d], g32 = (float)g[d];
+    hv[d] = (float)(silu((double)u32) * (double)g32);
+  }
+#ifdef ORACLE_PLANT_MX_NO_H_QUANT
+  for (int64_t d = 0; d < Dx; ++d)
+    for (int64_t n = 0; n < H; ++n)
+      y[n] += scale * (double)hv[d] * mx_value(wd_q, wd_s, (size_t)d * H + n, (size_t)(d / 32) * H + n);
+#else
+  oracle_mx_quantize_rows(1, Dx, OR_F32, hv, h_q, h_s);
+  for (int64_t d = 0; d < Dx; ++d) {
+    const double hd = mx_value(h_q, h_s, (size_t)d, (size_t)(d / 32));
+    for (int64_t n = 0; n < H; ++n)
+      y[n] += scale * hd * mx_value(wd_q, wd_s, (size_t)d * H + n, (size_t)(d / 32) * H + n);
+  }
+#endif
+  free(u);
+  free(g);
+  free(hv);
+  free(h_q);
+  free(h_s);
+}
+
+/* Output rows of the layer with MXFP8 operands, for the listed tokens, given
+ * the routing (as oracle_layer_rows): A_q [S][H] with A_s [S][H/32] (the MX
+ * blocks of each token row); W_up_q, W_gate_q [E][H][D] with scales
+ * [E][H/32][D]; W_down_q [E][D][H] with scales [E][D/32][H]; the shared
+ * expert's [H][Ds], [H/32][Ds] and [Ds][H], [Ds/32][H] (Ds = 0: none). */
+void oracle_layer_rows_mx(int64_t H, int64_t D, int64_t E, int64_t k, int64_t Ds,
+                          const uint8_t* A_q, const uint8_t* A_s, const uint8_t* Wu_q,
+                          const uint8_t* Wu_s, const uint8_t* Wg_q, const uint8_t* Wg_s,
+                          const uint8_t* Wd_q, const uint8_t* Wd_s, const uint8_t* Wsu_q,
+                          const uint8_t* Wsu_s, const uint8_t* Wsg_q, const uint8_t* Wsg_s,
+                          const uint8_t* Wsd_q, const uint8_t* Wsd_s, const int32_t* ids,
+                          const float* w, const uint8_t* kept, int64_t n_rows,
+                          const int64_t* tokens, double* O) {
+  (void)E;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t i = 0; i < n_rows; ++i) {
+    const int64_t t = tokens[i];
+    double* y = O + (size_t)i * H;
+    for (int64_t n = 0; n < H; ++n) y[n] = 0.0;
+    const uint8_t* a_q = A_q + (size_t)t * H;
+    const uint8_t* a_s = A_s + (size_t)t * (H / 32);
+    for (int64_t j = 0; j < k; ++j) {
+      const size_t f = (size_t)t * k + j;
+      if (kept && !kept[f]) continue;
+      const size_t e = (size_t)ids[f];
+      ffn_accumulate_mx(H, D, a_q, a_s, Wu_q + e * H * D, Wu_s + e * (H / 32) * D,
+                        Wg_q + e * H * D, Wg_s + e * (H / 32) * D, Wd_q + e * D * H,
+                        Wd_s + e * (D / 32) * H, (double)w[f], y);
+    }
+    if (Ds > 0)
+      ffn_accumulate_mx(H, Ds, a_q, a_s, Wsu_q, Wsu_s, Wsg_q, Wsg_s, Wsd_q, Wsd_s, 1.0, y);
   }
 }
 

@@ -367,9 +367,164 @@ def check_weights_sum_one_layer(orc):
     _close(O, one, 1e-6, "identical experts with weights summing to 1")
 
 
+# ---------------------------------------------------------------------- MXFP8
+
+def _e4m3_table():
+    """Every finite non-negative E4M3 value, from torch's float8_e4m3fn
+    (a library's decoding of the format), indexed by code 0x00 .. 0x7E."""
+    codes = torch.arange(0x7F, dtype=torch.uint8).view(torch.float8_e4m3fn)
+    return codes.to(torch.float64).numpy()
+
+
+def check_e4m3_decode(orc):
+    codes = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    got = orc.e4m3_values(codes)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan) and nan.sum() == 2, "NaN codes 0x7F, 0xFF"
+    assert np.array_equal(got[~nan], ref[~nan]), "E4M3 values vs torch float8_e4m3fn"
+    assert np.array_equal(np.signbit(got[~nan]), np.signbit(ref[~nan])), "signed zero"
+
+
+def check_e4m3_encode(orc):
+    """Nearest E4M3 value by brute force over the 127 magnitudes, ties to the
+    even code; |x| >= 448 saturates; zero results keep the sign. Inputs: every
+    value, every midpoint between neighbours (the ties), random values over
+    all binades and the subnormal range, values past 448."""
+    table = _e4m3_table()
+    mids = (table[1:] + table[:-1]) / 2
+    rng = np.random.default_rng(21)
+    rand = np.ldexp(rng.random(3000) + 0.5, rng.integers(-14, 10, 3000))
+    x = np.concatenate([table, mids, rand, [448.0, 449.0, 463.9, 464.0, 500.0, 1e30,
+                                            2.0 ** -10, 2.0 ** -11]])
+    x = np.concatenate([x, -x, [0.0, -0.0]])
+    got = orc.e4m3_encode(x)
+    a = np.abs(x)
+    ref = np.empty(x.size, dtype=np.uint8)
+    for i, v in enumerate(a):
+        if v >= 448.0:
+            c = 0x7E
+        else:
+            d = np.abs(table - v)
+            best = np.flatnonzero(d == d.min())
+            c = int(best[0]) if best.size == 1 else int(best[best % 2 == 0][0])
+        ref[i] = c | (0x80 if np.signbit(x[i]) else 0)
+    bad = np.flatnonzero(got != ref)
+    assert bad.size == 0, f"E4M3 rounding: {x[bad[:5]]} -> {got[bad[:5]]}, expected {ref[bad[:5]]}"
+    # a library's rounding of the same values inside the finite range
+    inr = a < 464.0
+    lib = torch.from_numpy(x[inr]).to(torch.float32).to(torch.float8_e4m3fn).view(torch.uint8)
+    assert np.array_equal(got[inr], lib.numpy()), "E4M3 rounding vs torch float8_e4m3fn"
+
+
+def check_mx_golden(orc):
+    for b in _golden("worked_mxfp8.json")["blocks"]:
+        v = np.asarray(b["values"], dtype=np.float32)[None, :]
+        c, s = orc.mx_quantize_rows(v)
+        assert int(s[0, 0]) == b["scale_code"], f"scale of {b['values'][:4]}: {s[0, 0]}"
+        assert c[0].tolist() == b["codes"], f"codes of {b['values'][:4]}: {c[0][:6]}"
+        # the same block along a column of a [32][N] matrix
+        cc, sc = orc.mx_quantize_cols(np.ascontiguousarray(np.repeat(v.T, 3, axis=1)))
+        assert np.all(sc == b["scale_code"]) and np.all(cc[:, 1] == c[0])
+
+
+def _mx_reference(x64, axis):
+    """The MX rule written with numpy / torch pieces: scale exponent from the
+    block maximum's binary exponent, elements by torch's E4M3 rounding after
+    the saturation at 448 (torch has no saturation of its own)."""
+    x = np.moveaxis(np.asarray(x64, dtype=np.float64), axis, -1)
+    blocks = x.reshape(x.shape[:-1] + (x.shape[-1] // 32, 32))
+    amax = np.abs(blocks).max(axis=-1)
+    _, e2 = np.frexp(amax)
+    se = np.where(amax > 0, np.clip(e2 - 1 - 8, -127, 127), -127)
+    y = np.clip(blocks / np.ldexp(1.0, se)[..., None], -448.0, 448.0)
+    q = torch.from_numpy(y).to(torch.float32).to(torch.float8_e4m3fn)
+    codes = q.view(torch.uint8).numpy().reshape(x.shape)
+    vals = q.to(torch.float64).numpy() * np.ldexp(1.0, se)[..., None]
+    return (np.moveaxis(codes, -1, axis), np.moveaxis((se + 127).astype(np.uint8), -1, axis),
+            np.moveaxis(vals.reshape(x.shape), -1, axis))
+
+
+def check_mx_quantize_reference(orc):
+    rng = np.random.default_rng(22)
+    for dtype in (wk.F32, wk.BF16):
+        X = _rand((7, 96), 1.0, dtype, [22, 0])
+        X64 = _f64(X).copy()
+        X64[0, :32] = 0.0                     # an all-zero block
+        X64[1, 32:64] *= 2.0 ** -120          # a block near the bottom of the scale range
+        X64[2, 64:] = np.ldexp(1.0, rng.integers(-6, 6, 32))  # exact after scaling
+        Xq = X64.astype(np.float32)
+        c, s = orc.mx_quantize_rows(Xq)
+        rc, rs, _ = _mx_reference(Xq, -1)
+        assert np.array_equal(s, rs), "MX scales vs the reference rule"
+        assert np.array_equal(c, rc), "MX codes vs the reference rule"
+        back = orc.e4m3_values(c[2, 64:]) * np.ldexp(1.0, int(s[2, 2]) - 127)
+        assert np.array_equal(back, X64[2, 64:]), "powers of two survive quantisation"
+        cc, sc = orc.mx_quantize_cols(np.ascontiguousarray(Xq.T))
+        assert np.array_equal(cc, c.T) and np.array_equal(sc, s.T), "rows vs columns"
+    # scaling a block by 2^j moves its scale by j and keeps its codes
+    X = _rand((4, 64), 1.0, wk.F32, [22, 1])
+    c0, s0 = orc.mx_quantize_rows(X)
+    c1, s1 = orc.mx_quantize_rows((X.astype(np.float64) * 2.0 ** 5).astype(np.float32))
+    assert np.array_equal(c0, c1) and np.array_equal(s1.astype(int), s0.astype(int) + 5)
+
+
+def _mx_layer_reference(orc_q, L, ids, w, kept):
+    """Dense brute force of the MXFP8 layer (torch float64): every expert on
+    every token masked by the routing; operands dequantised with the reference
+    rule; u, g and the SwiGLU value rounded to fp32, the SwiGLU rows
+    requantised along D before the down projection."""
+    A = _mx_reference(_f64(L["A"]), -1)[2]
+    deq = lambda W: _mx_reference(_f64(W), -2)[2]
+    Wu, Wg, Wd = deq(L["W_up"]), deq(L["W_gate"]), deq(L["W_down"])
+    S, k = ids.shape
+    E = Wu.shape[0]
+    M = np.zeros((S, E))
+    for s in range(S):
+        for j in range(k):
+            if kept is None or kept[s, j]:
+                M[s, int(ids[s, j])] += float(w[s, j])
+
+    def ffn(a, wu, wg, wd):
+        u = (a @ wu).astype(np.float32).astype(np.float64)
+        g = (a @ wg).astype(np.float32).astype(np.float64)
+        h = (torch.nn.functional.silu(torch.from_numpy(u)).numpy() * g).astype(np.float32)
+        return _mx_reference(h.astype(np.float64), -1)[2] @ wd
+
+    O = sum(M[:, e:e + 1] * ffn(A, Wu[e], Wg[e], Wd[e]) for e in range(E))
+    if L.get("Ws_up") is not None:
+        O = O + ffn(A, deq(L["Ws_up"]), deq(L["Ws_gate"]), deq(L["Ws_down"]))
+    return O
+
+
+def _mx_layer(orc, L, ids, w, kept=None, tokens=None):
+    q = orc.mx_quantize_cols
+    sh = {}
+    if L.get("Ws_up") is not None:
+        sh = dict(Wsu=q(L["Ws_up"]), Wsg=q(L["Ws_gate"]), Wsd=q(L["Ws_down"]))
+    Aq, As = orc.mx_quantize_rows(L["A"])
+    return orc.layer_rows_mx(Aq, As, q(L["W_up"]), q(L["W_gate"]), q(L["W_down"]), ids, w,
+                             kept, tokens, **sh)
+
+
+def check_layer_mx_dense(orc):
+    for dtype in (wk.F32, wk.BF16):
+        for (S, H, D, E, k, C, Ds) in ((20, 64, 32, 4, 2, 0, 0), (17, 32, 64, 5, 3, 6, 32)):
+            L = _tiny_layer(dtype, S, H, D, E, k, Ds, seed=S + H)
+            out = _layer(orc, L, k, capacity=C)  # the routing
+            got = _mx_layer(orc, L, out["ids"], out["w"], out["kept"])
+            ref = _mx_layer_reference(orc, L, out["ids"], out["w"], out["kept"])
+            _close(got, ref, 1e-12, f"MXFP8 layer vs dense brute force dtype={dtype} Ds={Ds}")
+            # against the unquantised layer: the format's own error, a few % of RMS
+            rms = float(np.sqrt(np.mean(out["O"] ** 2)))
+            err = float(np.max(np.abs(got - out["O"]))) / rms
+            assert 0.0 < err < 0.5, f"MXFP8 layer vs unquantised: {err:.3f} of RMS"
+
+
 CHECKS = [check_golden_layer, check_golden_align, check_golden_topk, check_logits_matmul,
           check_topk_library, check_topk_invariants, check_align_bruteforce,
           check_capacity_mask, check_layer_dense, check_plain_ffn, check_down_scaling,
           check_expert_permutation, check_token_permutation, check_capacity_limits,
           check_zero_expert, check_shared_only, check_weights_sum_one_layer,
-          check_router_bias, check_layer_rows_subset]
+          check_router_bias, check_layer_rows_subset, check_e4m3_decode, check_e4m3_encode,
+          check_mx_golden, check_mx_quantize_reference, check_layer_mx_dense]
