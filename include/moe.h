@@ -253,6 +253,33 @@ moe_status moe_forward(const moe_shape* shape, const void* A, const void* W_up,
                        const int32_t* num_tokens_post_padded, void* O, void* workspace,
                        size_t workspace_bytes, void* stream);
 
+/*
+ * moe_forward for callers that cannot allocate device memory: code being
+ * captured into a HIP graph, tight serving loops, harnesses that forbid
+ * hipMalloc. The same computation, kernels and results as moe_forward, bit
+ * for bit, with no workspace argument: the workspace is an array in the
+ * library's device image, MOE_NOALLOC_SCRATCH_BYTES per GPU, which each GPU
+ * the library runs on holds from its first use until the process ends. The
+ * call itself allocates nothing (no hipMalloc, no allocating library call,
+ * no events: the per-stage timer does not record it).
+ *  - Shapes whose moe_forward_workspace_bytes exceeds the array return
+ *    MOE_ERR_WORKSPACE_TOO_SMALL before anything is enqueued (decode-sized
+ *    calls fit: e.g. S = 64 tokens of the DeepSeek-V3-style layer, H = 7168,
+ *    256 experts top-8 plus a shared expert, needs about 35 MB).
+ *  - Every call on one GPU uses that GPU's one array and leaves its contents
+ *    behind; each call clears what must start at zero itself. Calls that
+ *    overlap on one GPU (other streams, other host threads) race on the
+ *    array and give wrong results: serialise them.
+ *  - Other arguments, errors and flags as moe_forward.
+ */
+#define MOE_NOALLOC_SCRATCH_BYTES (64u << 20)
+moe_status moe_forward_noalloc(const moe_shape* shape, const void* A, const void* W_up,
+                               const void* W_gate, const void* W_down, const void* Ws_up,
+                               const void* Ws_gate, const void* Ws_down,
+                               const float* topk_weights, const int32_t* sorted_ids,
+                               const int32_t* expert_ids, const int32_t* num_tokens_post_padded,
+                               void* O, void* stream);
+
 /* Static, never-NULL text for a status code. */
 const char* moe_status_string(moe_status status);
 

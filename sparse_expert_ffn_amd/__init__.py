@@ -19,7 +19,7 @@ __all__ = ["MOE_F32", "MOE_BF16", "MoeError", "moe_shape", "make_shape", "load_l
            "moe_align_block_size",
            "moe_forward_workspace_bytes", "moe_forward", "moe_status_string",
            "moe_profile_enable", "moe_profile_collect", "moe_device_query", "moe_trace_attach",
-           "forward_status",
+           "moe_forward_noalloc", "MOE_NOALLOC_SCRATCH_BYTES", "forward_status",
            "build",
            "LIB_PATH", "STATUS", "MOE_FORWARD_STATUS_OFFSET", "MOE_STATUS_READY_TIMEOUT"]
 
@@ -37,6 +37,8 @@ MOE_FUSED_LAUNCH = 8  # up/gate and down GEMMs in one persistent launch (bf16)
 # byte offset of the int32 status word in the moe_forward workspace, and its bits
 MOE_FORWARD_STATUS_OFFSET = 128
 MOE_STATUS_READY_TIMEOUT = 1
+# device array behind moe_forward_noalloc, per GPU
+MOE_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 STATUS = {0: "MOE_OK", 1: "MOE_ERR_INVALID_ARGUMENT", 2: "MOE_ERR_UNSUPPORTED",
           3: "MOE_ERR_WORKSPACE_TOO_SMALL", 4: "MOE_ERR_HIP"}
@@ -45,7 +47,8 @@ STATUS = {0: "MOE_OK", 1: "MOE_ERR_INVALID_ARGUMENT", 2: "MOE_ERR_UNSUPPORTED",
 EXPORTS = ("moe_gate_workspace_bytes", "moe_gate_topk", "moe_align_workspace_bytes",
            "moe_align_block_size",
            "moe_forward_workspace_bytes", "moe_forward", "moe_status_string",
-           "moe_profile_enable", "moe_profile_collect", "moe_device_query", "moe_trace_attach")
+           "moe_profile_enable", "moe_profile_collect", "moe_device_query", "moe_trace_attach",
+           "moe_forward_noalloc")
 
 
 class MoeError(RuntimeError):
@@ -115,6 +118,8 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.moe_device_query.argtypes = [ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_int),
                                      ctypes.c_char_p, sz]
     lib.moe_trace_attach.argtypes = [vp, sz]
+    lib.moe_forward_noalloc.argtypes = [sp] + [vp] * 13
+    lib.moe_forward_noalloc.restype = ctypes.c_int
     for name in ("moe_gate_topk", "moe_align_block_size", "moe_forward", "moe_profile_enable",
                  "moe_profile_collect", "moe_device_query", "moe_trace_attach"):
         getattr(lib, name).restype = ctypes.c_int
@@ -214,6 +219,20 @@ def moe_forward(shape, A, W_up, W_gate, W_down, Ws_up, Ws_gate, Ws_down, topk_we
         _addr(expert_ids), _addr(num_tokens_post_padded), _addr(O), wa, wn, _stream(stream))
     if check:
         _check("moe_forward", code)
+    return code
+
+
+def moe_forward_noalloc(shape, A, W_up, W_gate, W_down, Ws_up, Ws_gate, Ws_down, topk_weights,
+                        sorted_ids, expert_ids, num_tokens_post_padded, O, stream=None,
+                        check=True) -> int:
+    """moe_forward with the library's own device array as the workspace (at
+    most MOE_NOALLOC_SCRATCH_BYTES): the call allocates nothing."""
+    code = load_library().moe_forward_noalloc(
+        ctypes.byref(shape), _addr(A), _addr(W_up), _addr(W_gate), _addr(W_down), _addr(Ws_up),
+        _addr(Ws_gate), _addr(Ws_down), _addr(topk_weights), _addr(sorted_ids),
+        _addr(expert_ids), _addr(num_tokens_post_padded), _addr(O), _stream(stream))
+    if check:
+        _check("moe_forward_noalloc", code)
     return code
 
 

@@ -160,7 +160,37 @@ hipError_t run_stage(int stage, hipStream_t st, F launch) {
   return hipSuccess;
 }
 
-// moe_forward on a given workspace; timing = false records no stage events.
+// ------------------------------------------------ allocation-free workspace
+// The workspace of moe_forward_noalloc: one array per GPU in the library's
+// device image, held from the module's load until the process ends. In host
+// code `scratch` names a host-side stand-in, not the device array: the
+// device address comes from hipGetSymbolAddress, taken once per device with
+// that device current, and only that address is passed to kernels.
+constexpr size_t kScratchBytes = (size_t)MOE_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_dev[kMaxDevices] = {nullptr};
+
+// The current device's scratch address (looked up on its first use).
+moe_status scratch_address(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return MOE_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return MOE_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (g_scratch_dev[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr)
+      return MOE_ERR_HIP;
+    g_scratch_dev[dev] = p;
+  }
+  *out = g_scratch_dev[dev];
+  return MOE_OK;
+}
+
+// moe_forward on a given workspace. timing = false: no stage events (the
+// allocation-free entry point creates none).
 moe_status forward_impl(const moe_shape* shape, const void* A, const void* W_up,
                         const void* W_gate, const void* W_down, const void* Ws_up,
                         const void* Ws_gate, const void* Ws_down, const float* topk_weights,
@@ -382,6 +412,28 @@ moe_status moe_forward(const moe_shape* shape, const void* A, const void* W_up,
                       sorted_ids, expert_ids, num_tokens_post_padded, O, workspace,
                       workspace_bytes, stream, true);
 }
+
+moe_status moe_forward_noalloc(const moe_shape* shape, const void* A, const void* W_up,
+                               const void* W_gate, const void* W_down, const void* Ws_up,
+                               const void* Ws_gate, const void* Ws_down,
+                               const float* topk_weights, const int32_t* sorted_ids,
+                               const int32_t* expert_ids, const int32_t* num_tokens_post_padded,
+                               void* O, void* stream) {
+  moe_status st = check_forward_dims(shape);
+  if (st != MOE_OK) return st;
+  if (forward_layout(shape).total > sizeof(scratch)) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  if (shape->S == 0)
+    return forward_impl(shape, A, W_up, W_gate, W_down, Ws_up, Ws_gate, Ws_down, topk_weights,
+                        sorted_ids, expert_ids, num_tokens_post_padded, O, nullptr, 0, stream,
+                        false);
+  void* ws = nullptr;
+  st = scratch_address(&ws);
+  if (st != MOE_OK) return st;
+  return forward_impl(shape, A, W_up, W_gate, W_down, Ws_up, Ws_gate, Ws_down, topk_weights,
+                      sorted_ids, expert_ids, num_tokens_post_padded, O, ws, sizeof(scratch),
+                      stream, false);
+}
+
 
 moe_status moe_trace_attach(void* buffer, size_t bytes) {
   if (!MOE_TRACE) return MOE_ERR_UNSUPPORTED;

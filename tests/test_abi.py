@@ -185,3 +185,20 @@ def test_forward_status_word_layout(lib):
     for kw in (dict(), dict(S=1, E=1, k=1), dict(dtype=moe.MOE_F32, block_size=128),
                dict(fused_launch=True), dict(atomic_combine=True)):
         assert moe.moe_forward_workspace_bytes(shape(**kw)) >= off + 4, kw
+
+
+def test_noalloc_validation(lib):
+    """The allocation-free forward rejects shapes whose workspace exceeds its
+    device array, and bad arguments, before touching the device."""
+    macros = _header_macros()
+    assert "MOE_NOALLOC_SCRATCH_BYTES" in open(HEADER).read()
+    assert moe.MOE_NOALLOC_SCRATCH_BYTES == 64 << 20
+    big = shape(S=16384, H=2048, D=2048, E=64, k=2, capacity=512, block_size=256)
+    assert moe.moe_forward_workspace_bytes(big) > moe.MOE_NOALLOC_SCRATCH_BYTES
+    f = lambda s: lib.moe_forward_noalloc(ctypes.byref(s) if s is not None else None,
+                                          *([FAKE] * 4), None, None, None, *([FAKE] * 5), None)
+    assert f(big) == 3                       # MOE_ERR_WORKSPACE_TOO_SMALL
+    assert f(None) == 1
+    assert f(shape(k=9)) == 1
+    assert f(shape(block_size=48)) == 2
+    assert macros  # header parsed
