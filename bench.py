@@ -28,6 +28,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 MFMA
 PEAK_F32_TFLOPS = 157.3     # MI355X fp32 (MFMA / vector)
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 
@@ -67,17 +68,21 @@ def layer_counts(wl, counts_e, bm):
     counts (routing-dependent)."""
     kept = int(counts_e.sum())
     touched = int((counts_e > 0).sum())
-    b = wl.elem_bytes
+    # expert weights: bf16 / fp32 elements, or MXFP8 (a byte per element and a
+    # scale byte per 32)
+    b = 33.0 / 32.0 if wl.mxfp8 else wl.elem_bytes
     f_gate = 2.0 * wl.S * wl.H * wl.E
     f_up = 4.0 * wl.H * wl.D * kept + 4.0 * wl.H * wl.D_shared * wl.S
     f_down = 2.0 * wl.D * wl.H * kept + 2.0 * wl.D_shared * wl.H * wl.S
     w_expert = 3.0 * wl.H * wl.D * b
     bytes_w = touched * w_expert + 3.0 * wl.H * wl.D_shared * b
-    bytes_up = touched * 2.0 * wl.H * wl.D * b + 2.0 * wl.H * wl.D_shared * b + wl.S * wl.H * b
-    bytes_io = 2.0 * wl.S * wl.H * b + wl.H * wl.E * b
+    bytes_up = touched * 2.0 * wl.H * wl.D * b + 2.0 * wl.H * wl.D_shared * b + \
+        wl.S * wl.H * wl.elem_bytes
+    bytes_io = 2.0 * wl.S * wl.H * wl.elem_bytes + wl.H * wl.E * wl.elem_bytes
     # both expert GEMMs in one kernel: the touched weights, A, and the fp32
     # slot rows it writes (h stays between its two halves)
-    bytes_experts = bytes_w + wl.S * wl.H * b + 4.0 * wl.H * (kept + (wl.S if wl.D_shared else 0))
+    bytes_experts = bytes_w + wl.S * wl.H * wl.elem_bytes + \
+        4.0 * wl.H * (kept + (wl.S if wl.D_shared else 0))
     return {"kept": kept, "touched": touched, "flops_gate": f_gate, "flops_up": f_up,
             "flops_down": f_down, "flops": f_gate + f_up + f_down,
             "bytes": bytes_w + bytes_io, "bytes_up": bytes_up, "bytes_experts": bytes_experts}
@@ -187,7 +192,8 @@ def setup_workload(wl, args, torch, moe, dev="cuda"):
     from sparse_expert_ffn_amd import workloads as wk
     from sparse_expert_ffn_amd.layer import MoEBuffers, suggest_block_size
 
-    bm = args.block_size or suggest_block_size(wl.S, wl.k, wl.E, wl.capacity, wl.dtype)
+    dtype = moe.MOE_MXFP8 if wl.mxfp8 else wl.dtype
+    bm = args.block_size or suggest_block_size(wl.S, wl.k, wl.E, wl.capacity, dtype)
 
     def td(a):
         if a is None:
@@ -218,12 +224,22 @@ def setup_workload(wl, args, torch, moe, dev="cuda"):
         Wsu = td(wk.draw_tensor(wl, wk.T_WSUP, (wl.H, wl.D_shared), ssu))
         Wsg = td(wk.draw_tensor(wl, wk.T_WSGATE, (wl.H, wl.D_shared), ssu))
         Wsd = td(wk.draw_tensor(wl, wk.T_WSDOWN, (wl.D_shared, wl.H), ssd))
+    if wl.mxfp8:  # the expert weights packed once, as a weight load would
+        def pack(W):
+            if W is None:
+                return None
+            E, K, N = (1,) + tuple(W.shape) if W.dim() == 2 else tuple(W.shape)
+            out = torch.empty(moe.moe_mxfp8_weight_bytes(E, K, N), dtype=torch.uint8, device=dev)
+            moe.moe_pack_mxfp8_weights(W, out)
+            return out
+        Wu, Wg, Wd, Wsu, Wsg, Wsd = (pack(x) for x in (Wu, Wg, Wd, Wsu, Wsg, Wsd))
+        torch.cuda.synchronize()
     n_copies = max(1, args.weight_copies)
     copies = [(Wu, Wg, Wd, Wsu, Wsg, Wsd)]
     for _ in range(n_copies - 1):  # same values, other addresses
         copies.append(tuple(None if x is None else x.clone() for x in copies[0]))
     buf = MoEBuffers(wl.S, wl.H, wl.D, wl.E, wl.k, wl.D_shared, wl.capacity, bm,
-                     wl.renormalize, wl.dtype, sched_quota=args.sched == "quota",
+                     wl.renormalize, dtype, sched_quota=args.sched == "quota",
                      fused_launch=args.launch == "one", device=dev)
     stream = torch.cuda.current_stream()
     n_step = [0]
@@ -266,18 +282,18 @@ def measure(wl, args, steps, warmup, torch, moe, full=True):
     torch.cuda.synchronize()
     wall = time.perf_counter() - w0
     moe.moe_profile_enable(False)
-    stage_ms, n_calls = moe.moe_profile_collect(4)
+    stage_ms, n_calls = moe.moe_profile_collect(5)
     ms = ev0.elapsed_time(ev1) / steps
     up_ms = stage_ms[1] / max(n_calls, 1)
     # setup, down and combine kernels, timed in a few extra steps after the
     # timed region
-    moe.moe_profile_enable(True, stages=(0, 2, 3))
+    moe.moe_profile_enable(True, stages=(0, 2, 3, 4))
     n_extra = min(steps, 10)
     for _ in range(n_extra):
         step()
     torch.cuda.synchronize()
     moe.moe_profile_enable(False)
-    small_ms, n_small = moe.moe_profile_collect(4)
+    small_ms, n_small = moe.moe_profile_collect(5)
     down_ms = small_ms[2] / max(n_small, 1)
     # per-step times (an event pair per step), for the median; after the timed
     # region, which holds no per-step markers
@@ -291,7 +307,8 @@ def measure(wl, args, steps, warmup, torch, moe, full=True):
     med_ms = float(np.median([e0.elapsed_time(e1) for e0, e1 in evs])) if evs else None
     status = moe.forward_status(buf.forward_ws)
 
-    peak = PEAK_BF16_TFLOPS if wl.dtype == wk.BF16 else PEAK_F32_TFLOPS
+    peak = PEAK_FP8_TFLOPS if wl.mxfp8 else (PEAK_BF16_TFLOPS if wl.dtype == wk.BF16
+                                             else PEAK_F32_TFLOPS)
     # the roofline kernel: up/gate, or with one launch both expert GEMMs
     k_flops = cnt["flops_up"] + cnt["flops_down"] if one else cnt["flops_up"]
     k_bytes = cnt["bytes_experts"] if one else cnt["bytes_up"]
@@ -331,9 +348,11 @@ def measure(wl, args, steps, warmup, torch, moe, full=True):
               "D_shared": wl.D_shared, "capacity": wl.capacity, "block_size": bm,
               "scheduler": args.sched, "launch": args.launch, "weight_copies": n_copies,
               "parallelism": "single GPU"}
+    if wl.mxfp8:
+        layer["quantize_ms"] = small_ms[4] / max(n_small, 1)
     rec = {"ms_per_step": ms, "value": wl.S / (ms * 1e-3), "config": config, "roofline": roof,
            "layer": layer, "routing": routing, "steps": steps, "warmup": warmup,
-           "dtype": "bf16" if wl.dtype == wk.BF16 else "f32"}
+           "dtype": "mxfp8" if wl.mxfp8 else ("bf16" if wl.dtype == wk.BF16 else "f32")}
     del buf
     torch.cuda.empty_cache()
     return rec

@@ -63,7 +63,11 @@ typedef enum {
 
 typedef enum {
   MOE_F32 = 0,   /* activations, weights and output are fp32                */
-  MOE_BF16 = 1   /* bf16 activations/weights/output; accumulation is fp32  */
+  MOE_BF16 = 1,  /* bf16 activations/weights/output; accumulation is fp32  */
+  MOE_MXFP8 = 2  /* MXFP8 expert GEMMs: bf16 activations, router and output;
+                    expert weights packed by moe_pack_mxfp8_weights; the
+                    GEMM operands (token rows, expert weights, SwiGLU rows)
+                    are MXFP8, accumulation fp32 (see moe_forward)          */
 } moe_dtype;
 
 /* Shape of one MoE layer call. */
@@ -245,6 +249,16 @@ size_t moe_forward_workspace_bytes(const moe_shape* shape);
  * 256 for bf16), 16-byte aligned arrays, and each of A, one expert's weight
  * matrix and the workspace's SwiGLU rows under 2 GiB (else
  * MOE_ERR_UNSUPPORTED).
+ *
+ * dtype MOE_MXFP8: A is bf16; W_up, W_gate, W_down (and Ws_*) point to
+ * weights packed by moe_pack_mxfp8_weights ([E][H][D], [E][H][D], [E][D][H];
+ * the shared expert's [H][Ds], [H][Ds], [Ds][H] packed with E = 1). Each
+ * token row is quantised to MXFP8 along H, each SwiGLU row (computed in
+ * fp32 from the fp32 accumulators) along D, by the rule above; products of
+ * the MXFP8 values accumulate in fp32; the combine and O are as in bf16
+ * mode. Requires H, D, D_shared multiples of 128, block_size 64, 128 or 256,
+ * and none of the MOE_COMBINE_ATOMIC, MOE_SCHED_QUOTA, MOE_FUSED_LAUNCH flags
+ * (else MOE_ERR_UNSUPPORTED).
  */
 moe_status moe_forward(const moe_shape* shape, const void* A, const void* W_up,
                        const void* W_gate, const void* W_down, const void* Ws_up,
@@ -280,15 +294,55 @@ moe_status moe_forward_noalloc(const moe_shape* shape, const void* A, const void
                                const int32_t* expert_ids, const int32_t* num_tokens_post_padded,
                                void* O, void* stream);
 
+/*
+ * MXFP8 expert weights (the Mixture-of-Kittens page names MXFP8 as the
+ * low-precision format of its MoE kernels; the format is the OCP
+ * Microscaling specification's): FP8 E4M3 elements (1 sign, 4 exponent bits
+ * of bias 7, 3 mantissa bits; largest magnitude 448) in blocks of 32
+ * consecutive values along the reduction dimension, each block sharing an
+ * E8M0 scale byte x standing for 2^(x - 127). A block of values v is
+ * quantised to the scale 2^e, e = floor(log2 max |v|) - 8 clamped to
+ * [-127, 127] (e = -127 for an all-zero block), and the elements v / 2^e
+ * rounded to the nearest E4M3 value, ties to the even code, magnitudes past
+ * 448 saturating to 448 (a zero result keeps the sign of v).
+ *
+ * moe_pack_mxfp8_weights quantises a bf16 weight tensor W [E][K][N] (the
+ * layer's layouts: W_up, W_gate [E][H][D] with K = H, N = D; W_down
+ * [E][D][H] with K = D, N = H; a shared expert's as E = 1) along K and
+ * writes it into `packed` (moe_mxfp8_weight_bytes(E, K, N) bytes, device
+ * memory, 16-byte aligned) in the stage-blocked layout the MXFP8 GEMMs
+ * stream: for expert e, n-tile j (columns 128 j .. 128 j + 127), stage s (K
+ * values 64 s .. 64 s + 63), the 8448-byte block at ((e (N/128) + j) (K/64)
+ * + s) * 8448 holds column c's 64 codes at 64 c (K ascending) and its two
+ * scales (K blocks 2 s and 2 s + 1) at 8192 + 2 c. Requires K % 64 == 0,
+ * N % 128 == 0 (else MOE_ERR_UNSUPPORTED). Enqueued on `stream`; a one-time
+ * step (for example at weight load), not part of moe_forward.
+ */
+size_t moe_mxfp8_weight_bytes(int64_t E, int64_t K, int64_t N);  /* 0 if unsupported */
+moe_status moe_pack_mxfp8_weights(const void* W, int64_t E, int64_t K, int64_t N, void* packed,
+                                  void* stream);
+
+/*
+ * The same quantisation on the rows of a plain matrix X [R][K] (dtype
+ * MOE_BF16 or MOE_F32; K % 32 == 0): codes [R][K] (E4M3 bytes) and scales
+ * [R][K/32] (E8M0 bytes), row-major. moe_forward quantises the token rows
+ * and the SwiGLU rows of an MXFP8 layer with exactly this rule (into its own
+ * blocked layout in the workspace); this call exposes it on its own, for
+ * callers and for checking it.
+ */
+moe_status moe_quantize_mxfp8(const void* X, int64_t R, int64_t K, int32_t dtype, uint8_t* codes,
+                              uint8_t* scales, void* stream);
+
 /* Static, never-NULL text for a status code. */
 const char* moe_status_string(moe_status status);
 
 /*
  * Per-stage timing of moe_forward (measurement aid, not part of the layer).
  * stages are 0 = setup, 1 = up/gate GEMM, 2 = down GEMM, 3 = combine /
- * output cast. After moe_profile_enable(stage_mask) with bit s of stage_mask
- * set, each moe_forward call records a pair of HIP events on its stream around
- * the kernel of stage s; stage_mask 0 turns timing off, a mask outside 0..15
+ * output cast, 4 = the MXFP8 token-row quantisation. After
+ * moe_profile_enable(stage_mask) with bit s of stage_mask set, each
+ * moe_forward call records a pair of HIP events on its stream around the
+ * kernel of stage s; stage_mask 0 turns timing off, a mask outside 0..31
  * returns MOE_ERR_INVALID_ARGUMENT. Each recorded pair adds two marker packets
  * to the stream, so time only the stages you need. moe_profile_collect
  * waits for those events, adds each stage's elapsed milliseconds to

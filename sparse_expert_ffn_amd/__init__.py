@@ -14,7 +14,8 @@ from __future__ import annotations
 import ctypes
 import os
 
-__all__ = ["MOE_F32", "MOE_BF16", "MoeError", "moe_shape", "make_shape", "load_library",
+__all__ = ["MOE_F32", "MOE_BF16", "MOE_MXFP8", "moe_mxfp8_weight_bytes", "moe_pack_mxfp8_weights",
+           "moe_quantize_mxfp8", "MoeError", "moe_shape", "make_shape", "load_library",
            "moe_gate_workspace_bytes", "moe_gate_topk", "moe_align_workspace_bytes",
            "moe_align_block_size",
            "moe_forward_workspace_bytes", "moe_forward", "moe_status_string",
@@ -30,6 +31,7 @@ LIB_PATH = os.environ.get("SPARSE_EXPERT_FFN_LIB") or os.path.join(
 
 MOE_F32 = 0
 MOE_BF16 = 1
+MOE_MXFP8 = 2  # MXFP8 expert GEMMs (bf16 activations, packed MXFP8 expert weights)
 MOE_OUTPUT_F32 = 1
 MOE_COMBINE_ATOMIC = 2
 MOE_SCHED_QUOTA = 4  # ablation baseline: static per-expert workgroup quota
@@ -48,7 +50,8 @@ EXPORTS = ("moe_gate_workspace_bytes", "moe_gate_topk", "moe_align_workspace_byt
            "moe_align_block_size",
            "moe_forward_workspace_bytes", "moe_forward", "moe_status_string",
            "moe_profile_enable", "moe_profile_collect", "moe_device_query", "moe_trace_attach",
-           "moe_forward_noalloc")
+           "moe_forward_noalloc", "moe_mxfp8_weight_bytes", "moe_pack_mxfp8_weights",
+           "moe_quantize_mxfp8")
 
 
 class MoeError(RuntimeError):
@@ -120,6 +123,12 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.moe_trace_attach.argtypes = [vp, sz]
     lib.moe_forward_noalloc.argtypes = [sp] + [vp] * 13
     lib.moe_forward_noalloc.restype = ctypes.c_int
+    lib.moe_mxfp8_weight_bytes.argtypes = [i64, i64, i64]
+    lib.moe_mxfp8_weight_bytes.restype = sz
+    lib.moe_pack_mxfp8_weights.argtypes = [vp, i64, i64, i64, vp, vp]
+    lib.moe_pack_mxfp8_weights.restype = ctypes.c_int
+    lib.moe_quantize_mxfp8.argtypes = [vp, i64, i64, ctypes.c_int32, vp, vp, vp]
+    lib.moe_quantize_mxfp8.restype = ctypes.c_int
     for name in ("moe_gate_topk", "moe_align_block_size", "moe_forward", "moe_profile_enable",
                  "moe_profile_collect", "moe_device_query", "moe_trace_attach"):
         getattr(lib, name).restype = ctypes.c_int
@@ -236,14 +245,44 @@ def moe_forward_noalloc(shape, A, W_up, W_gate, W_down, Ws_up, Ws_gate, Ws_down,
     return code
 
 
-def moe_profile_enable(enable: bool, stages=(0, 1, 2, 3)) -> None:
+def moe_mxfp8_weight_bytes(E: int, K: int, N: int) -> int:
+    """Bytes of a weight tensor [E][K][N] packed for the MXFP8 GEMMs."""
+    return int(load_library().moe_mxfp8_weight_bytes(E, K, N))
+
+
+def moe_pack_mxfp8_weights(W, packed, stream=None, check=True) -> int:
+    """Quantise a bf16 weight tensor W [E][K][N] (device) along K to MXFP8
+    into ``packed`` (moe_mxfp8_weight_bytes(E, K, N) device bytes)."""
+    E, K, N = (1,) + tuple(W.shape) if W.dim() == 2 else tuple(W.shape)
+    code = load_library().moe_pack_mxfp8_weights(_addr(W), E, K, N, _addr(packed),
+                                                 _stream(stream))
+    if check:
+        _check("moe_pack_mxfp8_weights", code)
+    return code
+
+
+def moe_quantize_mxfp8(X, codes, scales, stream=None, check=True) -> int:
+    """MXFP8 codes [R][K] and scales [R][K/32] of the rows of X [R][K]
+    (bf16 or fp32 device tensor)."""
+    import torch
+    R, K = X.shape
+    dt = MOE_BF16 if X.dtype == torch.bfloat16 else MOE_F32
+    code = load_library().moe_quantize_mxfp8(_addr(X), R, K, dt, _addr(codes), _addr(scales),
+                                             _stream(stream))
+    if check:
+        _check("moe_quantize_mxfp8", code)
+    return code
+
+
+def moe_profile_enable(enable: bool, stages=(0, 1, 2, 3, 4)) -> None:
     """Time the given moe_forward stages (0 setup, 1 up/gate, 2 down, 3
-    combine) with HIP events on the call's stream, or stop timing."""
+    combine, 4 MXFP8 token-row quantisation) with HIP events on the call's
+    stream, or stop timing."""
     mask = sum(1 << s for s in set(stages)) if enable else 0
     _check("moe_profile_enable", load_library().moe_profile_enable(mask))
 
 
-def moe_profile_collect(n_stages: int = 4):
+def moe_profile_collect(n_stages: int = 5):
     """(per-stage milliseconds summed over recorded calls, number of calls)."""
     buf = (ctypes.c_float * n_stages)()
     n = ctypes.c_int(0)

@@ -25,7 +25,8 @@ moe_status check_routing_dims(const moe_shape* s) {
   if (s == nullptr) return MOE_ERR_INVALID_ARGUMENT;
   if ((s->flags & ~(MOE_OUTPUT_F32 | MOE_COMBINE_ATOMIC | MOE_SCHED_QUOTA | MOE_FUSED_LAUNCH)) != 0)
     return MOE_ERR_INVALID_ARGUMENT;
-  if (s->dtype != MOE_F32 && s->dtype != MOE_BF16) return MOE_ERR_INVALID_ARGUMENT;
+  if (s->dtype != MOE_F32 && s->dtype != MOE_BF16 && s->dtype != MOE_MXFP8)
+    return MOE_ERR_INVALID_ARGUMENT;
   if (s->S < 0 || s->E < 1 || s->k < 1 || s->k > s->E) return MOE_ERR_INVALID_ARGUMENT;
   if (s->E > kMaxE || s->k > kMaxK) return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
@@ -42,11 +43,37 @@ moe_status check_align_dims(const moe_shape* s) {
   return MOE_OK;
 }
 
+// Bytes of a stage-blocked MXFP8 matrix of `rows` rows and K columns
+// (64 code bytes and 2 scale bytes per row and stage of 64 K values).
+int64_t mx_blocked_bytes(int64_t rows, int64_t K) { return rows * (K / 64) * 66; }
+
+// MXFP8 forward: H, D, D_shared multiples of 128 (whole n-tiles and K
+// stages), 64/128/256-row blocks, the slot combine, two launches.
+moe_status check_mx_forward_dims(const moe_shape* s) {
+  if (s->H % 128 || s->D % 128 || s->D_shared % 128) return MOE_ERR_UNSUPPORTED;
+  if (s->block_size != 64 && s->block_size != 128 && s->block_size != 256)
+    return MOE_ERR_UNSUPPORTED;
+  if (s->flags & (MOE_COMBINE_ATOMIC | MOE_SCHED_QUOTA | MOE_FUSED_LAUNCH))
+    return MOE_ERR_UNSUPPORTED;
+  const int64_t BM = s->block_size;
+  const int64_t cap_rows = (s->S * s->k + s->E * (BM - 1) + BM - 1) / BM * BM;
+  const int64_t s_rows = (s->S + BM - 1) / BM * BM;
+  if (!fits_buffer(mx_blocked_bytes(cap_rows, s->H)) || !fits_buffer(mx_blocked_bytes(s_rows, s->H)) ||
+      !fits_buffer(mx_blocked_bytes(cap_rows, s->D)) ||
+      !fits_buffer(mx_blocked_bytes(s_rows, s->D_shared)) ||
+      !fits_buffer(mx_blocked_bytes(s->D, s->H)) || !fits_buffer(mx_blocked_bytes(s->H, s->D)) ||
+      !fits_buffer(mx_blocked_bytes(s->D_shared, s->H)) ||
+      !fits_buffer(mx_blocked_bytes(s->H, s->D_shared)))
+    return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
 moe_status check_forward_dims(const moe_shape* s) {
   moe_status st = check_align_dims(s);
   if (st != MOE_OK) return st;
   if (s->H < 1 || s->D < 1 || s->D_shared < 0) return MOE_ERR_INVALID_ARGUMENT;
   if (s->H % 8 || s->D % 8 || s->D_shared % 8) return MOE_ERR_UNSUPPORTED;
+  if (s->dtype == MOE_MXFP8) return check_mx_forward_dims(s);
   if (!forward_lds_ok(s->dtype, s->block_size)) return MOE_ERR_UNSUPPORTED;
   if ((s->flags & MOE_FUSED_LAUNCH) &&
       (s->dtype != MOE_BF16 || (s->flags & MOE_SCHED_QUOTA)))
@@ -79,13 +106,13 @@ AlignLayout align_layout(const moe_shape* s) {
 }
 
 bool out_bf16(const moe_shape* s) {
-  return s->dtype == MOE_BF16 && (s->flags & MOE_OUTPUT_F32) == 0;
+  return s->dtype != MOE_F32 && (s->flags & MOE_OUTPUT_F32) == 0;
 }
 
 bool atomic_combine(const moe_shape* s) { return (s->flags & MOE_COMBINE_ATOMIC) != 0; }
 
 struct ForwardLayout {
-  size_t counters, ready, oacc, y, ys, kept, h, hs, total;
+  size_t counters, ready, oacc, y, ys, kept, h, hs, a_blk, as_blk, total;
   int64_t n_ready;
 };
 
@@ -110,8 +137,19 @@ ForwardLayout forward_layout(const moe_shape* s) {
   const size_t ys_bytes = (atom || s->D_shared == 0) ? 0 : (size_t)s->S * s->H * sizeof(float);
   L.kept = L.ys + round_up(ys_bytes, kAlignUp);
   L.h = L.kept + round_up(atom ? 0 : (size_t)F, kAlignUp);
+  if (s->dtype == MOE_MXFP8) {
+    // stage-blocked quantised rows: h and hs, then the activation rows the
+    // GEMMs read (routed in sorted order, shared in token order)
+    L.hs = L.h + round_up((size_t)mx_blocked_bytes(cap_rows, s->D), kAlignUp);
+    L.a_blk = L.hs + round_up((size_t)mx_blocked_bytes(s_rows, s->D_shared), kAlignUp);
+    L.as_blk = L.a_blk + round_up((size_t)mx_blocked_bytes(cap_rows, s->H), kAlignUp);
+    L.total = L.as_blk +
+              round_up(s->D_shared > 0 ? (size_t)mx_blocked_bytes(s_rows, s->H) : 0, kAlignUp);
+    return L;
+  }
   L.hs = L.h + round_up((size_t)cap_rows * s->D * es, kAlignUp);
   L.total = L.hs + round_up((size_t)s_rows * s->D_shared * es, kAlignUp);
+  L.a_blk = L.as_blk = L.total;
   return L;
 }
 
@@ -260,6 +298,8 @@ moe_status forward_impl(const moe_shape* shape, const void* A, const void* W_up,
   p.Ds = shape->D_shared;
   p.F = shape->S * shape->k;
   p.grid = 0;
+  p.a_blk = ws + L.a_blk;
+  p.as_blk = ws + L.as_blk;
   p.trace = g_trace;
   p.trace_cap = g_trace_cap;
   // bf16 h in 32-column slabs per block (the down kernel's K stages then read
@@ -277,7 +317,19 @@ moe_status forward_impl(const moe_shape* shape, const void* A, const void* W_up,
   };
   if (run_stage(0, hs, [&] { return launch_forward_setup(p, hs); }) != hipSuccess)
     return MOE_ERR_HIP;
-  if (p.fused) {
+  if (dt == MOE_MXFP8) {
+    // activation rows quantised into the stage-blocked layout the GEMMs read,
+    // then the two MXFP8 GEMMs
+    const int64_t cap_rows = (p.F + p.E * (BM - 1) + BM - 1) / BM * BM;
+    const int64_t s_rows = p.Ds > 0 ? (p.S + BM - 1) / BM * BM : 0;
+    if (run_stage(4, hs, [&] { return launch_mx_gather(p, BM, cap_rows, s_rows, hs); }) !=
+        hipSuccess)
+      return MOE_ERR_HIP;
+    if (run_stage(1, hs, [&] { return launch_forward_mx(p, BM, true, hs); }) != hipSuccess)
+      return MOE_ERR_HIP;
+    if (run_stage(2, hs, [&] { return launch_forward_mx(p, BM, false, hs); }) != hipSuccess)
+      return MOE_ERR_HIP;
+  } else if (p.fused) {
     if (run_stage(1, hs, [&] { return launch_forward_fused(p, BM, hs); }) != hipSuccess)
       return MOE_ERR_HIP;
   } else {
@@ -313,7 +365,8 @@ const char* moe_status_string(moe_status status) {
 
 size_t moe_gate_workspace_bytes(const moe_shape* shape) {
   if (check_routing_dims(shape) != MOE_OK) return 0;
-  const GateSplit g = gate_split_plan(shape->S, shape->H, shape->E, shape->dtype);
+  const GateSplit g = gate_split_plan(shape->S, shape->H, shape->E,
+                                      shape->dtype == MOE_MXFP8 ? MOE_BF16 : shape->dtype);
   if (g.splits < 2) return 0;
   return round_up((size_t)g.splits * shape->S * shape->E * sizeof(float), kAlignUp);
 }
@@ -328,11 +381,13 @@ moe_status moe_gate_topk(const moe_shape* shape, const void* A, const void* W_ro
   if (shape->S == 0) return MOE_OK;
   if (topk_ids == nullptr || topk_weights == nullptr) return MOE_ERR_INVALID_ARGUMENT;
   const float* G = logits_in;
+  // the MXFP8 layer's activations and router weights are bf16
+  const int gdt = shape->dtype == MOE_MXFP8 ? MOE_BF16 : shape->dtype;
   if (logits_in == nullptr) {
     if (A == nullptr || W_router == nullptr || logits_out == nullptr) return MOE_ERR_INVALID_ARGUMENT;
     if (shape->H < 1) return MOE_ERR_INVALID_ARGUMENT;
     if (shape->H % 8 || !aligned16(A) || !aligned16(W_router)) return MOE_ERR_UNSUPPORTED;
-    const int64_t es = shape->dtype == MOE_BF16 ? 2 : 4;
+    const int64_t es = gdt == MOE_BF16 ? 2 : 4;
     if (!fits_buffer(shape->S * shape->H * es) || !fits_buffer(shape->H * shape->E * es))
       return MOE_ERR_UNSUPPORTED;
     G = logits_out;
@@ -341,7 +396,7 @@ moe_status moe_gate_topk(const moe_shape* shape, const void* A, const void* W_ro
   TopkParams tp{G, topk_ids, topk_weights, shape->S, shape->E, shape->k, shape->renormalize};
   if (logits_in == nullptr) {
     GateParams gp{A, W_router, router_bias, logits_out, shape->S, shape->H, shape->E};
-    const GateSplit plan = gate_split_plan(shape->S, shape->H, shape->E, shape->dtype);
+    const GateSplit plan = gate_split_plan(shape->S, shape->H, shape->E, gdt);
     if (plan.splits >= 2) {  // H split: partial scores, then sum + routing
       if (workspace == nullptr || workspace_bytes < moe_gate_workspace_bytes(shape))
         return MOE_ERR_WORKSPACE_TOO_SMALL;
@@ -350,9 +405,9 @@ moe_status moe_gate_topk(const moe_shape* shape, const void* A, const void* W_ro
                  ? MOE_OK
                  : MOE_ERR_HIP;
     }
-    if (gate_topk_fusable(gp, shape->dtype))  // one kernel: scores and routing
+    if (gate_topk_fusable(gp, gdt))  // one kernel: scores and routing
       return launch_gate_topk(gp, tp, hs) == hipSuccess ? MOE_OK : MOE_ERR_HIP;
-    if (launch_gate(gp, shape->dtype, hs) != hipSuccess) return MOE_ERR_HIP;
+    if (launch_gate(gp, gdt, hs) != hipSuccess) return MOE_ERR_HIP;
   } else if (logits_out != nullptr && logits_out != logits_in) {
     if (hipMemcpyAsync(logits_out, logits_in, (size_t)shape->S * shape->E * sizeof(float),
                        hipMemcpyDeviceToDevice, hs) != hipSuccess)
@@ -435,6 +490,34 @@ moe_status moe_forward_noalloc(const moe_shape* shape, const void* A, const void
 }
 
 
+size_t moe_mxfp8_weight_bytes(int64_t E, int64_t K, int64_t N) {
+  if (E < 1 || K < 64 || N < 128 || K % 64 || N % 128) return 0;
+  return (size_t)(E * mx_blocked_bytes(N, K));
+}
+
+moe_status moe_pack_mxfp8_weights(const void* W, int64_t E, int64_t K, int64_t N, void* packed,
+                                  void* stream) {
+  if (W == nullptr || packed == nullptr) return MOE_ERR_INVALID_ARGUMENT;
+  if (E < 1 || K < 1 || N < 1) return MOE_ERR_INVALID_ARGUMENT;
+  if (K % 64 || N % 128 || !aligned16(W) || !aligned16(packed)) return MOE_ERR_UNSUPPORTED;
+  return launch_mx_pack_weights(W, E, K, N, packed, reinterpret_cast<hipStream_t>(stream)) ==
+                 hipSuccess
+             ? MOE_OK
+             : MOE_ERR_HIP;
+}
+
+moe_status moe_quantize_mxfp8(const void* X, int64_t R, int64_t K, int32_t dtype, uint8_t* codes,
+                              uint8_t* scales, void* stream) {
+  if (R < 0 || K < 1 || (dtype != MOE_F32 && dtype != MOE_BF16)) return MOE_ERR_INVALID_ARGUMENT;
+  if (R == 0) return MOE_OK;
+  if (X == nullptr || codes == nullptr || scales == nullptr) return MOE_ERR_INVALID_ARGUMENT;
+  if (K % 32 || !aligned16(X) || !aligned16(codes)) return MOE_ERR_UNSUPPORTED;
+  return launch_mx_quantize_rows(X, dtype, R, K, codes, scales,
+                                 reinterpret_cast<hipStream_t>(stream)) == hipSuccess
+             ? MOE_OK
+             : MOE_ERR_HIP;
+}
+
 moe_status moe_trace_attach(void* buffer, size_t bytes) {
   if (!MOE_TRACE) return MOE_ERR_UNSUPPORTED;
   if (buffer == nullptr) {
@@ -471,7 +554,7 @@ moe_status moe_device_query(int* cu_count, int* max_clock_khz, char* name, size_
 }
 
 moe_status moe_profile_enable(int stage_mask) {
-  if (stage_mask < 0 || stage_mask > 15) return MOE_ERR_INVALID_ARGUMENT;
+  if (stage_mask < 0 || stage_mask > 31) return MOE_ERR_INVALID_ARGUMENT;
   std::lock_guard<std::mutex> lk(g_prof_mu);
   g_prof_on = stage_mask != 0;
   g_prof_mask = (unsigned)stage_mask;

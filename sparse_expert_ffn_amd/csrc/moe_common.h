@@ -122,6 +122,8 @@ struct ForwardParams {
   int fused;              // 1: up/gate and down in one launch (bf16)
   int slots_nt;           // 1: the slot rows Y / Ys are written and read with the
                           // non-temporal hint (they far exceed the MALL)
+  void* a_blk;            // MXFP8: stage-blocked quantised rows of the routed m-blocks
+  void* as_blk;           // MXFP8: the same for the shared expert's m-blocks
   void* trace;            // per-task timing records (libraries built with MOE_TRACE), or null
   int64_t trace_cap;      // records that fit the trace buffer
 };
@@ -177,5 +179,13 @@ hipError_t launch_forward_fused(const ForwardParams& p, int BM, hipStream_t st);
 hipError_t launch_forward_finalize(const ForwardParams& p, hipStream_t st);
 hipError_t launch_forward_combine(const ForwardParams& p, hipStream_t st);
 int forward_lds_ok(int dtype, int BM);
+// MXFP8 mode (moe_mx.hip)
+hipError_t launch_mx_quantize_rows(const void* X, int dtype, int64_t R, int64_t K, uint8_t* codes,
+                                   uint8_t* scales, hipStream_t st);
+hipError_t launch_mx_pack_weights(const void* W, int64_t E, int64_t K, int64_t N, void* packed,
+                                  hipStream_t st);
+hipError_t launch_mx_gather(const ForwardParams& p, int BM, int64_t cap_rows, int64_t s_rows,
+                            hipStream_t st);
+hipError_t launch_forward_mx(const ForwardParams& p, int BM, bool up, hipStream_t st);
 
 }  // namespace moe

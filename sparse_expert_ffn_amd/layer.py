@@ -8,7 +8,7 @@ from __future__ import annotations
 
 import torch
 
-from . import (MOE_BF16, make_shape, moe_align_block_size, moe_align_workspace_bytes,
+from . import (MOE_BF16, MOE_F32, MOE_MXFP8, make_shape, moe_align_block_size, moe_align_workspace_bytes,
                moe_forward, moe_forward_workspace_bytes, moe_gate_topk, moe_gate_workspace_bytes)
 
 
@@ -18,7 +18,7 @@ class MoEBuffers:
                  fused_launch=False, device="cuda"):
         self.shape = make_shape(S, H, D, E, k, D_shared, capacity, block_size, renormalize,
                                 dtype, out_f32, atomic_combine, sched_quota, fused_launch)
-        self.tdtype = torch.bfloat16 if dtype == MOE_BF16 and not out_f32 else torch.float32
+        self.tdtype = torch.bfloat16 if dtype != MOE_F32 and not out_f32 else torch.float32
         dev = torch.device(device)
         cap = S * k + E * (block_size - 1)
         i32, f32 = torch.int32, torch.float32
@@ -64,13 +64,15 @@ def suggest_block_size(S: int, k: int, E: int, capacity: int = 0, dtype: int = 1
     expert's rows costs little more than their own work and streams that
     expert's weights once: pick the smallest block that holds the expected
     largest expert, taken as 1.25x the mean rows per expert, or the
-    capacity when that is smaller (no expert keeps more). 256 for bf16 only."""
+    capacity when that is smaller (no expert keeps more). 256 for bf16 and
+    MXFP8 only; MXFP8 takes 64 at least."""
     mean = S * k / max(E, 1)
     want = 1.25 * mean
     if capacity > 0:
         want = min(want, capacity)
-    top = 256 if dtype == 1 else 128
-    for bm in (16, 32, 64, 128, 256):
+    top = 256 if dtype != MOE_F32 else 128
+    # the MXFP8 tiles come in 64, 128 and 256 rows
+    for bm in ((64, 128, 256) if dtype == MOE_MXFP8 else (16, 32, 64, 128, 256)):
         if bm >= want or bm == top:
             return bm
     return top

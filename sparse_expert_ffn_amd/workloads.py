@@ -56,6 +56,7 @@ class Workload:
     zipf_s: float = 1.2
     renormalize: int = 1
     seed: int = 0
+    mxfp8: bool = False         # expert GEMMs in MXFP8 (inputs still drawn in bf16)
 
     @property
     def capacity(self) -> int:
@@ -76,7 +77,7 @@ class Workload:
         return {"workload": self.name, "S": self.S, "H": self.H, "D": self.D,
                 "E": self.E, "k": self.k, "D_shared": self.D_shared,
                 "capacity": self.capacity,
-                "dtype": "f32" if self.dtype == F32 else "bf16"}
+                "dtype": "f32" if self.dtype == F32 else ("mxfp8" if self.mxfp8 else "bf16")}
 
 
 WORKLOADS = {
@@ -91,6 +92,11 @@ WORKLOADS = {
     "dsv3": Workload("dsv3", S=4096, H=7168, D=2048, E=256, k=8, dtype=BF16,
                      D_shared=2048, router_std=1.0 / math.sqrt(7168)),
 }
+# The same layers with MXFP8 expert GEMMs (the Mixture-of-Kittens page's
+# low-precision format): identical inputs, the expert weights and the GEMM
+# operands quantised to MXFP8.
+for _n in ("prefill_bal", "prefill_skew", "decode", "dsv3"):
+    WORKLOADS[_n + "_mxfp8"] = dataclasses.replace(WORKLOADS[_n], name=_n + "_mxfp8", mxfp8=True)
 
 
 def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:

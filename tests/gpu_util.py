@@ -90,21 +90,39 @@ def bf16_output_excess(g16, o):
     return float(np.max(np.abs(g16 - o) / bound))
 
 
+def lib_dtype(wl):
+    """The C-ABI dtype of a workload: MOE_MXFP8 for its MXFP8 form."""
+    return moe.MOE_MXFP8 if wl.mxfp8 else wl.dtype
+
+
 def block_size_for(wl):
-    return suggest_block_size(wl.S, wl.k, wl.E, wl.capacity, wl.dtype)
+    return suggest_block_size(wl.S, wl.k, wl.E, wl.capacity, lib_dtype(wl))
 
 
 def buffers(wl, block_size=None, out_f32=False, atomic_combine=False, sched_quota=False,
             fused_launch=False):
     bm = block_size or block_size_for(wl)
     return MoEBuffers(wl.S, wl.H, wl.D, wl.E, wl.k, wl.D_shared, wl.capacity, bm,
-                      wl.renormalize, wl.dtype, out_f32=out_f32,
+                      wl.renormalize, lib_dtype(wl), out_f32=out_f32,
                       atomic_combine=atomic_combine, sched_quota=sched_quota,
                       fused_launch=fused_launch, device=DEV)
 
 
+def pack_mxfp8(W):
+    """A bf16 device weight tensor [E][K][N] (or [K][N]) packed for the
+    MXFP8 GEMMs by the library."""
+    if W is None:
+        return None
+    E, K, N = (1,) + tuple(W.shape) if W.dim() == 2 else tuple(W.shape)
+    packed = torch.empty(moe.moe_mxfp8_weight_bytes(E, K, N), dtype=torch.uint8,
+                         device=W.device)
+    moe.moe_pack_mxfp8_weights(W, packed)
+    return packed
+
+
 class DeviceLayer:
-    """Every input of a layer on the device (weights streamed per expert)."""
+    """Every input of a layer on the device (weights streamed per expert).
+    For an MXFP8 workload the expert weights are packed on the device."""
 
     def __init__(self, wl, li=None):
         self.wl = wl
@@ -114,12 +132,11 @@ class DeviceLayer:
         self.A = dev(li.A)
         self.Wr = dev(li.Wr)
         self.bias = dev(li.bias)
-        self.W_up = dev(li.W_up)
-        self.W_gate = dev(li.W_gate)
-        self.W_down = dev(li.W_down)
-        self.Ws_up = dev(li.Ws_up)
-        self.Ws_gate = dev(li.Ws_gate)
-        self.Ws_down = dev(li.Ws_down)
+        ws = [dev(x) for x in (li.W_up, li.W_gate, li.W_down, li.Ws_up, li.Ws_gate, li.Ws_down)]
+        if wl.mxfp8:
+            ws = [pack_mxfp8(w) for w in ws]
+        (self.W_up, self.W_gate, self.W_down, self.Ws_up, self.Ws_gate,
+         self.Ws_down) = ws
 
     def forward(self, buf):
         return buf.forward(self.A, self.W_up, self.W_gate, self.W_down, self.Ws_up,

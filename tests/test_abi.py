@@ -25,7 +25,7 @@ def lib():
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_exports_every_declared_symbol(lib):
@@ -202,3 +202,31 @@ def test_noalloc_validation(lib):
     assert f(shape(k=9)) == 1
     assert f(shape(block_size=48)) == 2
     assert macros  # header parsed
+
+
+def test_mxfp8_validation(lib):
+    """MXFP8 entry points reject bad arguments before touching the device."""
+    assert moe.moe_mxfp8_weight_bytes(64, 2048, 2048) == 64 * 16 * 32 * 8448
+    assert moe.moe_mxfp8_weight_bytes(1, 96, 128) == 0       # K not a multiple of 64
+    assert moe.moe_mxfp8_weight_bytes(1, 128, 96) == 0       # N not a multiple of 128
+    pack = lambda W, E, K, N, out: lib.moe_pack_mxfp8_weights(W, E, K, N, out, None)
+    assert pack(None, 1, 128, 128, FAKE) == 1
+    assert pack(FAKE, 0, 128, 128, FAKE) == 1
+    assert pack(FAKE, 1, 96, 128, FAKE) == 2
+    assert pack(FAKE, 1, 128, 128, FAKE + 8) == 2             # misaligned
+    q = lambda X, R, K, dt, c, s: lib.moe_quantize_mxfp8(X, R, K, dt, c, s, None)
+    assert q(FAKE, 4, 64, 7, FAKE, FAKE) == 1                 # dtype
+    assert q(FAKE, 4, 48, moe.MOE_BF16, FAKE, FAKE) == 2      # K % 32
+    assert q(None, 4, 64, moe.MOE_BF16, FAKE, FAKE) == 1
+    assert q(None, 0, 64, moe.MOE_BF16, None, None) == 0      # empty
+    # the MXFP8 forward's shape rules
+    ok = shape(S=64, H=256, D=384, E=8, k=2, block_size=64, dtype=moe.MOE_MXFP8)
+    assert moe.moe_forward_workspace_bytes(ok) > 0
+    for bad in (dict(H=200), dict(D=200), dict(block_size=32), dict(block_size=16)):
+        s = shape(**dict(dict(S=64, H=256, D=384, E=8, k=2, block_size=64,
+                              dtype=moe.MOE_MXFP8), **bad))
+        assert moe.moe_forward_workspace_bytes(s) == 0, bad
+    for flag in ("atomic_combine", "sched_quota", "fused_launch"):
+        s = moe.make_shape(64, 256, 384, 8, 2, block_size=64, dtype=moe.MOE_MXFP8,
+                           **{flag: True})
+        assert moe.moe_forward_workspace_bytes(s) == 0, flag

@@ -180,12 +180,14 @@ def test_scanner_follows_branches_and_back_edges():
 
 @pytest.mark.skipif(shutil.which(os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")) is None,
                     reason="hipcc not available")
+@pytest.mark.parametrize("source", ["moe_gemm.hip", "moe_mx.hip"])
 @pytest.mark.parametrize("variant", ["plain", "trace"])
-def test_gemm_kernels_have_no_valu_sgpr_hazard(tmp_path, variant):
-    """Both library builds: the plain one and the one with timing records."""
+def test_gemm_kernels_have_no_valu_sgpr_hazard(tmp_path, variant, source):
+    """Every source with LDS-direct loads, in both library builds: the plain
+    one and the one with timing records."""
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-    src = os.path.join(buildlib.PKG, "csrc", "moe_gemm.hip")
-    out = tmp_path / "moe_gemm.s"
+    src = os.path.join(buildlib.PKG, "csrc", source)
+    out = tmp_path / "kernels.s"
     flags = [f for f in buildlib.HIPCC_FLAGS if f not in ("-shared", "-fPIC")]
     if variant == "trace":
         flags += buildlib.TRACE_FLAGS
