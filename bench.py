@@ -42,9 +42,10 @@ def parse():
     ap.add_argument("--block-size", type=int, default=0)
     ap.add_argument("--tokens", type=int, default=0,
                     help="override the workload's token count S (capacity recomputed)")
-    ap.add_argument("--sched", choices=("queue", "quota"), default="queue",
-                    help="grouped-GEMM scheduler: per-XCD atomic task queues (default) or "
-                         "the static per-expert workgroup quota (ablation baseline)")
+    ap.add_argument("--sched", choices=("queue", "batch", "quota"), default="queue",
+                    help="grouped-GEMM scheduler: per-XCD atomic task queues (default), the "
+                         "same queues claimed 4 tasks per atomic, or the static per-expert "
+                         "workgroup quota (ablation baseline)")
     ap.add_argument("--launch", choices=("two", "one"), default="two",
                     help="the expert GEMMs as two persistent launches (up/gate, then down) "
                          "or as one (down tasks wait per m-block for its up/gate tasks)")
@@ -240,7 +241,8 @@ def setup_workload(wl, args, torch, moe, dev="cuda"):
         copies.append(tuple(None if x is None else x.clone() for x in copies[0]))
     buf = MoEBuffers(wl.S, wl.H, wl.D, wl.E, wl.k, wl.D_shared, wl.capacity, bm,
                      wl.renormalize, dtype, sched_quota=args.sched == "quota",
-                     fused_launch=args.launch == "one", device=dev)
+                     fused_launch=args.launch == "one", device=dev,
+                     extra_flags=moe.MOE_SCHED_BATCH if args.sched == "batch" else 0)
     stream = torch.cuda.current_stream()
     n_step = [0]
 

@@ -119,6 +119,18 @@ typedef struct {
  * bit, as the two-launch form. The per-stage timer then reports the one
  * kernel as stage 1 and nothing as stage 2. */
 #define MOE_FUSED_LAUNCH 8
+/* flags (not with MOE_SCHED_QUOTA or MOE_FUSED_LAUNCH, else
+ * MOE_ERR_UNSUPPORTED): batched claims, the Weave review's two-level claiming
+ * (section 5.2, pitfall 1). Each atomic on a task queue takes 4 consecutive
+ * tasks, which the workgroup then runs in turn, instead of one. Same tiles,
+ * same results; fewer atomics, coarser balance at the end of each queue. */
+#define MOE_SCHED_BATCH 16
+/* flags, for tests of the status word only (not with MOE_SCHED_QUOTA or
+ * MOE_FUSED_LAUNCH): the call does not reset the grouped GEMMs' task queue
+ * counters, which keep the values the previous call on this workspace left.
+ * The queues then hand out no tasks or too few, O is wrong, and the status
+ * word reports MOE_STATUS_TASKS_LOST. */
+#define MOE_TEST_SKIP_QUEUE_RESET 32
 
 /* The call's status word: an int32 at this byte offset of the moe_forward
  * workspace. Every moe_forward call sets it to 0 before its GEMMs run; once
@@ -134,6 +146,17 @@ typedef struct {
  *     so O holds NaN there. The two-launch path never sets it. */
 #define MOE_FORWARD_STATUS_OFFSET 128
 #define MOE_STATUS_READY_TIMEOUT 1
+/*   MOE_STATUS_TASKS_LOST: a two-launch grouped GEMM handed out fewer tasks
+ *     than its task space holds, so some output rows were never computed (its
+ *     queue counters did not start at zero; something else wrote the
+ *     workspace during the call).
+ *   MOE_STATUS_QUEUE_COUNT: a task queue counter ended at another value than
+ *     the claims of a complete run leave (batch x (successful atomics + one
+ *     failed atomic per workgroup)).
+ * The last workgroup of each two-launch GEMM to find every queue empty makes
+ * both checks; the one-launch kernel and the quota scheduler do not. */
+#define MOE_STATUS_TASKS_LOST 2
+#define MOE_STATUS_QUEUE_COUNT 4
 
 /*
  * Gate scores and softmax top-k routing.

@@ -22,7 +22,9 @@ __all__ = ["MOE_F32", "MOE_BF16", "MOE_MXFP8", "moe_mxfp8_weight_bytes", "moe_pa
            "moe_profile_enable", "moe_profile_collect", "moe_device_query", "moe_trace_attach",
            "moe_forward_noalloc", "MOE_NOALLOC_SCRATCH_BYTES", "forward_status",
            "build",
-           "LIB_PATH", "STATUS", "MOE_FORWARD_STATUS_OFFSET", "MOE_STATUS_READY_TIMEOUT"]
+           "LIB_PATH", "STATUS", "MOE_FORWARD_STATUS_OFFSET", "MOE_STATUS_READY_TIMEOUT",
+           "MOE_STATUS_TASKS_LOST", "MOE_STATUS_QUEUE_COUNT", "MOE_SCHED_BATCH",
+           "MOE_TEST_SKIP_QUEUE_RESET"]
 
 # SPARSE_EXPERT_FFN_LIB: load the library from another path (e.g. a build
 # with different compile-time tile settings)
@@ -36,9 +38,13 @@ MOE_OUTPUT_F32 = 1
 MOE_COMBINE_ATOMIC = 2
 MOE_SCHED_QUOTA = 4  # ablation baseline: static per-expert workgroup quota
 MOE_FUSED_LAUNCH = 8  # up/gate and down GEMMs in one persistent launch (bf16)
+MOE_SCHED_BATCH = 16  # batched claims: 4 tasks per queue atomic
+MOE_TEST_SKIP_QUEUE_RESET = 32  # testing the status word: keep the previous call's queue counters
 # byte offset of the int32 status word in the moe_forward workspace, and its bits
 MOE_FORWARD_STATUS_OFFSET = 128
 MOE_STATUS_READY_TIMEOUT = 1
+MOE_STATUS_TASKS_LOST = 2
+MOE_STATUS_QUEUE_COUNT = 4
 # device array behind moe_forward_noalloc, per GPU
 MOE_NOALLOC_SCRATCH_BYTES = 64 << 20
 
@@ -74,10 +80,10 @@ class moe_shape(ctypes.Structure):
 
 def make_shape(S, H, D, E, k, D_shared=0, capacity=0, block_size=128, renormalize=1,
                dtype=MOE_BF16, out_f32=False, atomic_combine=False,
-               sched_quota=False, fused_launch=False) -> moe_shape:
+               sched_quota=False, fused_launch=False, extra_flags=0) -> moe_shape:
     flags = ((MOE_OUTPUT_F32 if out_f32 else 0) | (MOE_COMBINE_ATOMIC if atomic_combine else 0)
              | (MOE_SCHED_QUOTA if sched_quota else 0)
-             | (MOE_FUSED_LAUNCH if fused_launch else 0))
+             | (MOE_FUSED_LAUNCH if fused_launch else 0) | extra_flags)
     return moe_shape(S, H, D, E, k, D_shared, capacity, block_size, renormalize, dtype, flags)
 
 

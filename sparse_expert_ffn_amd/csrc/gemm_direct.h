@@ -33,12 +33,15 @@
 //    its own stage-kt loads, then one barrier per stage.
 #pragma once
 
+#include <type_traits>
+
 #include "gemm_tile.h"
 
 namespace moe {
 
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
 typedef int i32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 // Schedule knobs (compile time, chosen by measurement):
 //  MOE_PINGPONG   1: the two waves of each SIMD alternate between reading
@@ -53,6 +56,11 @@ typedef int i32x4_t __attribute__((ext_vector_type(4)));
 #endif
 #ifndef MOE_MFMA_PRIO
 #define MOE_MFMA_PRIO 0
+#endif
+//  MOE_MFMA32     1: the persistent GEMMs' cores (tiles of 128 rows or more
+//                 and their half tiles) use v_mfma_f32_32x32x16_bf16.
+#ifndef MOE_MFMA32
+#define MOE_MFMA32 0
 #endif
 
 // Raw buffer descriptor (gfx9): base[47:0], stride 0, num_records = bytes,
@@ -126,8 +134,23 @@ __device__ __forceinline__ void wait_vmcnt() {
 // kernels whose SGPR pressure makes the compiler restore the buffer
 // descriptors from VGPR lanes next to the loads; the asm hazard test finds
 // the sites).
+// MF: the MFMA shape, 16 (v_mfma_f32_16x16x32_bf16) or 32
+// (v_mfma_f32_32x32x16_bf16). With 32, a row block is 32 rows, a column
+// block 32 columns, and a K step 16 elements:
+//  - A operand: lane l holds row l % 32, K elements 8 (l / 32) .. +7 of the
+//    step (one ds_read_b128);
+//  - B operand: lane l holds column l % 32, the same K elements (two
+//    ds_read_b64_tr_b16: 16-lane group g addresses k-rows 8 (g / 2) + i / 4
+//    (+4 for the second read) and columns 16 (g % 2) + 4 (i % 4) .. +3);
+//  - accumulators: lane l, register r holds row 8 (r / 4) + 4 (l / 32) +
+//    r % 4, column l % 32;
+//  - B's column pairs are swizzled by ((k & 3) << 1) | ((k >> 3) & 1), so that
+//    the two column halves a read's 32 lanes address at the same k-rows, and
+//    the k-rows 8 apart, fall in different 32-byte slots.
+// Each 32-column step of K adds its products in the same order for any BM, so
+// a half tile reproduces the whole tile's sums bit for bit (for the same MF).
 template <int BM_, int NB_, int NW_ = 8, int BK_ = 64, int LDS_BUDGET = 144 * 1024,
-          bool B_STREAM = false, bool VALU_SGPR = false>
+          bool B_STREAM = false, bool VALU_SGPR = false, int MF = 16>
 struct TileGemmDirect {
   static constexpr bool DIRECT = true;  // the LDS-direct core (vs gemm_tile.h)
   static constexpr int BM = BM_, BN = 128, NB = NB_;
@@ -147,11 +170,13 @@ struct TileGemmDirect {
   static constexpr int LDS_BYTES = NSTAGE * STAGE;
   static_assert(NSTAGE >= 2, "at least two LDS stages");
   static_assert(BK == 32 || BK == 64, "stage K");
+  static_assert(MF == 16 || MF == 32, "MFMA shape");
   static constexpr int WM = BM >= 32 ? 2 : 1;
   static constexpr int WN = NW / WM;
-  static constexpr int MI = BM / WM / 16;
-  static constexpr int NI = BN / WN / 16;
-  static constexpr int KSTEPS = BK / 32;
+  static constexpr int MI = BM / WM / MF;     // row blocks per wave
+  static constexpr int NI = BN / WN / MF;     // column blocks per wave and matrix
+  static constexpr int KS = 512 / MF;         // K elements per MFMA step (32 or 16)
+  static constexpr int KSTEPS = BK / KS;
   static constexpr int ADIST = MOE_A_DIST;
   // 1 KB (one wave instruction) units per stage
   static constexpr int A_INSTR = A_LDS / 1024;
@@ -165,7 +190,9 @@ struct TileGemmDirect {
   static_assert(MI >= 1 && NI >= 1, "tile too small for the waves");
   static_assert(LDS_BYTES <= 160 * 1024, "LDS");
 
-  f32x4_t acc[NB][MI][NI];
+  using acc_t = std::conditional_t<MF == 32, f32x16_t, f32x4_t>;
+  static constexpr int ACC_N = MF == 32 ? 16 : 4;
+  acc_t acc[NB][MI][NI];
   uint32_t aoff[A_PW];   // per-lane A row byte offset + logical chunk (kOob = zero)
   uint32_t boff[B_PW];   // per-lane B offset at k-stage 0 (kOob = zero column strip)
   i32x4_t rsrc_a;
@@ -174,7 +201,12 @@ struct TileGemmDirect {
   uint32_t a_stage_bytes;  // A bytes from one K stage to the next (see setup)
   int64_t K_;
 
-  __device__ __forceinline__ static int bswz(int k) { return (k & 3) | (((k >> 3) & 1) << 2); }
+  __device__ __forceinline__ static int bswz(int k) {
+    if constexpr (MF == 32)
+      return ((k & 3) << 1) | ((k >> 3) & 1);
+    else
+      return (k & 3) | (((k >> 3) & 1) << 2);
+  }
   // A chunk swizzle (8 chunks per 128-byte row, or 4 per 64-byte row). Chosen
   // by measurement, with an LDS probe of exactly the fragment-read pattern on
   // 256 workgroups: these keys sustain 234 B/clk per CU; the keys that spread
@@ -185,6 +217,8 @@ struct TileGemmDirect {
   __device__ __forceinline__ static int aswz(int r) {
     if constexpr (ACH == 8)
       return (r >> 1) & 7;
+    else if constexpr (MF == 32)
+      return ((r >> 2) & 1) | (((r >> 3) & 1) << 1);
     else
       return ((r >> 2) & 1) << 1;
   }
@@ -195,7 +229,7 @@ struct TileGemmDirect {
 #pragma unroll
       for (int i = 0; i < MI; ++i)
 #pragma unroll
-        for (int j = 0; j < NI; ++j) acc[m][i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        for (int j = 0; j < NI; ++j) acc[m][i][j] = acc_t{};
   }
 
   // A: buffer of a_bytes at a_base, row_off(r) = byte offset of row r or kOob.
@@ -302,8 +336,10 @@ struct TileGemmDirect {
         i16x4_t h[2];
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
-          const int k = ks * 32 + 8 * lg + 4 * hh + (lr >> 2);
-          const int n = wn0 + j * 16 + 4 * (lr & 3);
+          const int k = MF == 32 ? ks * 16 + 8 * (lg >> 1) + 4 * hh + (lr >> 2)
+                                 : ks * 32 + 8 * lg + 4 * hh + (lr >> 2);
+          const int n = MF == 32 ? wn0 + j * 32 + 16 * (lg & 1) + 4 * (lr & 3)
+                                 : wn0 + j * 16 + 4 * (lr & 3);
           const int c = n >> 3;
           const int pc = ((((c >> 1) ^ bswz(k)) << 1) | (c & 1));
           const char* p = base + A_LDS + m * B_MAT + k * B_ROWB + (pc << 4) + ((n & 4) << 1);
@@ -318,8 +354,8 @@ struct TileGemmDirect {
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int wm0 = (wave / WN) * (BM / WM);
-    const int r = wm0 + i * 16 + (lane & 15);
-    const int c = ks * 4 + (lane >> 4);
+    const int r = MF == 32 ? wm0 + i * 32 + (lane & 31) : wm0 + i * 16 + (lane & 15);
+    const int c = MF == 32 ? ks * 2 + (lane >> 5) : ks * 4 + (lane >> 4);
     return *reinterpret_cast<const uint4*>(base + r * A_ROWB + ((c ^ aswz(r)) << 4));
   }
 
@@ -327,10 +363,16 @@ struct TileGemmDirect {
 #pragma unroll
     for (int m = 0; m < NB; ++m)
 #pragma unroll
-      for (int j = 0; j < NI; ++j)
-        acc[m][i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-            __builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b[m][j]), acc[m][i][j],
-            0, 0, 0);
+      for (int j = 0; j < NI; ++j) {
+        if constexpr (MF == 32)
+          acc[m][i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              __builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b[m][j]),
+              acc[m][i][j], 0, 0, 0);
+        else
+          acc[m][i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              __builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b[m][j]),
+              acc[m][i][j], 0, 0, 0);
+      }
   }
 
   // MFMAs of this wave's row blocks [LO, HI) over one stage, as straight-line
@@ -382,7 +424,7 @@ struct TileGemmDirect {
     }
   }
 
-  // Number of this wave's 16-row blocks up to the last row for which
+  // Number of this wave's row blocks (MF rows) up to the last row for which
   // valid(r) holds (r = tile row); blocks after it are padding only.
   template <typename Valid>
   __device__ __forceinline__ int active_blocks(Valid valid) const {
@@ -397,7 +439,7 @@ struct TileGemmDirect {
       const uint64_t m = __ballot(r < R && valid(wm0 + r));
       if (m) last = b + 63 - __clzll(m);
     }
-    return __builtin_amdgcn_readfirstlane((last + 16) / 16);
+    return __builtin_amdgcn_readfirstlane((last + MF) / MF);
   }
 
   // K loop over a ring of NSTAGE stage slots in one LDS array for a wave
@@ -569,18 +611,50 @@ struct TileGemmDirect {
     // this lane's first row and column, opaque to the optimiser: the row and
     // column indices are formed here rather than hoisted out of a caller's
     // task loop and held in registers through its K loop
-    int lrow = (wave / WN) * (BM / WM) + (lane >> 4) * 4;
-    int lcol = (wave % WN) * (BN / WN) + (lane & 15);
+    int lrow = (wave / WN) * (BM / WM) + (MF == 32 ? (lane >> 5) : (lane >> 4)) * 4;
+    int lcol = (wave % WN) * (BN / WN) + (lane & (MF - 1));
     asm volatile("" : "+v"(lrow), "+v"(lcol));
 #pragma unroll
     for (int m = 0; m < NB; ++m)
 #pragma unroll
-      for (int i = 0; i < MI; ++i)
+      for (int i = 0; i < MI; ++i) {
+        // one row block at a time (its row indices and addresses are not
+        // all formed ahead and held in registers)
+        if constexpr (MF == 32) __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int j = 0; j < NI; ++j)
 #pragma unroll
-          for (int r = 0; r < 4; ++r)
-            f(m, lrow + i * 16 + r, lcol + j * 16, acc[m][i][j][r]);
+          for (int r = 0; r < ACC_N; ++r)
+            f(m, lrow + i * MF + acc_row(r), lcol + j * MF, acc[m][i][j][r]);
+      }
+  }
+
+  // Row offset of accumulator register r within its block, relative to the
+  // lane's first row.
+  __device__ __forceinline__ static constexpr int acc_row(int r) {
+    return MF == 32 ? 8 * (r >> 2) + (r & 3) : r;
+  }
+
+  // f(tile row, tile column, value of matrix 0, value of matrix 1) for each
+  // element of a two-matrix tile, one row block at a time (the accumulator
+  // reads of a block are not hoisted into VGPRs ahead of the others).
+  template <typename F>
+  __device__ __forceinline__ void for_each_pair(F f) const {
+    static_assert(NB == 2, "two matrices");
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    int lrow = (wave / WN) * (BM / WM) + (MF == 32 ? (lane >> 5) : (lane >> 4)) * 4;
+    int lcol = (wave % WN) * (BN / WN) + (lane & (MF - 1));
+    asm volatile("" : "+v"(lrow), "+v"(lcol));
+#pragma unroll
+    for (int i = 0; i < MI; ++i) {
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int j = 0; j < NI; ++j)
+#pragma unroll
+        for (int r = 0; r < ACC_N; ++r)
+          f(lrow + i * MF + acc_row(r), lcol + j * MF, acc[0][i][j][r], acc[1][i][j][r]);
+    }
   }
 };
 

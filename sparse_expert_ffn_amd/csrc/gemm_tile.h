@@ -403,6 +403,27 @@ struct TileGemm {
           for (int r = 0; r < 4; ++r)
             f(m, wm0 + i * 16 + (lane >> 4) * 4 + r, wn0 + j * 16 + (lane & 15), acc[m][i][j][r]);
   }
+
+  // f(tile row, tile column, value of matrix 0, value of matrix 1) for each
+  // element of a two-matrix tile, one 16-row block at a time.
+  template <typename F>
+  __device__ __forceinline__ void for_each_pair(F f) const {
+    static_assert(NB == 2, "two matrices");
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    int lrow = (wave / WN) * (BM / WM) + (lane >> 4) * 4;
+    int lcol = (wave % WN) * (BN / WN) + (lane & 15);
+    asm volatile("" : "+v"(lrow), "+v"(lcol));
+#pragma unroll
+    for (int i = 0; i < MI; ++i) {
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int j = 0; j < NI; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          f(lrow + i * 16 + r, lcol + j * 16, acc[0][i][j][r], acc[1][i][j][r]);
+    }
+  }
 };
 
 }  // namespace moe

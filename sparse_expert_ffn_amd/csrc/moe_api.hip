@@ -23,7 +23,8 @@ bool fits_buffer(int64_t bytes) { return bytes >= 0 && bytes < ((int64_t)1 << 31
 
 moe_status check_routing_dims(const moe_shape* s) {
   if (s == nullptr) return MOE_ERR_INVALID_ARGUMENT;
-  if ((s->flags & ~(MOE_OUTPUT_F32 | MOE_COMBINE_ATOMIC | MOE_SCHED_QUOTA | MOE_FUSED_LAUNCH)) != 0)
+  if ((s->flags & ~(MOE_OUTPUT_F32 | MOE_COMBINE_ATOMIC | MOE_SCHED_QUOTA | MOE_FUSED_LAUNCH |
+                    MOE_SCHED_BATCH | MOE_TEST_SKIP_QUEUE_RESET)) != 0)
     return MOE_ERR_INVALID_ARGUMENT;
   if (s->dtype != MOE_F32 && s->dtype != MOE_BF16 && s->dtype != MOE_MXFP8)
     return MOE_ERR_INVALID_ARGUMENT;
@@ -77,6 +78,10 @@ moe_status check_forward_dims(const moe_shape* s) {
   if (!forward_lds_ok(s->dtype, s->block_size)) return MOE_ERR_UNSUPPORTED;
   if ((s->flags & MOE_FUSED_LAUNCH) &&
       (s->dtype != MOE_BF16 || (s->flags & MOE_SCHED_QUOTA)))
+    return MOE_ERR_UNSUPPORTED;
+  // batching and the queue-reset test hook act on the two-launch queues
+  if ((s->flags & (MOE_SCHED_BATCH | MOE_TEST_SKIP_QUEUE_RESET)) &&
+      (s->flags & (MOE_SCHED_QUOTA | MOE_FUSED_LAUNCH)))
     return MOE_ERR_UNSUPPORTED;
   // the kernels address A, each expert's weight matrices and the SwiGLU rows
   // through 32-bit buffer offsets: each must stay below 2 GiB
@@ -282,6 +287,8 @@ moe_status forward_impl(const moe_shape* shape, const void* A, const void* W_up,
   p.ready = reinterpret_cast<int*>(ws + L.ready);
   p.n_ready = L.n_ready;
   p.fused = (shape->flags & MOE_FUSED_LAUNCH) ? 1 : 0;
+  p.claim_batch = (shape->flags & MOE_SCHED_BATCH) ? kClaimBatch : 1;
+  p.keep_counters = (shape->flags & MOE_TEST_SKIP_QUEUE_RESET) ? 1 : 0;
   // Slot rows far larger than the 256 MB MALL (DeepSeek-V3 sizes: 0.94 GB)
   // go to HBM and come back from it anyway: the down kernel stores them and
   // the combine loads them with the non-temporal hint (measured: down -3%,

@@ -24,6 +24,15 @@ constexpr int kCounterInts = kQuotaBase + 2 * kQuotaStride;
 // (MOE_FORWARD_STATUS_OFFSET); bits as MOE_STATUS_* there.
 constexpr int kStatusWord = 32;
 constexpr int kStatusReadyTimeout = 1;
+constexpr int kStatusTasksLost = 2;
+constexpr int kStatusQueueCount = 4;
+// Queue bookkeeping of the two-launch grouped GEMMs, also in the counter
+// block: per GEMM g (0 up/gate, 1 down) the task parts handed out
+// (kDoneBase + 2 g) and the workgroups that found no task left
+// (kDoneBase + 2 g + 1).
+constexpr int kDoneBase = 16;
+// Tasks claimed per queue atomic with the batched-claims flag.
+constexpr int kClaimBatch = 4;
 
 __device__ __forceinline__ float bf16_to_f32(bf16_t x) {
   return __uint_as_float(((uint32_t)x) << 16);
@@ -122,6 +131,8 @@ struct ForwardParams {
   int fused;              // 1: up/gate and down in one launch (bf16)
   int slots_nt;           // 1: the slot rows Y / Ys are written and read with the
                           // non-temporal hint (they far exceed the MALL)
+  int claim_batch;        // task parts claimed per queue atomic (1, or kClaimBatch)
+  int keep_counters;      // testing: the setup kernel leaves the queue counters as they are
   void* a_blk;            // MXFP8: stage-blocked quantised rows of the routed m-blocks
   void* as_blk;           // MXFP8: the same for the shared expert's m-blocks
   void* trace;            // per-task timing records (libraries built with MOE_TRACE), or null

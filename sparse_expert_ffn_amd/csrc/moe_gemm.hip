@@ -47,9 +47,15 @@ template <int BM>
 constexpr int stage_k() {
   return MOE_STAGE_K > 0 ? MOE_STAGE_K : (BM >= 256 ? 32 : 64);
 }
+// MFMA shape of the persistent GEMMs' cores for tiles of BM rows (and of
+// their half tiles, which must add in the same order).
+template <int BM>
+constexpr int mfma_shape() {
+  return MOE_MFMA32 && BM >= 128 ? 32 : 16;
+}
 template <int BM, int NB, int STAGING, bool BS>
 struct TileSel<bf16_t, BM, NB, STAGING, BS> {
-  using type = TileGemmDirect<BM, NB, 8, stage_k<BM>(), 144 * 1024, BS>;
+  using type = TileGemmDirect<BM, NB, 8, stage_k<BM>(), 144 * 1024, BS, false, mfma_shape<BM>()>;
 };
 
 template <typename TG>
@@ -385,7 +391,9 @@ struct HalfSel {
 template <int BM, int NB, int STAGING, bool BS>
 struct HalfSel<bf16_t, BM, NB, STAGING, BS> {
   using type = std::conditional_t<(BM >= 64),
-                                  typename TileSel<bf16_t, BM / 2, NB, STAGING, BS>::type, void>;
+                                  TileGemmDirect<BM / 2, NB, 8, stage_k<BM / 2>(), 144 * 1024, BS,
+                                                 false, mfma_shape<BM>()>,
+                                  void>;
 };
 
 // ---------------------------------------------------- quota scheduler
@@ -534,37 +542,16 @@ __device__ __forceinline__ int64_t upgate_task(const ForwardParams& p, const Tas
     }, Bm, bb, N, n0, nc);
     run_mainloop(g, smem, p.H, [&](int r) { return s_tok[r] >= 0; });
     T* out = reinterpret_cast<T*>(shared ? p.hs : p.h);
-    const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
-    // this lane's first tile row and column; opaque to the optimiser, so the
-    // 32 row indices below are formed here, per task, instead of being
-    // hoisted out of the task loop and held in registers through the K loop
-    int lrow = (wave / TG::WN) * (BM / TG::WM) + (lane >> 4) * 4;
-    int lcol = (wave % TG::WN) * (BN / TG::WN) + (lane & 15);
-    asm volatile("" : "+v"(lrow), "+v"(lcol));
-#pragma unroll
-    for (int i = 0; i < TG::MI; ++i) {
-      // one 16-row block at a time: keeps the accumulator reads from being
-      // hoisted into VGPRs all at once
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int jj = 0; jj < TG::NI; ++jj)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int row = lrow + i * 16 + r;
-          const int64_t col = n0 + lcol + jj * 16;
-          if (s_tok[row] >= 0 && col < N) {
-            const float u = g.acc[0][i][jj][r];
-            const float gv = g.acc[1][i][jj][r];
-            const int brow = row0 + row;  // row in the block
-            const size_t o = p.h_blocked
-                                 ? (size_t)b * BMB * N + (size_t)(col >> 5) * (BMB * 32) +
-                                       brow * 32 + (col & 31)
-                                 : (size_t)(b * BMB + brow) * N + col;
-            out[o] = from_f32<T>(silu_f32(u) * gv);
-          }
-        }
-    }
+    g.for_each_pair([&](int row, int c, float u, float gv) {
+      const int64_t col = n0 + c;
+      if (s_tok[row] >= 0 && col < N) {
+        const int brow = row0 + row;  // row in the block
+        const size_t o = p.h_blocked ? (size_t)b * BMB * N + (size_t)(col >> 5) * (BMB * 32) +
+                                           brow * 32 + (col & 31)
+                                     : (size_t)(b * BMB + brow) * N + col;
+        out[o] = from_f32<T>(silu_f32(u) * gv);
+      }
+    });
     return shared ? ts.nb_r + b : b;
   }
 }
@@ -576,7 +563,7 @@ __global__ __launch_bounds__((tile_threads<T, BM, 2, 2>()), 1) void upgate_kerne
   __shared__ int64_t s_task;
   __shared__ int s_tok[BM];
   const TaskSpace ts = task_space(p, BM, BN, p.D, p.Ds);
-  int q = blockIdx.x % kXcds, tried = 0;
+  Claimer cs(blockIdx.x % kXcds);
   QuotaState qs = quota_init(p.E);
   using TH = typename HalfSel<T, BM, 2, 2, BS>::type;
   constexpr bool kHalves = !std::is_void<TH>::value;
@@ -588,7 +575,7 @@ __global__ __launch_bounds__((tile_threads<T, BM, 2, 2>()), 1) void upgate_kerne
         const int64_t t = claim_quota(p, ts, p.counters + kQuotaBase, qs);
         s_task = t < 0 ? -1 : t << 2;
       } else {
-        s_task = claim_task_split(p.counters, ts.total, wgs_per_xcd(), split, q, tried);
+        s_task = claim_checked(p, 0, ts.total, split, cs);
       }
     }
     trace_stamp(0);
@@ -760,8 +747,7 @@ __global__ __launch_bounds__((tile_threads<T, BM, kDownStrips, 1>()), 1) void do
   __shared__ int s_f[BM];   // output row: slot f (routed) or token (shared)
   __shared__ float s_w[BM];
   const TaskSpace ts = task_space(p, BM, kDownStrips * BN, p.H, p.H);
-  int q = blockIdx.x % kXcds, tried = 0;
-  int* counters = p.counters + kXcds;
+  Claimer cs(blockIdx.x % kXcds);
   QuotaState qs = quota_init(p.E);
   TG g;
   for (;;) {
@@ -773,7 +759,7 @@ __global__ __launch_bounds__((tile_threads<T, BM, kDownStrips, 1>()), 1) void do
         // whole tiles only: split into halves, the down tasks measured no
         // faster, and the half-tile code slowed the whole-tile path (prefill
         // down +3 to +5%)
-        s_task = claim_task_split(counters, ts.total, wgs_per_xcd(), false, q, tried);
+        s_task = claim_checked(p, 1, ts.total, false, cs);
       }
     }
     trace_stamp(0);
@@ -828,7 +814,7 @@ __device__ __forceinline__ bool wait_count(const int* ctr, int need) {
 // compiler short of SGPRs; it restores descriptors from VGPR lanes right
 // before loads).
 template <int BM, bool BS>
-using FusedTile = TileGemmDirect<BM, 2, 8, stage_k<BM>(), 144 * 1024, BS, true>;
+using FusedTile = TileGemmDirect<BM, 2, 8, stage_k<BM>(), 144 * 1024, BS, true, mfma_shape<BM>()>;
 
 template <int BM, int BN, bool BS>
 __global__ __launch_bounds__((tile_threads<bf16_t, BM, 2, 2>()), 1) void fused_kernel(
@@ -1231,9 +1217,10 @@ int forward_lds_ok(int dtype, int BM) {
 // Clear what must start at zero with a fill kernel rather than a memset node,
 // so the whole call can be captured in a HIP graph: the task counters, and
 // either the fp32 accumulator (atomic combine) or the kept flags (slot combine).
+// keep_queues (testing): leave the queue counters [0, 2 kXcds) as they are.
 __global__ __launch_bounds__(256) void setup_kernel(float* acc, int64_t n, uint8_t* flags,
                                                     int64_t nflags, int* counters, int* ready,
-                                                    int64_t nready) {
+                                                    int64_t nready, int keep_queues) {
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   const int64_t i0 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (acc != nullptr) {
@@ -1248,7 +1235,8 @@ __global__ __launch_bounds__(256) void setup_kernel(float* acc, int64_t n, uint8
     for (int64_t i = i0; i < n16; i += stride) f16[i] = make_uint4(0, 0, 0, 0);
     for (int64_t i = n16 * 16 + i0; i < nflags; i += stride) flags[i] = 0;
   }
-  for (int64_t i = i0; i < kCounterInts; i += stride) counters[i] = 0;
+  for (int64_t i = i0; i < kCounterInts; i += stride)
+    if (!keep_queues || i >= 2 * kXcds) counters[i] = 0;
   for (int64_t i = i0; i < nready; i += stride) ready[i] = 0;
 }
 
@@ -1261,7 +1249,7 @@ hipError_t launch_forward_setup(const ForwardParams& p, hipStream_t st) {
   if (blocks < 1) blocks = 1;
   if (blocks > 4096) blocks = 4096;
   hipLaunchKernelGGL(setup_kernel, dim3((unsigned)blocks), dim3(256), 0, st, acc, n, flags, nf,
-                     p.counters, p.ready, p.fused ? p.n_ready : (int64_t)0);
+                     p.counters, p.ready, p.fused ? p.n_ready : (int64_t)0, p.keep_counters);
   return hipGetLastError();
 }
 

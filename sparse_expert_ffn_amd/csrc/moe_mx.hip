@@ -339,10 +339,10 @@ __global__ __launch_bounds__(512, 1) void upgate_mx_kernel(ForwardParams p) {
   __shared__ int64_t s_task;
   __shared__ int s_tok[BM];
   const TaskSpace ts = task_space(p, BM, 128, p.D, p.Ds);
-  int q = blockIdx.x % kXcds, tried = 0;
+  Claimer cs(blockIdx.x % kXcds);
   TG g;
   for (;;) {
-    if (threadIdx.x == 0) s_task = claim_task(p.counters, ts.total, q, tried);
+    if (threadIdx.x == 0) s_task = claim_checked(p, 0, ts.total, false, cs) >> 2;
     trace_stamp(0);
     __syncthreads();
     const int64_t t = uniform64(s_task);
@@ -418,10 +418,10 @@ __global__ __launch_bounds__(512, 1) void down_mx_kernel(ForwardParams p) {
   __shared__ int s_tok[BM];
   __shared__ int s_f[BM];
   const TaskSpace ts = task_space(p, BM, 256, p.H, p.H);
-  int q = blockIdx.x % kXcds, tried = 0;
+  Claimer cs(blockIdx.x % kXcds);
   TG g;
   for (;;) {
-    if (threadIdx.x == 0) s_task = claim_task(p.counters + kXcds, ts.total, q, tried);
+    if (threadIdx.x == 0) s_task = claim_checked(p, 1, ts.total, false, cs) >> 2;
     trace_stamp(0);
     __syncthreads();
     const int64_t t = uniform64(s_task);

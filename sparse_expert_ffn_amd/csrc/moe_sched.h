@@ -99,6 +99,20 @@ __device__ __forceinline__ int64_t claim_task(int* counters, int64_t total, int&
   return -1;
 }
 
+// Workgroups per XCD of this grid.
+__device__ __forceinline__ int64_t wgs_per_xcd() {
+  return gridDim.x >= kXcds ? gridDim.x / kXcds : 1;
+}
+
+// Thread 0's claim state in one persistent workgroup: the queue it claims
+// from, how many queues it has found empty, and the claims left of its last
+// batch on queue q.
+struct Claimer {
+  int q, tried;
+  int64_t c_next, c_end;
+  __device__ explicit Claimer(int q0) : q(q0), tried(0), c_next(0), c_end(0) {}
+};
+
 // Long-tail splitting (the Weave review's tail handling, section 5.1). Tasks
 // cost about the same, so when a queue's n tasks are not a multiple of its R
 // workgroups, n mod R of them form a last round that only some workgroups
@@ -112,14 +126,34 @@ __device__ __forceinline__ int64_t claim_task(int* counters, int64_t total, int&
 // bit. Claimed ids are (task << 2) | part: part 0 = whole tile, 1 = the first
 // half of the rows, 2 = the second. R = workgroups per XCD; split = false
 // keeps every task whole.
+//
+// Batched claims (the Weave review's two-level claiming, section 5.2): with
+// batch > 1 one atomic takes `batch` consecutive claims of the queue, which
+// the workgroup then runs one after the other. Fewer atomics, coarser
+// balance at the end of each queue.
+//
+// done (or null) counts the claims handed out, for the end-of-kernel check
+// (queue_check).
 __device__ __forceinline__ int64_t claim_task_split(int* counters, int64_t total, int64_t R,
-                                                    bool split, int& q, int& tried) {
-  while (tried < kXcds) {
+                                                    bool split, int batch, Claimer& cs,
+                                                    int* done) {
+  while (cs.tried < kXcds) {
+    const int q = cs.q;
     const int64_t lo = total * q / kXcds;
     const int64_t n = total * (q + 1) / kXcds - lo;
     if (n > 0) {
       const int64_t k = split ? n % R : 0;  // tasks cut in two
-      const int c = atomicAdd(&counters[q], 1);
+      int64_t c;
+      if (cs.c_next < cs.c_end) {
+        c = cs.c_next++;
+      } else {
+        c = atomicAdd(&counters[q], batch);
+        if (c < n + k) {
+          cs.c_next = c + 1;
+          cs.c_end = c + batch < n + k ? c + batch : n + k;
+          if (done) atomicAdd(done, (int)(cs.c_end - c));
+        }
+      }
       if (c < n + k) {
         const int64_t whole = n - k;
         if (c < whole) return (lo + c) << 2;
@@ -127,15 +161,57 @@ __device__ __forceinline__ int64_t claim_task_split(int* counters, int64_t total
         return ((lo + whole + v / 2) << 2) | (1 + (v & 1));
       }
     }
-    q = (q + 1) % kXcds;
-    ++tried;
+    cs.q = (q + 1) % kXcds;
+    ++cs.tried;
   }
   return -1;
 }
 
-// Workgroups per XCD of this grid.
-__device__ __forceinline__ int64_t wgs_per_xcd() {
-  return gridDim.x >= kXcds ? gridDim.x / kXcds : 1;
+// The end-of-kernel check of one grouped GEMM's queues, run by thread 0 of
+// each workgroup once it has found every queue empty. The last workgroup to
+// get there checks what the claims must have left:
+//  - the claims handed out (`done`) equal the task parts of the task space;
+//    fewer means tasks never ran, as when the counters did not start at zero
+//    (kStatusTasksLost);
+//  - each queue with tasks ends at batch * (its successful atomics + one
+//    failed atomic per workgroup), an empty queue at 0 (kStatusQueueCount).
+// A failure sets its bit in the call's status word.
+__device__ __forceinline__ void queue_check(const int* queues, const int* done, int* exits,
+                                            int* status, int64_t total, int64_t R, bool split,
+                                            int batch) {
+  const int grid = (int)gridDim.x;
+  const int prev = __hip_atomic_fetch_add(exits, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+  if (prev != grid - 1) return;
+  int64_t parts = 0;
+  bool counts_ok = true;
+  for (int q = 0; q < kXcds; ++q) {
+    const int64_t lo = total * q / kXcds;
+    const int64_t n = total * (q + 1) / kXcds - lo;
+    const int64_t k = split ? n % R : 0;
+    parts += n + k;
+    const int64_t want = n > 0 ? (int64_t)batch * ((n + k + batch - 1) / batch + grid) : 0;
+    const int got = __hip_atomic_load(&queues[q], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
+    if ((int64_t)got != want) counts_ok = false;
+  }
+  const int d = __hip_atomic_load(done, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
+  int bits = 0;
+  if ((int64_t)d != parts) bits |= kStatusTasksLost;
+  if (!counts_ok) bits |= kStatusQueueCount;
+  if (bits) atomicOr(status, bits);
+}
+
+// Claim with the call's batching and bookkeeping for grouped GEMM g (0
+// up/gate, 1 down), whose queues are at counters + g * kXcds; on finding
+// every queue empty, run the end-of-kernel check. Thread 0 only.
+__device__ __forceinline__ int64_t claim_checked(const ForwardParams& p, int g, int64_t total,
+                                                 bool split, Claimer& cs) {
+  int* queues = p.counters + g * kXcds;
+  int* done = p.counters + kDoneBase + 2 * g;
+  const int64_t R = wgs_per_xcd();
+  const int64_t c = claim_task_split(queues, total, R, split, p.claim_batch, cs, done);
+  if (c < 0)
+    queue_check(queues, done, done + 1, p.counters + kStatusWord, total, R, split, p.claim_batch);
+  return c;
 }
 
 struct TaskSpace {

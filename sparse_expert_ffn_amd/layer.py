@@ -15,9 +15,10 @@ from . import (MOE_BF16, MOE_F32, MOE_MXFP8, make_shape, moe_align_block_size, m
 class MoEBuffers:
     def __init__(self, S, H, D, E, k, D_shared=0, capacity=0, block_size=128, renormalize=1,
                  dtype=MOE_BF16, out_f32=False, atomic_combine=False, sched_quota=False,
-                 fused_launch=False, device="cuda"):
+                 fused_launch=False, device="cuda", extra_flags=0):
         self.shape = make_shape(S, H, D, E, k, D_shared, capacity, block_size, renormalize,
-                                dtype, out_f32, atomic_combine, sched_quota, fused_launch)
+                                dtype, out_f32, atomic_combine, sched_quota, fused_launch,
+                                extra_flags)
         self.tdtype = torch.bfloat16 if dtype != MOE_F32 and not out_f32 else torch.float32
         dev = torch.device(device)
         cap = S * k + E * (block_size - 1)

@@ -87,7 +87,7 @@ def test_gate_topk_validation(lib):
     assert gate(lib, dec, ws=FAKE, wsn=need - 1) == 3   # too small
     assert gate(lib, dec, ws=FAKE + 4, wsn=need) == 2   # misaligned
     s = shape()
-    s.flags = 16                                        # undefined flag bit
+    s.flags = 64                                        # undefined flag bit
     assert gate(lib, s) == 1
 
 
@@ -155,8 +155,12 @@ def test_forward_validation(lib):
     assert fwd(lib, shape(dtype=moe.MOE_F32, fused_launch=True)) == 2
     assert fwd(lib, shape(fused_launch=True, sched_quota=True)) == 2
     s = shape()
-    s.flags = 16                                        # undefined flag bit
+    s.flags = 64                                        # undefined flag bit
     assert fwd(lib, s) == 1
+    # batched claims and the queue-reset test hook: the two-launch queues only
+    for f in (moe.MOE_SCHED_BATCH, moe.MOE_TEST_SKIP_QUEUE_RESET):
+        assert fwd(lib, shape(fused_launch=True, extra_flags=f)) == 2
+        assert fwd(lib, shape(sched_quota=True, extra_flags=f)) == 2
     assert moe.moe_forward_workspace_bytes(shape(dtype=moe.MOE_F32, fused_launch=True)) == 0
     # readiness counters: one per routed and per shared m-block, more workspace
     assert (moe.moe_forward_workspace_bytes(shape(D_shared=64, fused_launch=True))
@@ -182,6 +186,17 @@ def test_forward_status_word_layout(lib):
     queues = int(re.search(r"kQuotaBase\s*=\s*(\d+)", common).group(1))
     assert word * 4 == off and timeout == moe.MOE_STATUS_READY_TIMEOUT
     assert 16 <= word < queues, "inside the counter block, clear of the task queues"
+    lost = int(re.search(r"kStatusTasksLost\s*=\s*(\d+)", common).group(1))
+    count = int(re.search(r"kStatusQueueCount\s*=\s*(\d+)", common).group(1))
+    assert macros["MOE_STATUS_TASKS_LOST"] == moe.MOE_STATUS_TASKS_LOST == lost
+    assert macros["MOE_STATUS_QUEUE_COUNT"] == moe.MOE_STATUS_QUEUE_COUNT == count
+    bits = [timeout, lost, count]
+    assert all(b & (b - 1) == 0 for b in bits) and len(set(bits)) == 3, "distinct single bits"
+    # the per-GEMM done / exit counters: after both GEMMs' queues, before the status word
+    done = int(re.search(r"kDoneBase\s*=\s*(\d+)", common).group(1))
+    assert 16 <= done and done + 4 <= word
+    for f in ("MOE_SCHED_BATCH", "MOE_TEST_SKIP_QUEUE_RESET"):
+        assert macros[f] == getattr(moe, f)
     for kw in (dict(), dict(S=1, E=1, k=1), dict(dtype=moe.MOE_F32, block_size=128),
                dict(fused_launch=True), dict(atomic_combine=True)):
         assert moe.moe_forward_workspace_bytes(shape(**kw)) >= off + 4, kw

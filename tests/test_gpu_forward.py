@@ -11,6 +11,7 @@ import pytest
 import torch
 
 import oracle
+import sparse_expert_ffn_amd as moe
 from sparse_expert_ffn_amd import workloads as wk
 from tests.gpu_util import DeviceLayer, bf16_output_excess, buffers, dev, host, parity
 
@@ -42,6 +43,7 @@ def run_case(orc, wl, bm=None, li=None, logits=None, poison=True, atomic=False):
         buf.route(logits_in=dev(G_o))
         O = L.forward(buf)
         torch.cuda.synchronize()
+        assert moe.forward_status(buf.forward_ws) == 0, "status word set"
         assert np.array_equal(buf.topk_ids.cpu().numpy(), ref["ids"]), "routing differs"
         outs[out_f32] = host(O)
         assert np.all(np.isfinite(outs[out_f32])), "non-finite output"
