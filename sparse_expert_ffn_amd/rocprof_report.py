@@ -23,7 +23,9 @@ Derived figures per kernel (averages over its dispatches):
     GRBM_GUI_ACTIVE / XCDs (the GRBM counters are summed over the XCDs);
   - LDS active / bank-conflict share = counter / (cycles x CUs);
   - waves waiting on instruction issue = SQ_WAIT_INST_ANY / SQ_WAVE_CYCLES;
-  - effective clock = GRBM_COUNT / XCDs / duration.
+  - effective clock = GRBM_COUNT / XCDs / duration;
+  - the cycle shares and the clock only for kernels of MIN_COUNTER_US or more
+    (the counter window of a short dispatch is much longer than the kernel).
 
 Usage (from the repository root, on a machine with the GPU):
 
@@ -44,6 +46,7 @@ import glob
 import json
 import os
 import re
+import shlex
 import subprocess
 import sys
 import time
@@ -56,6 +59,8 @@ SIMDS = 1024
 CUS = 256
 PEAK_BF16_TFLOPS = 2500.0
 PEAK_HBM_GBS = 8000.0
+# kernels shorter than this get no cycle-share or clock figures
+MIN_COUNTER_US = 50.0
 
 SQ_COUNTERS = ("SQ_VALU_MFMA_BUSY_CYCLES", "SQ_LDS_BANK_CONFLICT", "SQ_LDS_IDX_ACTIVE",
                "SQ_WAVE_CYCLES", "SQ_WAIT_INST_ANY", "GRBM_GUI_ACTIVE", "GRBM_COUNT")
@@ -198,6 +203,11 @@ def digest(out_dir: str, algorithmic=None):
         d = s.get("_dur")
         if cnt and d:
             r["clock_ghz"] = _avg([c / XCDS / ns for c, ns in zip(cnt, d) if ns > 0])
+        if r["avg_us"] < MIN_COUNTER_US:
+            # the counters' collection window is several µs longer than a
+            # short dispatch: shares of its cycles and the clock say nothing
+            for key in ("mfma_busy", "lds_active", "lds_bank_conflict", "clock_ghz"):
+                r.pop(key, None)
         for prefix, alg in algorithmic.items():
             if name.startswith(prefix):
                 sec = r["avg_us"] * 1e-6
@@ -257,7 +267,7 @@ def run_passes(workload: str, out_dir: str, steps: int, warmup: int, passes, lim
         cmd = ["rocprofv3", *opts, "--output-format", "csv", "-d",
                os.path.abspath(os.path.join(out_dir, p)), "-o", p, "--", *prog]
         cmds.append(cmd)
-        print(f"[rocprof] pass {p}: {' '.join(cmd)}", flush=True)
+        print(f"[rocprof] pass {p}: {shlex.join(cmd)}", flush=True)
         t0 = time.time()
         r = subprocess.run(cmd, cwd="/tmp", env=env, timeout=limit,
                            stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
@@ -338,7 +348,7 @@ def main(argv=None):
     if a.mode == "run":
         cmds = run_passes(a.workload, a.out, a.steps, a.warmup, passes, a.limit)
         with open(cmds_file, "w") as fh:
-            json.dump([" ".join(c) for c in cmds], fh, indent=1)
+            json.dump([shlex.join(c) for c in cmds], fh, indent=1)
     cmds = json.load(open(cmds_file)) if os.path.exists(cmds_file) else []
     rel = [re.sub(re.escape(ROOT) + "/", "", c).replace(sys.executable, "python3") for c in cmds]
     rel = [re.sub(r"-d \S+/(\w+) ", r"-d OUT/\1 ", c) for c in rel]

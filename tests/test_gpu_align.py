@@ -49,10 +49,15 @@ GRID = [  # (S, k, E, BM, C)
     (64, 8, 256, 16, 0), (1000, 3, 24, 48, 0), (513, 5, 100, 64, 40), (16384, 2, 64, 128, 512),
     (16384, 8, 256, 128, 0), (8192, 4, 64, 128, 0), (4097, 8, 1024, 16, 0), (1, 1, 1, 1, 0),
     (1, 8, 1024, 128, 0), (2000, 1, 7, 1, 0), (3000, 2, 33, 256, 0), (333, 6, 6, 5, 3),
-    # around the one-workgroup / three-launch boundary (16384 assignments), and
+    # around the one-workgroup / multi-workgroup boundary (16384 assignments), and
     # 1024 experts with 256-row blocks on both paths
     (8192, 2, 64, 64, 0), (16385, 1, 33, 32, 0), (600, 2, 1024, 256, 0),
-    (17000, 1, 1024, 256, 0)]
+    (17000, 1, 1024, 256, 0),
+    # multi-workgroup path: one and two experts (segment counts split in four
+    # parts per expert), E just past 128 (one part), a segment count that is
+    # not a multiple of four, capacity drops with many segments
+    (20000, 1, 1, 16, 0), (9001, 2, 2, 7, 100), (33000, 1, 130, 64, 0),
+    (16500, 2, 64, 256, 300)]
 
 
 @pytest.mark.parametrize("dist", wk.ID_DISTS)
