@@ -36,6 +36,12 @@ namespace moe {
 typedef int i32x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
+// Row blocks whose A fragments are read ahead of the MFMAs (all of the
+// stage's by default: a row block has only NB MFMAs to cover a read).
+#ifndef MOE_MX_ADIST
+#define MOE_MX_ADIST 4
+#endif
+
 constexpr int kMxK = 64;          // K values per stage
 constexpr int kMxRowBytes = 66;   // per row and stage: 64 codes + 2 scales
 
@@ -184,9 +190,10 @@ struct TileGemmMx {
   }
 
   // MFMAs of one stage for this wave's row blocks [0, NA), software-
-  // pipelined: the B fragments and row block 0's A fragment are read first,
-  // then the read of block i + 1 goes out ahead of block i's MFMAs, so the
-  // matrix core works while the next fragment comes back from LDS. between(i)
+  // pipelined: the B fragments and the first MOE_MX_ADIST row blocks' A
+  // fragments are read first, then the read of block i + MOE_MX_ADIST goes
+  // out ahead of block i's MFMAs, so the matrix core works while later
+  // fragments come back from LDS. between(i)
   // runs after block i's MFMAs (the next stage's loads go out one at a time
   // there). The instruction order is pinned with scheduling-group barriers.
   template <int NA, typename Between>
@@ -205,23 +212,25 @@ struct TileGemmMx {
         b[m] = read_frag(bm, col, h);
         sb[m] = *reinterpret_cast<const unsigned char*>(bm + BN * 64 + col * 2 + h);
       }
-      i32x8_t a[2];
-      int sa[2];
-      auto read_a = [&](int i, int slot) {
+      constexpr int D = MOE_MX_ADIST < NA ? MOE_MX_ADIST : NA;  // blocks read ahead
+      i32x8_t a[NA];
+      int sa[NA];
+      auto read_a = [&](int i) {
         const int r = wm0 + i * 32 + (lane & 31);
-        a[slot] = read_frag(base, r, h);
-        sa[slot] = *reinterpret_cast<const unsigned char*>(base + BM * 64 + r * 2 + h);
+        a[i] = read_frag(base, r, h);
+        sa[i] = *reinterpret_cast<const unsigned char*>(base + BM * 64 + r * 2 + h);
       };
-      read_a(0, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 3 * NB + 3, 0);
+#pragma unroll
+      for (int i = 0; i < D; ++i) read_a(i);
+      __builtin_amdgcn_sched_group_barrier(0x100, 3 * NB + 3 * D, 0);
 #pragma unroll
       for (int i = 0; i < NA; ++i) {
-        if (i + 1 < NA) read_a(i + 1, (i + 1) & 1);
+        if (i + D < NA) read_a(i + D);
 #pragma unroll
         for (int m = 0; m < NB; ++m)
           acc[m][i] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-              a[i & 1], b[m], acc[m][i], 0, 0, 0, sa[i & 1], 0, sb[m]);
-        if (i + 1 < NA) __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
+              a[i], b[m], acc[m][i], 0, 0, 0, sa[i], 0, sb[m]);
+        if (i + D < NA) __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
         __builtin_amdgcn_sched_group_barrier(0x008, NB, 0);
         between(i);
       }

@@ -37,26 +37,36 @@ __device__ __forceinline__ int mx_scale_exp(float amax) {
   return e < -127 ? -127 : e;             // be <= 254 keeps e <= 119
 }
 
-// The E4M3 code nearest to x (finite), ties to the even code, |x| >= 448
-// saturating; a zero result keeps x's sign.
-__device__ __forceinline__ uint32_t e4m3_code(float x) {
-  const uint32_t bits = __float_as_uint(x);
-  const uint32_t sign = (bits >> 24) & 0x80u;
-  const float a = __uint_as_float(bits & 0x7FFFFFFFu);
-  if (a >= 448.0f) return sign | 0x7Eu;
-  if (a < 0.015625f) {  // below 2^-6: multiples of 2^-9 (exact scaling, RNE)
-    return sign | (uint32_t)__builtin_rintf(a * 512.0f);  // 8 becomes 2^-6 = code 0x08
-  }
-  const uint32_t ab = bits & 0x7FFFFFFFu;
-  uint32_t e = (ab >> 23) - 120;          // E + 7 (E >= -6, so 1 .. 15)
-  uint32_t m = (ab >> 20) & 7;            // top 3 mantissa bits
-  const uint32_t rest = ab & 0xFFFFFu;    // the 20 bits rounded away
-  if (rest > 0x80000u || (rest == 0x80000u && (m & 1u))) ++m;
-  if (m == 8) {
-    m = 0;
-    ++e;
-  }
-  return sign | (e << 3) | m;
+// E4M3 codes (bytes 0, 1 of the result; bytes 2, 3 from `old`, or with
+// HIGH, bytes 2, 3 = the codes and bytes 0, 1 from `old`) of the finite
+// values x0, x1: the code nearest to the value, ties to the even code, a
+// magnitude of 448 or more giving 448 and a zero result keeping the sign.
+// v_cvt_pk_fp8_f32 rounds to nearest even into the OCP E4M3 format; with its
+// inputs clamped to +-448 it saturates as the rule asks. (Checked on the GPU
+// against a software encoder of the same rule, for every float of magnitude
+// up to 1024, both signs: no difference.)
+template <bool HIGH = false>
+__device__ __forceinline__ uint32_t e4m3_pair(float x0, float x1, uint32_t old = 0) {
+  x0 = fminf(fmaxf(x0, -448.0f), 448.0f);
+  x1 = fminf(fmaxf(x1, -448.0f), 448.0f);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(x0, x1, (int)old, HIGH);
+}
+
+// The largest of v over each group of 32 lanes (lanes 0-31, 32-63), in every
+// lane of the group. Quad swaps (xor 1, xor 2) and the half-row and row
+// mirrors run on DPP (a max is its own all-reduce under any pairing that
+// joins the halves), then one swizzle joins the two 16-lane rows.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float max32_lanes(float v) {
+  v = fmaxf(v, dpp_f32<0xB1>(v));   // quad_perm [1,0,3,2]
+  v = fmaxf(v, dpp_f32<0x4E>(v));   // quad_perm [2,3,0,1]
+  v = fmaxf(v, dpp_f32<0x141>(v));  // row_half_mirror
+  v = fmaxf(v, dpp_f32<0x140>(v));  // row_mirror
+  // lane ^ 16 within each 32 (bitmask swizzle: and 0x1F, xor 0x10)
+  return fmaxf(v, __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x401F)));
 }
 
 // Quantise 32 values (one block) to codes packed 4 per uint32 and the scale.
@@ -67,10 +77,8 @@ __device__ __forceinline__ uint32_t mx_block(const float (&v)[32], uint32_t (&co
   const int e = mx_scale_exp(amax);
 #pragma unroll
   for (int w = 0; w < 8; ++w) {
-    uint32_t c = 0;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) c |= e4m3_code(ldexpf(v[4 * w + j], -e)) << (8 * j);
-    codes[w] = c;
+    const uint32_t lo = e4m3_pair(ldexpf(v[4 * w], -e), ldexpf(v[4 * w + 1], -e));
+    codes[w] = e4m3_pair<true>(ldexpf(v[4 * w + 2], -e), ldexpf(v[4 * w + 3], -e), lo);
   }
   return (uint32_t)(e + 127);
 }
@@ -317,16 +325,23 @@ __device__ __forceinline__ void upgate_mx_task(const ForwardParams& p, const Tas
   for (int i = 0; i < TG::MI; ++i) {
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int row = lrow + i * 32 + 8 * (r >> 2) + (r & 3);
-      const float h = silu_f32(g.acc[0][i][r]) * g.acc[1][i][r];
-      float amax = fabsf(h);
+    for (int r = 0; r < 16; r += 2) {  // two rows per conversion
+      float x[2];
+      int e[2];
 #pragma unroll
-      for (int x = 1; x < 32; x <<= 1) amax = fmaxf(amax, __shfl_xor(amax, x, 32));
-      const int e = mx_scale_exp(amax);
-      if (s_tok[row] >= 0) {
-        blk[row * 64 + (col % kMxK)] = (uint8_t)e4m3_code(ldexpf(h, -e));
-        if ((lane & 31) == 0) blk[BM * 64 + row * 2 + half] = (uint8_t)(e + 127);
+      for (int q = 0; q < 2; ++q) {
+        const float h = silu_f32(g.acc[0][i][r + q]) * g.acc[1][i][r + q];
+        e[q] = mx_scale_exp(max32_lanes(fabsf(h)));
+        x[q] = ldexpf(h, -e[q]);
+      }
+      const uint32_t c = e4m3_pair(x[0], x[1]);
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const int row = lrow + i * 32 + 8 * ((r + q) >> 2) + ((r + q) & 3);
+        if (s_tok[row] >= 0) {
+          blk[row * 64 + (col % kMxK)] = (uint8_t)(c >> (8 * q));
+          if ((lane & 31) == 0) blk[BM * 64 + row * 2 + half] = (uint8_t)(e[q] + 127);
+        }
       }
     }
   }

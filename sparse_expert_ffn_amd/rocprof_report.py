@@ -249,9 +249,12 @@ def markdown(d, title: str, commands) -> str:
     return "\n".join(lines) + "\n"
 
 
-def bench_cmd(workload: str, steps: int, warmup: int, extra=()):
-    return [sys.executable, os.path.join(ROOT, "bench.py"), "--steps", str(steps), "--warmup",
-            str(warmup), "--no-cpu-baseline", "--other", "", "--workload", workload, *extra]
+def bench_cmd(workload: str, steps, warmup, extra=()):
+    """bench.py on one workload; steps / warmup None: the benchmark's own
+    defaults (the timed run whose HIP-event figures the trace must match)."""
+    counts = [] if steps is None else ["--steps", str(steps), "--warmup", str(warmup)]
+    return [sys.executable, os.path.join(ROOT, "bench.py"), *counts, "--no-cpu-baseline",
+            "--other", "", "--workload", workload, *extra]
 
 
 def run_passes(workload: str, out_dir: str, steps: int, warmup: int, passes, limit: int,
@@ -262,8 +265,14 @@ def run_passes(workload: str, out_dir: str, steps: int, warmup: int, passes, lim
     cmds = []
     for p in passes:
         opts = PASSES.get(p) or CALIBRATION[p]
-        prog = ([sys.executable, os.path.join(ROOT, "bench.py"), "--copy-calibration"]
-                if p in CALIBRATION else bench_cmd(workload, steps, warmup, extra))
+        # the kernel trace of the default timed run (its averages must agree
+        # with the bench line's event timing); counters on a short run
+        if p in CALIBRATION:
+            prog = [sys.executable, os.path.join(ROOT, "bench.py"), "--copy-calibration"]
+        elif p == "trace":
+            prog = bench_cmd(workload, None, None, extra)
+        else:
+            prog = bench_cmd(workload, steps, warmup, extra)
         cmd = ["rocprofv3", *opts, "--output-format", "csv", "-d",
                os.path.abspath(os.path.join(out_dir, p)), "-o", p, "--", *prog]
         cmds.append(cmd)
@@ -306,9 +315,24 @@ def algorithmic_counts(workload: str, out_dir: str):
     down_flops = 2.0 * wl.D * wl.H * kept + 2.0 * wl.D_shared * wl.H * wl.S
     down_bytes = touched * wl.D * wl.H * e + wl.D_shared * wl.H * e + \
         (kept + (wl.S if wl.D_shared else 0)) * wl.D * e
-    return {"upgate_kernel": {"flops": roof["flops_per_launch"], "bytes": roof["bytes_per_launch"]},
-            "down_kernel": {"flops": down_flops, "bytes": down_bytes},
-            "down_stream_kernel": {"flops": down_flops, "bytes": down_bytes}}
+    up = {"flops": roof["flops_per_launch"], "bytes": roof["bytes_per_launch"]}
+    down = {"flops": down_flops, "bytes": down_bytes}
+    if wl.mxfp8:  # 1 code byte per element and one scale byte per 32
+        down["bytes"] = down_bytes / e * 33 / 32
+        return {"upgate_mx_kernel": up, "down_mx_kernel": down}
+    return {"upgate_kernel": up, "down_kernel": down, "down_stream_kernel": down}
+
+
+def bench_line(log: str):
+    """The last bench.py JSON line in a pass log, or None."""
+    if not os.path.exists(log):
+        return None
+    line = None
+    with open(log) as fh:
+        for ln in fh:
+            if ln.startswith("{") and '"metric"' in ln:
+                line = ln
+    return json.loads(line) if line else None
 
 
 def traffic_record(d, workload: str, block_size: int, commands):
@@ -364,6 +388,16 @@ def main(argv=None):
             f"--out OUT --steps {a.steps} --warmup {a.warmup}",
             "which runs, from /tmp with TMPDIR=/tmp:"] + rel
     md = markdown(d, f"{a.workload}: kernel times and counters (MI355X, gfx950)", head)
+    bl = bench_line(tl)
+    if bl is not None:
+        r = bl["roofline"]
+        md += ("\nThe trace pass's own bench line (the default timed run, inputs resident): "
+               f"{bl['value'] / 1e6:.3f} M tokens/s, {bl['ms_per_step']:.4f} ms per step; "
+               f"{r['kernel']}, average launch by HIP events on its stream: "
+               f"{r['avg_launch_ms'] * 1e3:.1f} µs, {r['achieved']:.0f} {r['unit']} = "
+               f"{r['frac']:.3f} of {r['peak']:.0f} {r['unit']} (bound: {r['bound']}). "
+               "The trace averages above also hold the warm-up launches and the "
+               "profiler's own overhead.\n")
     print(md)
     if a.md:
         with open(a.md, "w") as fh:

@@ -113,7 +113,8 @@ def main(argv=None):
     wl = wk.WORKLOADS[a.workload]
     if a.tokens:
         wl = wl.with_tokens(a.tokens)
-    bm = a.block_size or suggest_block_size(wl.S, wl.k, wl.E, wl.capacity, wl.dtype)
+    dtype = moe.MOE_MXFP8 if wl.mxfp8 else wl.dtype
+    bm = a.block_size or suggest_block_size(wl.S, wl.k, wl.E, wl.capacity, dtype)
     li = wk.draw_layer(wl)
 
     def td(x):
@@ -126,9 +127,19 @@ def main(argv=None):
 
     ins = [td(x) for x in (li.A, li.Wr, li.W_up, li.W_gate, li.W_down, li.Ws_up, li.Ws_gate,
                            li.Ws_down)]
+    if wl.mxfp8:  # expert weights packed once for the MXFP8 GEMMs
+        def pack(W):
+            if W is None:
+                return None
+            E, K, N = (1,) + tuple(W.shape) if W.dim() == 2 else tuple(W.shape)
+            out = torch.empty(moe.moe_mxfp8_weight_bytes(E, K, N), dtype=torch.uint8,
+                              device="cuda")
+            moe.moe_pack_mxfp8_weights(W, out)
+            return out
+        ins = ins[:2] + [pack(w) for w in ins[2:]]
     bias = td(li.bias)
     buf = MoEBuffers(wl.S, wl.H, wl.D, wl.E, wl.k, wl.D_shared, wl.capacity, bm,
-                     wl.renormalize, wl.dtype, fused_launch=a.launch == "one", device="cuda")
+                     wl.renormalize, dtype, fused_launch=a.launch == "one", device="cuda")
     trace = torch.zeros(HEADER_BYTES + a.records * REC.itemsize, dtype=torch.uint8,
                         device="cuda")
     for _ in range(a.warmup):

@@ -65,6 +65,9 @@ def _edge_rows():
         b[20] = -0.0
         b[21] = -(2.0 ** (k - 20))              # a tiny negative: rounds to -0
         b[22:] = rng.standard_normal(10) * 2.0 ** (k - 12)
+        b[22:26] = (np.arange(4) + 0.5) * 2.0 ** (k - 8 - 9)  # ties in the subnormal range
+        b[26] = 464 * 2.0 ** (k - 8)            # half-way to 480: saturates to 448
+        b[27] = -447.9 * 2.0 ** (k - 8)         # just inside the top code
         rows.append(b)
     rows.append(np.zeros(32))
     X = np.concatenate(rows).reshape(-1, 64) if len(rows) % 2 == 0 else \
