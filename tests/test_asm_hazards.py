@@ -180,17 +180,21 @@ def test_scanner_follows_branches_and_back_edges():
 
 @pytest.mark.skipif(shutil.which(os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")) is None,
                     reason="hipcc not available")
-@pytest.mark.parametrize("source", ["moe_gemm.hip", "moe_mx.hip"])
-@pytest.mark.parametrize("variant", ["plain", "trace"])
+@pytest.mark.parametrize("source,variant", [("moe_gemm.hip", "plain"), ("moe_gemm.hip", "trace"),
+                                            ("moe_gemm.hip", "mfma32"), ("moe_mx.hip", "plain"),
+                                            ("moe_mx.hip", "trace")])
 def test_gemm_kernels_have_no_valu_sgpr_hazard(tmp_path, variant, source):
-    """Every source with LDS-direct loads, in both library builds: the plain
-    one and the one with timing records."""
+    """Every source with LDS-direct loads, in both library builds (the plain
+    one and the one with timing records), and the GEMMs with the 32x32x16
+    MFMA core option."""
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
     src = os.path.join(buildlib.PKG, "csrc", source)
     out = tmp_path / "kernels.s"
     flags = [f for f in buildlib.HIPCC_FLAGS if f not in ("-shared", "-fPIC")]
     if variant == "trace":
         flags += buildlib.TRACE_FLAGS
+    elif variant == "mfma32":
+        flags += ["-DMOE_MFMA32=1"]
     cmd = [hipcc, *flags, "-I", os.path.join(buildlib.ROOT, "include"), "-I",
            os.path.join(buildlib.PKG, "csrc"), "-S", "--cuda-device-only", src, "-o", str(out)]
     r = subprocess.run(cmd, capture_output=True, text=True)
