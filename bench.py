@@ -46,6 +46,9 @@ def parse():
                     help="grouped-GEMM scheduler: per-XCD atomic task queues (default), the "
                          "same queues claimed 4 tasks per atomic, or the static per-expert "
                          "workgroup quota (ablation baseline)")
+    ap.add_argument("--combine", choices=("pass", "fused"), default="pass",
+                    help="the router-weighted combine as a pass of its own after the down "
+                         "GEMM (default) or inside its epilogue (last arrival per token)")
     ap.add_argument("--launch", choices=("two", "one"), default="two",
                     help="the expert GEMMs as two persistent launches (up/gate, then down) "
                          "or as one (down tasks wait per m-block for its up/gate tasks)")
@@ -242,7 +245,8 @@ def setup_workload(wl, args, torch, moe, dev="cuda"):
     buf = MoEBuffers(wl.S, wl.H, wl.D, wl.E, wl.k, wl.D_shared, wl.capacity, bm,
                      wl.renormalize, dtype, sched_quota=args.sched == "quota",
                      fused_launch=args.launch == "one", device=dev,
-                     extra_flags=moe.MOE_SCHED_BATCH if args.sched == "batch" else 0)
+                     extra_flags=(moe.MOE_SCHED_BATCH if args.sched == "batch" else 0) |
+                     (moe.MOE_COMBINE_FUSED if args.combine == "fused" else 0))
     stream = torch.cuda.current_stream()
     n_step = [0]
 
@@ -348,7 +352,8 @@ def measure(wl, args, steps, warmup, torch, moe, full=True):
              "median_ms_per_step": med_ms, "wall_s": wall, "status_word": status}
     config = {"workload": wl.name, "S": wl.S, "H": wl.H, "D": wl.D, "E": wl.E, "k": wl.k,
               "D_shared": wl.D_shared, "capacity": wl.capacity, "block_size": bm,
-              "scheduler": args.sched, "launch": args.launch, "weight_copies": n_copies,
+              "scheduler": args.sched, "launch": args.launch, "combine": args.combine,
+              "weight_copies": n_copies,
               "parallelism": "single GPU"}
     if wl.mxfp8:
         layer["quantize_ms"] = small_ms[4] / max(n_small, 1)

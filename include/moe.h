@@ -131,6 +131,18 @@ typedef struct {
  * The queues then hand out no tasks or too few, O is wrong, and the status
  * word reports MOE_STATUS_TASKS_LOST. */
 #define MOE_TEST_SKIP_QUEUE_RESET 32
+/* flags (bf16 and fp32; not with MOE_COMBINE_ATOMIC, MOE_FUSED_LAUNCH or
+ * MOE_MXFP8, else MOE_ERR_UNSUPPORTED): the deterministic combine inside the
+ * down GEMM's epilogue (vLLM fused_moe note, "What we can actually change":
+ * the expert merge fused into the second GEMM) instead of a pass of its own.
+ * Each down task writes its rows to their slots and counts one arrival per
+ * (token, 256-column tile); the task that brings a tile's count to the
+ * token's kept slots (plus one with a shared expert) adds the token's rows
+ * there, its own from registers, in slot order and then the shared row, as
+ * the pass does: the same output, bit for bit. Tokens with no kept slot and
+ * no shared expert get a zero row from a small kernel. The down GEMM then
+ * runs on the task queues at every size. */
+#define MOE_COMBINE_FUSED 64
 
 /* The call's status word: an int32 at this byte offset of the moe_forward
  * workspace. Every moe_forward call sets it to 0 before its GEMMs run; once

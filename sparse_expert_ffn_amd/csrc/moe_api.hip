@@ -24,7 +24,7 @@ bool fits_buffer(int64_t bytes) { return bytes >= 0 && bytes < ((int64_t)1 << 31
 moe_status check_routing_dims(const moe_shape* s) {
   if (s == nullptr) return MOE_ERR_INVALID_ARGUMENT;
   if ((s->flags & ~(MOE_OUTPUT_F32 | MOE_COMBINE_ATOMIC | MOE_SCHED_QUOTA | MOE_FUSED_LAUNCH |
-                    MOE_SCHED_BATCH | MOE_TEST_SKIP_QUEUE_RESET)) != 0)
+                    MOE_SCHED_BATCH | MOE_TEST_SKIP_QUEUE_RESET | MOE_COMBINE_FUSED)) != 0)
     return MOE_ERR_INVALID_ARGUMENT;
   if (s->dtype != MOE_F32 && s->dtype != MOE_BF16 && s->dtype != MOE_MXFP8)
     return MOE_ERR_INVALID_ARGUMENT;
@@ -54,7 +54,7 @@ moe_status check_mx_forward_dims(const moe_shape* s) {
   if (s->H % 128 || s->D % 128 || s->D_shared % 128) return MOE_ERR_UNSUPPORTED;
   if (s->block_size != 64 && s->block_size != 128 && s->block_size != 256)
     return MOE_ERR_UNSUPPORTED;
-  if (s->flags & (MOE_COMBINE_ATOMIC | MOE_SCHED_QUOTA | MOE_FUSED_LAUNCH))
+  if (s->flags & (MOE_COMBINE_ATOMIC | MOE_SCHED_QUOTA | MOE_FUSED_LAUNCH | MOE_COMBINE_FUSED))
     return MOE_ERR_UNSUPPORTED;
   const int64_t BM = s->block_size;
   const int64_t cap_rows = (s->S * s->k + s->E * (BM - 1) + BM - 1) / BM * BM;
@@ -78,6 +78,9 @@ moe_status check_forward_dims(const moe_shape* s) {
   if (!forward_lds_ok(s->dtype, s->block_size)) return MOE_ERR_UNSUPPORTED;
   if ((s->flags & MOE_FUSED_LAUNCH) &&
       (s->dtype != MOE_BF16 || (s->flags & MOE_SCHED_QUOTA)))
+    return MOE_ERR_UNSUPPORTED;
+  // the fused combine replaces the slot combine pass of the two-launch path
+  if ((s->flags & MOE_COMBINE_FUSED) && (s->flags & (MOE_COMBINE_ATOMIC | MOE_FUSED_LAUNCH)))
     return MOE_ERR_UNSUPPORTED;
   // batching and the queue-reset test hook act on the two-launch queues
   if ((s->flags & (MOE_SCHED_BATCH | MOE_TEST_SKIP_QUEUE_RESET)) &&
@@ -117,9 +120,14 @@ bool out_bf16(const moe_shape* s) {
 bool atomic_combine(const moe_shape* s) { return (s->flags & MOE_COMBINE_ATOMIC) != 0; }
 
 struct ForwardLayout {
-  size_t counters, ready, oacc, y, ys, kept, h, hs, a_blk, as_blk, total;
-  int64_t n_ready;
+  size_t counters, ready, arr, oacc, y, ys, kept, h, hs, a_blk, as_blk, total;
+  int64_t n_ready, n_arr;
 };
+
+bool fused_combine(const moe_shape* s) { return (s->flags & MOE_COMBINE_FUSED) != 0; }
+
+// 256-column tiles of H (a down task's width)
+int64_t arrival_tiles(const moe_shape* s) { return (s->H + 255) / 256; }
 
 ForwardLayout forward_layout(const moe_shape* s) {
   const size_t es = s->dtype == MOE_BF16 ? 2 : 4;
@@ -133,7 +141,10 @@ ForwardLayout forward_layout(const moe_shape* s) {
   L.ready = round_up(kCounterInts * sizeof(int), kAlignUp);
   // one readiness counter per routed and per shared m-block (one launch only)
   L.n_ready = (s->flags & MOE_FUSED_LAUNCH) ? cap_rows / BM + s_rows / BM : 0;
-  L.oacc = L.ready + round_up((size_t)L.n_ready * sizeof(int), kAlignUp);
+  L.arr = L.ready + round_up((size_t)L.n_ready * sizeof(int), kAlignUp);
+  // fused combine: one arrival counter per token and 256-column tile
+  L.n_arr = fused_combine(s) ? s->S * arrival_tiles(s) : 0;
+  L.oacc = L.arr + round_up((size_t)L.n_arr * sizeof(int), kAlignUp);
   // atomic combine: fp32 accumulator unless O itself is fp32
   const size_t oacc_bytes = (atom && out_bf16(s)) ? (size_t)s->S * s->H * sizeof(float) : 0;
   L.y = L.oacc + round_up(oacc_bytes, kAlignUp);
@@ -287,6 +298,9 @@ moe_status forward_impl(const moe_shape* shape, const void* A, const void* W_up,
   p.ready = reinterpret_cast<int*>(ws + L.ready);
   p.n_ready = L.n_ready;
   p.fused = (shape->flags & MOE_FUSED_LAUNCH) ? 1 : 0;
+  p.fused_combine = fused_combine(shape) ? 1 : 0;
+  p.arrivals = reinterpret_cast<int*>(ws + L.arr);
+  p.arr_tiles = arrival_tiles(shape);
   p.claim_batch = (shape->flags & MOE_SCHED_BATCH) ? kClaimBatch : 1;
   p.keep_counters = (shape->flags & MOE_TEST_SKIP_QUEUE_RESET) ? 1 : 0;
   // Slot rows far larger than the 256 MB MALL (DeepSeek-V3 sizes: 0.94 GB)
@@ -348,6 +362,11 @@ moe_status forward_impl(const moe_shape* shape, const void* A, const void* W_up,
   if (p.atomic_combine) {
     if (p.out_bf16 &&
         run_stage(3, hs, [&] { return launch_forward_finalize(p, hs); }) != hipSuccess)
+      return MOE_ERR_HIP;
+  } else if (p.fused_combine) {
+    // the combine ran in the down epilogue; tokens no task reached get zeros
+    if (p.Ds == 0 &&
+        run_stage(3, hs, [&] { return launch_zero_unrouted(p, hs); }) != hipSuccess)
       return MOE_ERR_HIP;
   } else if (run_stage(3, hs, [&] { return launch_forward_combine(p, hs); }) != hipSuccess) {
     return MOE_ERR_HIP;

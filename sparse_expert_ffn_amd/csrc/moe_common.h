@@ -131,6 +131,9 @@ struct ForwardParams {
   int fused;              // 1: up/gate and down in one launch (bf16)
   int slots_nt;           // 1: the slot rows Y / Ys are written and read with the
                           // non-temporal hint (they far exceed the MALL)
+  int fused_combine;      // 1: the combine in the down epilogue (arrival counts)
+  int* arrivals;          // fused combine: [S][arr_tiles] rows arrived per token and tile
+  int64_t arr_tiles;      // 256-column tiles of H
   int claim_batch;        // task parts claimed per queue atomic (1, or kClaimBatch)
   int keep_counters;      // testing: the setup kernel leaves the queue counters as they are
   void* a_blk;            // MXFP8: stage-blocked quantised rows of the routed m-blocks
@@ -189,6 +192,7 @@ hipError_t launch_forward_down(const ForwardParams& p, int dtype, int BM, hipStr
 hipError_t launch_forward_fused(const ForwardParams& p, int BM, hipStream_t st);
 hipError_t launch_forward_finalize(const ForwardParams& p, hipStream_t st);
 hipError_t launch_forward_combine(const ForwardParams& p, hipStream_t st);
+hipError_t launch_zero_unrouted(const ForwardParams& p, hipStream_t st);
 int forward_lds_ok(int dtype, int BM);
 // MXFP8 mode (moe_mx.hip)
 hipError_t launch_mx_quantize_rows(const void* X, int dtype, int64_t R, int64_t K, uint8_t* codes,

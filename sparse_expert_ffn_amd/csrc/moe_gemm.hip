@@ -607,6 +607,89 @@ __global__ __launch_bounds__((tile_threads<T, BM, 2, 2>()), 1) void upgate_kerne
 // weights run as the tile core's two matrices, sharing the h rows.
 constexpr int kDownStrips = 2;
 
+// ------------------------------------- the combine in the down epilogue
+// (MOE_COMBINE_FUSED). A token's output tile (256 columns) is complete once
+// every kept slot of the token, and the shared expert's row, has been
+// computed, by down tasks that may run on any XCD. Each task:
+//  1. writes its rows to their slots (Y[f], or Ys[token] for the shared
+//     expert) with device-scope stores, which write through the XCD's L2 to
+//     the level the XCDs share; a release fence and a barrier follow;
+//  2. counts one arrival per row in arrivals[token][tile] (device-scope
+//     atomic); a row whose count reaches the token's kept slots (+1 with a
+//     shared expert) was the token's last to arrive, and goes on a list;
+//  3. for the listed tokens the whole workgroup adds the token's rows in slot
+//     order, w * y each product rounded to fp32, then the shared row, and
+//     writes O, 256 columns per row; the rows are read back with device-scope
+//     loads (which do not take stale lines from the XCD's L2). The
+//     arithmetic is the slot combine pass's: the same output, bit for bit.
+// No task waits for another; the counters are cleared by the setup kernel.
+// Measured about 3x the down kernel's time at prefill sizes (the per-task
+// read-back of the other slots is latency-bound inside the epilogue, where
+// the separate pass streams the slots with the whole GPU), so it is an
+// option, not the default.
+template <int BM, int BN, typename TG>
+__device__ __forceinline__ void fused_combine_epilogue(const ForwardParams& p, TG& g, bool shared,
+                                                       int64_t j, int64_t n0, const int* s_tok,
+                                                       const int* s_f) {
+  constexpr int NT = kDownStrips * BN;  // columns per task
+  __shared__ int s_n;                   // tokens completed by this task
+  __shared__ int s_list[BM];            // their tile rows
+  __shared__ uint32_t s_mask[BM];       // the token's kept slots, per tile row
+  const int64_t H = p.H;
+  const int64_t k = p.k;
+  float* Yb = shared ? p.Ys : p.Y;
+  g.for_each([&](int m, int row, int col, float v) {
+    const int f = s_f[row];
+    const int64_t n = n0 + m * BN + col;
+    if (f >= 0 && n < H)
+      __hip_atomic_store(Yb + (size_t)f * H + n, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  });
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+  if (threadIdx.x == 0) s_n = 0;
+  __syncthreads();
+  if (threadIdx.x < BM) {
+    const int r = threadIdx.x;
+    const int tok = s_tok[r];
+    if (tok >= 0 && s_f[r] >= 0) {
+      uint32_t mask = 0;
+      int need = p.Ds > 0 ? 1 : 0;
+      for (int64_t jj = 0; jj < k; ++jj)
+        if (p.kept[(int64_t)tok * k + jj]) {
+          mask |= 1u << jj;
+          ++need;
+        }
+      s_mask[r] = mask;
+      const int old = __hip_atomic_fetch_add(p.arrivals + (int64_t)tok * p.arr_tiles + j, 1,
+                                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (old == need - 1) s_list[atomicAdd(&s_n, 1)] = r;
+    }
+  }
+  __syncthreads();
+  const int nl = s_n;
+  for (int q = threadIdx.x; q < nl * NT; q += TG::THREADS) {
+    const int r = s_list[q / NT];
+    const int64_t n = n0 + q % NT;
+    if (n >= H) continue;
+    const int64_t tok = s_tok[r];
+    const uint32_t mask = s_mask[r];
+    float a = 0.f;
+    for (int64_t jj = 0; jj < k; ++jj) {
+      if (!((mask >> jj) & 1u)) continue;
+      const int64_t f2 = tok * k + jj;
+      const float y =
+          __hip_atomic_load(p.Y + f2 * H + n, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      a = a + __fmul_rn(p.topk_w[f2], y);  // the product rounded, not fused
+    }
+    if (p.Ds > 0)
+      a += __hip_atomic_load(p.Ys + tok * H + n, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (p.out_bf16)
+      reinterpret_cast<bf16_t*>(p.O)[tok * H + n] = f32_to_bf16(a);
+    else
+      reinterpret_cast<float*>(p.O)[tok * H + n] = a;
+  }
+  (void)shared;
+}
+
 // One down task t of the task space ts, run by the whole workgroup.
 // before_rows(rb, shared) runs on every thread once the m-block is known and
 // before the barrier that precedes the task's first read of h (rb: the
@@ -618,7 +701,9 @@ constexpr int kDownStrips = 2;
 // WAITS: before_rows may give up a bounded wait for the m-block's SwiGLU
 // rows (it then returns true on thread 0): the task writes NaN to its output
 // rows instead of its product with whatever h held.
-template <typename T, int BMB, int BN, bool SLOT_NT, bool WAITS, typename TG, typename BeforeRows>
+// FCOMB: the combine runs here (p.fused_combine; see fused_combine_epilogue).
+template <typename T, int BMB, int BN, bool SLOT_NT, bool WAITS, bool FCOMB = false, typename TG,
+          typename BeforeRows>
 __device__ __forceinline__ void down_task(const ForwardParams& p, const TaskSpace& ts, int64_t t,
                                           int row0, TG& g, char* smem, int* s_tok, int* s_f,
                                           float* s_w, BeforeRows before_rows) {
@@ -717,6 +802,8 @@ __device__ __forceinline__ void down_task(const ForwardParams& p, const TaskSpac
         const int64_t n = n0 + m * BN + col;
         if (tok >= 0 && n < H) atomicAdd(O + (size_t)tok * H + n, s_w[row] * v);
       });
+    } else if constexpr (FCOMB) {
+      fused_combine_epilogue<BM, BN>(p, g, shared, j, n0, s_tok, s_f);
     } else {
       // the row into its own slot: routed -> Y[f], shared -> Ys[token]; the
       // combine applies the router weight
@@ -737,10 +824,24 @@ __device__ __forceinline__ void down_task(const ForwardParams& p, const TaskSpac
   }
 }
 
-template <typename T, int BM, int BN, bool BS>
+// The down kernel's tile core; with the fused combine (FC) the LDS-direct core
+// takes the wait-state form of its loads (the larger epilogue raises the SGPR
+// pressure until the compiler restores descriptors from VGPR lanes next to
+// the loads).
+template <typename T, int BM, bool BS, bool FC, bool DIRECT = TileSel<T, BM, 2, 1, BS>::type::DIRECT>
+struct DownTile {
+  using type = typename TileSel<T, BM, 2, 1, BS>::type;
+};
+template <typename T, int BM, bool BS>
+struct DownTile<T, BM, BS, true, true> {
+  using type = TileGemmDirect<BM, 2, 8, stage_k<BM>(), 144 * 1024, BS, true, mfma_shape<BM>()>;
+};
+
+template <typename T, int BM, int BN, bool BS, bool FC = false>
 __global__ __launch_bounds__((tile_threads<T, BM, kDownStrips, 1>()), 1) void down_kernel(
     ForwardParams p) {
-  using TG = typename TileSel<T, BM, kDownStrips, 1, BS>::type;
+  static_assert(kDownStrips == 2, "two strips per down task");
+  using TG = typename DownTile<T, BM, BS, FC>::type;
   extern __shared__ __align__(16) char smem[];
   __shared__ int64_t s_task;
   __shared__ int s_tok[BM];
@@ -769,8 +870,8 @@ __global__ __launch_bounds__((tile_threads<T, BM, kDownStrips, 1>()), 1) void do
       trace_record(p, kTraceDown, -1);
       break;
     }
-    down_task<T, BM, BN, true, false>(p, ts, c >> 2, 0, g, smem, s_tok, s_f, s_w,
-                                      [](int64_t, bool) { return false; });
+    down_task<T, BM, BN, !FC, false, FC>(p, ts, c >> 2, 0, g, smem, s_tok, s_f, s_w,
+                                         [](int64_t, bool) { return false; });
     trace_record(p, kTraceDown, c);
   }
 }
@@ -1120,7 +1221,7 @@ static bool down_stream_ok(const ForwardParams& p) {
   if (BM > 32) return false;
   const int64_t kmin = p.Ds > 0 ? std::min(p.D, p.Ds) : p.D;
   const int64_t kmax = p.Ds > 0 ? std::max(p.D, p.Ds) : p.D;
-  return !p.atomic_combine && !p.sched_quota &&
+  return !p.atomic_combine && !p.sched_quota && !p.fused_combine &&
          (kmin + TG::BK - 1) / TG::BK >= 2 * TG::NSTAGE - 1 &&
          (kmax + TG::BK - 1) / TG::BK <= 16;
 }
@@ -1151,6 +1252,17 @@ static hipError_t launch_upgate_t(const ForwardParams& p, hipStream_t st) {
 
 template <typename T, int BM>
 static hipError_t launch_down_t(const ForwardParams& p, hipStream_t st) {
+  if (p.fused_combine) {
+    constexpr int BN = down_bn<BM>();
+    if constexpr (sizeof(T) == 2) {
+      if (weights_streamed(p, BM))
+        return launch_persistent(down_kernel<T, BM, BN, true, true>,
+                                 lds_bytes<T, BM, kDownStrips, 1>(),
+                                 tile_threads<T, BM, kDownStrips, 1>(), p, st);
+    }
+    return launch_persistent(down_kernel<T, BM, BN, false, true>, lds_bytes<T, BM, kDownStrips, 1>(),
+                             tile_threads<T, BM, kDownStrips, 1>(), p, st);
+  }
   if constexpr (sizeof(T) == 2) {
     const bool bs = weights_streamed(p, BM);
     if (down_stream_ok<BM>(p))
@@ -1220,7 +1332,8 @@ int forward_lds_ok(int dtype, int BM) {
 // keep_queues (testing): leave the queue counters [0, 2 kXcds) as they are.
 __global__ __launch_bounds__(256) void setup_kernel(float* acc, int64_t n, uint8_t* flags,
                                                     int64_t nflags, int* counters, int* ready,
-                                                    int64_t nready, int keep_queues) {
+                                                    int64_t nready, int keep_queues, int* arrivals,
+                                                    int64_t narr) {
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   const int64_t i0 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (acc != nullptr) {
@@ -1238,6 +1351,7 @@ __global__ __launch_bounds__(256) void setup_kernel(float* acc, int64_t n, uint8
   for (int64_t i = i0; i < kCounterInts; i += stride)
     if (!keep_queues || i >= 2 * kXcds) counters[i] = 0;
   for (int64_t i = i0; i < nready; i += stride) ready[i] = 0;
+  for (int64_t i = i0; i < narr; i += stride) arrivals[i] = 0;
 }
 
 hipError_t launch_forward_setup(const ForwardParams& p, hipStream_t st) {
@@ -1245,11 +1359,13 @@ hipError_t launch_forward_setup(const ForwardParams& p, hipStream_t st) {
   const int64_t n = acc ? p.S * p.H : 0;
   uint8_t* flags = p.atomic_combine ? nullptr : p.kept;
   const int64_t nf = flags ? p.F : 0;
-  int64_t blocks = (std::max(n / 4, nf / 16) + 255) / 256;
+  const int64_t narr = p.fused_combine ? p.S * p.arr_tiles : 0;
+  int64_t blocks = (std::max(std::max(n / 4, nf / 16), narr) + 255) / 256;
   if (blocks < 1) blocks = 1;
   if (blocks > 4096) blocks = 4096;
   hipLaunchKernelGGL(setup_kernel, dim3((unsigned)blocks), dim3(256), 0, st, acc, n, flags, nf,
-                     p.counters, p.ready, p.fused ? p.n_ready : (int64_t)0, p.keep_counters);
+                     p.counters, p.ready, p.fused ? p.n_ready : (int64_t)0, p.keep_counters,
+                     p.arrivals, narr);
   return hipGetLastError();
 }
 
@@ -1338,6 +1454,32 @@ hipError_t launch_forward_combine(const ForwardParams& p, hipStream_t st) {
     nt ? go(combine_kernel<true, true>) : go(combine_kernel<true, false>);
   else
     nt ? go(combine_kernel<false, true>) : go(combine_kernel<false, false>);
+  return hipGetLastError();
+}
+
+// With the fused combine and no shared expert: tokens with no kept slot
+// (every choice dropped by the capacity) get the zero row the combine pass
+// would write. One wave per token: its lanes test the k kept flags.
+__global__ __launch_bounds__(256) void zero_unrouted_kernel(const uint8_t* kept, void* O, int64_t S,
+                                                            int64_t H, int64_t k, int out_bf16) {
+  const int lane = threadIdx.x & 63;
+  const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= S) return;
+  bool any = false;
+  for (int64_t j = lane; j < k; j += 64) any = any || kept[t * k + j] != 0;
+  if (__ballot(any)) return;
+  for (int64_t c = lane; c < H; c += 64) {
+    if (out_bf16)
+      reinterpret_cast<bf16_t*>(O)[t * H + c] = 0;
+    else
+      reinterpret_cast<float*>(O)[t * H + c] = 0.f;
+  }
+}
+
+hipError_t launch_zero_unrouted(const ForwardParams& p, hipStream_t st) {
+  if (p.S == 0) return hipSuccess;
+  hipLaunchKernelGGL(zero_unrouted_kernel, dim3((unsigned)((p.S + 3) / 4)), dim3(256), 0, st,
+                     p.kept, p.O, p.S, p.H, p.k, p.out_bf16);
   return hipGetLastError();
 }
 

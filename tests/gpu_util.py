@@ -100,12 +100,12 @@ def block_size_for(wl):
 
 
 def buffers(wl, block_size=None, out_f32=False, atomic_combine=False, sched_quota=False,
-            fused_launch=False):
+            fused_launch=False, extra_flags=0):
     bm = block_size or block_size_for(wl)
     return MoEBuffers(wl.S, wl.H, wl.D, wl.E, wl.k, wl.D_shared, wl.capacity, bm,
                       wl.renormalize, lib_dtype(wl), out_f32=out_f32,
                       atomic_combine=atomic_combine, sched_quota=sched_quota,
-                      fused_launch=fused_launch, device=DEV)
+                      fused_launch=fused_launch, device=DEV, extra_flags=extra_flags)
 
 
 def pack_mxfp8(W):

@@ -87,7 +87,7 @@ def test_gate_topk_validation(lib):
     assert gate(lib, dec, ws=FAKE, wsn=need - 1) == 3   # too small
     assert gate(lib, dec, ws=FAKE + 4, wsn=need) == 2   # misaligned
     s = shape()
-    s.flags = 64                                        # undefined flag bit
+    s.flags = 128                                       # undefined flag bit
     assert gate(lib, s) == 1
 
 
@@ -155,8 +155,16 @@ def test_forward_validation(lib):
     assert fwd(lib, shape(dtype=moe.MOE_F32, fused_launch=True)) == 2
     assert fwd(lib, shape(fused_launch=True, sched_quota=True)) == 2
     s = shape()
-    s.flags = 64                                        # undefined flag bit
+    s.flags = 128                                       # undefined flag bit
     assert fwd(lib, s) == 1
+    # the fused combine: not with the atomic combine, one launch, or MXFP8
+    assert fwd(lib, shape(atomic_combine=True, extra_flags=moe.MOE_COMBINE_FUSED)) == 2
+    assert fwd(lib, shape(fused_launch=True, extra_flags=moe.MOE_COMBINE_FUSED)) == 2
+    assert fwd(lib, shape(dtype=moe.MOE_MXFP8, H=256, D=256, block_size=64,
+                          extra_flags=moe.MOE_COMBINE_FUSED)) == 2
+    # its arrival counters take workspace
+    assert (moe.moe_forward_workspace_bytes(shape(extra_flags=moe.MOE_COMBINE_FUSED))
+            > moe.moe_forward_workspace_bytes(shape()))
     # batched claims and the queue-reset test hook: the two-launch queues only
     for f in (moe.MOE_SCHED_BATCH, moe.MOE_TEST_SKIP_QUEUE_RESET):
         assert fwd(lib, shape(fused_launch=True, extra_flags=f)) == 2
@@ -195,7 +203,7 @@ def test_forward_status_word_layout(lib):
     # the per-GEMM done / exit counters: after both GEMMs' queues, before the status word
     done = int(re.search(r"kDoneBase\s*=\s*(\d+)", common).group(1))
     assert 16 <= done and done + 4 <= word
-    for f in ("MOE_SCHED_BATCH", "MOE_TEST_SKIP_QUEUE_RESET"):
+    for f in ("MOE_SCHED_BATCH", "MOE_TEST_SKIP_QUEUE_RESET", "MOE_COMBINE_FUSED"):
         assert macros[f] == getattr(moe, f)
     for kw in (dict(), dict(S=1, E=1, k=1), dict(dtype=moe.MOE_F32, block_size=128),
                dict(fused_launch=True), dict(atomic_combine=True)):

@@ -191,3 +191,64 @@ def test_quota_scheduler_same_output(orc, name, S, bm):
                     Ws_gate=li.Ws_gate, Ws_down=li.Ws_down, logits=G)
     err, tol = parity(wl, outs[1], ref["O"])
     assert err <= tol
+
+
+FUSED_COMBINE_CASES = [("prefill_bal", 700, 128), ("prefill_bal", 700, 256),
+                       ("prefill_skew", 300, 256), ("dsv3", 40, 256), ("decode", 64, 16),
+                       ("tiny_fp32", 64, 16), ("drops", 200, 32), ("shared_drops", 64, 16)]
+
+
+@pytest.mark.parametrize("name,S,bm", FUSED_COMBINE_CASES)
+def test_fused_combine_same_output(orc, name, S, bm):
+    """The combine inside the down epilogue (last arrival per token and tile
+    adds the token's rows) gives the slot combine pass's output bit for bit:
+    fp32 and bf16 outputs, the shared expert, decode sizes (queue kernel),
+    capacity drops that leave tokens with no kept slot (zero rows), and every
+    routed assignment dropped beside a shared expert."""
+    if name == "drops":
+        wl = _small(wk.BF16, S=S, capacity_factor=0.2)
+    elif name == "shared_drops":
+        wl = _small(wk.BF16, S=S, capacity_factor=0.05, D_shared=64)
+    else:
+        wl = wk.WORKLOADS[name].with_tokens(S)
+    li = wk.draw_layer(wl)
+    L = DeviceLayer(wl, li)
+    G = orc.gate_logits(li.A, li.Wr, li.bias)
+    if name in ("drops", "shared_drops"):
+        kept = orc.layer(li.A, li.Wr, li.bias, li.W_up, li.W_gate, li.W_down, wl.k,
+                         renormalize=wl.renormalize, capacity=wl.capacity, logits=G)["kept"]
+        assert (kept.reshape(wl.S, wl.k).sum(axis=1) == 0).any(), "no token lost every slot"
+    f32_out = None
+    for out_f32 in ((True,) if wl.dtype == wk.F32 else (True, False)):
+        outs = []
+        for flags in (0, moe.MOE_COMBINE_FUSED):
+            buf = buffers(wl, bm, out_f32=out_f32, extra_flags=flags)
+            buf.forward_ws.fill_(0xFF)
+            buf.O.fill_(float("nan"))
+            buf.route(logits_in=dev(G))
+            outs.append(host(L.forward(buf)).copy())
+            torch.cuda.synchronize()
+            assert moe.forward_status(buf.forward_ws) == 0
+        assert np.all(np.isfinite(outs[1])), "non-finite output (a row never written?)"
+        assert np.array_equal(outs[0], outs[1]), f"out_f32={out_f32}: differs from the pass"
+        if out_f32:
+            f32_out = outs[1]
+    ref = orc.layer(li.A, li.Wr, li.bias, li.W_up, li.W_gate, li.W_down, wl.k,
+                    renormalize=wl.renormalize, capacity=wl.capacity, Ws_up=li.Ws_up,
+                    Ws_gate=li.Ws_gate, Ws_down=li.Ws_down, logits=G)
+    err, tol = parity(wl, f32_out, ref["O"])
+    assert err <= tol
+
+
+def test_fused_combine_repeat_calls():
+    """Repeated calls on the same buffers (arrival counters cleared by each
+    call's setup kernel) give the same output bit for bit."""
+    wl = wk.WORKLOADS["prefill_skew"].with_tokens(300)
+    L = DeviceLayer(wl)
+    buf = buffers(wl, 128, out_f32=True, extra_flags=moe.MOE_COMBINE_FUSED)
+    outs = []
+    for _ in range(3):
+        buf.run(L.A, L.Wr, L.W_up, L.W_gate, L.W_down, router_bias=L.bias)
+        torch.cuda.synchronize()
+        outs.append(host(buf.O).copy())
+    assert np.array_equal(outs[0], outs[1]) and np.array_equal(outs[0], outs[2])

@@ -7,6 +7,7 @@ import numpy as np
 import pytest
 import torch
 
+import sparse_expert_ffn_amd as moe
 from sparse_expert_ffn_amd import workloads as wk
 from tests.gpu_util import DeviceLayer, buffers, host
 
@@ -14,14 +15,17 @@ pytestmark = pytest.mark.gpu
 
 # decode: split gate, one-workgroup align, streaming down kernel; prefill_skew
 # at 300 tokens: fused gate + top-k, queue kernels; dsv3: the shared expert
-CASES = [("decode", 64, 16), ("prefill_skew", 300, 128), ("dsv3", 100, 256)]
+# (the last case with the combine inside the down epilogue: its arrival
+# counters are cleared by the same fill kernel)
+CASES = [("decode", 64, 16, 0), ("prefill_skew", 300, 128, 0), ("dsv3", 100, 256, 0),
+         ("prefill_skew", 300, 128, moe.MOE_COMBINE_FUSED)]
 
 
-@pytest.mark.parametrize("name,S,bm", CASES)
-def test_captured_step_replays_match_eager(name, S, bm):
+@pytest.mark.parametrize("name,S,bm,flags", CASES)
+def test_captured_step_replays_match_eager(name, S, bm, flags):
     wl = wk.WORKLOADS[name].with_tokens(S)
     L = DeviceLayer(wl)
-    buf = buffers(wl, bm, out_f32=True)
+    buf = buffers(wl, bm, out_f32=True, extra_flags=flags)
 
     def step():
         buf.run(L.A, L.Wr, L.W_up, L.W_gate, L.W_down, L.Ws_up, L.Ws_gate, L.Ws_down,
