@@ -147,10 +147,17 @@ __device__ __forceinline__ void wait_vmcnt() {
 //  - B's column pairs are swizzled by ((k & 3) << 1) | ((k >> 3) & 1), so that
 //    the two column halves a read's 32 lanes address at the same k-rows, and
 //    the k-rows 8 apart, fall in different 32-byte slots.
+// A64: A is loaded in 64-K stages of its own (128 bytes, a whole cache line,
+// of each gathered row per load) while B keeps 32-K stages (BK = 32). LDS slot
+// s holds A stage s and B stage s side by side; B stage kt sits in slot
+// kt % NSTAGE and A stage kt / 2 in slot (kt / 2) % NSTAGE. Each 32-K step
+// issues B stage kt + NSTAGE - 1 and one half of the loads of A stage
+// kt / 2 + NSTAGE - 1, so every step issues the same number of loads and one
+// vmcnt bound covers both rings.
 // Each 32-column step of K adds its products in the same order for any BM, so
 // a half tile reproduces the whole tile's sums bit for bit (for the same MF).
 template <int BM_, int NB_, int NW_ = 8, int BK_ = 64, int LDS_BUDGET = 144 * 1024,
-          bool B_STREAM = false, bool VALU_SGPR = false, int MF = 16>
+          bool B_STREAM = false, bool VALU_SGPR = false, int MF = 16, bool A64 = false>
 struct TileGemmDirect {
   static constexpr bool DIRECT = true;  // the LDS-direct core (vs gemm_tile.h)
   static constexpr int BM = BM_, BN = 128, NB = NB_;
@@ -158,8 +165,9 @@ struct TileGemmDirect {
   static constexpr int THREADS = 64 * NW;
   static constexpr int ES = 2;
   static constexpr int BK = BK_;              // 32 or 64 K elements per stage
-  static constexpr int ACH = BK / 8;          // 16-byte chunks per A row
-  static constexpr int A_ROWB = BK * ES;
+  static constexpr int A_BK = A64 ? 64 : BK;  // K elements per A stage
+  static constexpr int ACH = A_BK / 8;        // 16-byte chunks per A row
+  static constexpr int A_ROWB = A_BK * ES;
   static constexpr int B_ROWB = BN * ES;      // 256
   static constexpr int A_LDS = BM * A_ROWB;
   static constexpr int B_MAT = BK * B_ROWB;   // per matrix per stage
@@ -183,9 +191,12 @@ struct TileGemmDirect {
   static constexpr int B_INSTR = B_LDS / 1024;
   static constexpr int A_PW = (A_INSTR + NW - 1) / NW;   // per wave (upper bound)
   static constexpr int B_PW = B_INSTR / NW;
+  static constexpr int A_HPW = A_PW / 2;  // A64: A loads per wave and 32-K step
   // loads every wave issues per stage (waves with fewer A units wait for less)
-  static constexpr int MIN_PW = A_INSTR / NW + B_PW;
+  static constexpr int MIN_PW = A64 ? A_HPW + B_PW : A_INSTR / NW + B_PW;
   static_assert((NSTAGE - 2) * (A_PW + B_PW) < 64, "vmcnt range");
+  static_assert(!A64 || (BK == 32 && A_INSTR % NW == 0 && A_PW % 2 == 0),
+                "A64: 32-K B stages, A loads split evenly over waves and steps");
   static_assert(B_INSTR % NW == 0, "B loads split evenly over the waves");
   static_assert(MI >= 1 && NI >= 1, "tile too small for the waves");
   static_assert(LDS_BYTES <= 160 * 1024, "LDS");
@@ -251,7 +262,8 @@ struct TileGemmDirect {
     rsrc_a = make_srd(a_base, a_bytes);
 #pragma unroll
     for (int m = 0; m < NB; ++m) rsrc_b[m] = make_srd(B[m], b_bytes[m]);
-    a_stage_bytes = a_slab_rows ? (uint32_t)(BK / 32 * a_slab_rows * 64) : (uint32_t)(BK * ES);
+    a_stage_bytes =
+        a_slab_rows ? (uint32_t)(A_BK / 32 * a_slab_rows * 64) : (uint32_t)(A_BK * ES);
     b_stage_bytes = (uint32_t)(BK * ldb * ES);
 #pragma unroll
     for (int t = 0; t < A_PW; ++t) {
@@ -281,34 +293,65 @@ struct TileGemmDirect {
   // its B loads) of K stage kt into the stage buffer `base`.
   // SGPR_FROM_VALU: the caller cannot rule out that the compiler restores the
   // buffer descriptors from VGPR lanes right before (see dma16).
-  static constexpr int NPIECE = A_PW + B_PW;
+  static constexpr int NPIECE = A64 ? A_HPW + B_PW : A_PW + B_PW;  // loads per wave and step
+  // This wave's A load t (0 <= t < A_PW) of A stage ka into the A buffer abuf;
+  // t = t0, or t0 + A_HPW if hi (t0 a compile-time index after unrolling,
+  // so that aoff stays in registers).
   template <bool SGPR_FROM_VALU = VALU_SGPR>
-  __device__ __forceinline__ void issue_piece(char* base, int kt, int idx) {
+  __device__ __forceinline__ void issue_a(char* abuf, int ka, int t0, bool hi = false) {
     // wave-uniform (scalar) so the buffer resources stay in SGPRs
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    if (idx < A_PW) {
-      const int t = idx;
-      const int q = wave + NW * t;
-      if (q < A_INSTR) {  // wave-uniform
-        const int64_t k0 = (int64_t)kt * BK;
-        const int lane = threadIdx.x & 63;
-        const int r = q * (1024 / A_ROWB) + lane / ACH;
-        const int c = (lane % ACH) ^ aswz(r);
-        const uint32_t o = (aoff[t] != kOob && k0 + c * 8 < K_) ? aoff[t] + (uint32_t)kt * a_stage_bytes
-                                                                : kOob;
-        dma16<SGPR_FROM_VALU>(rsrc_a, o, base + q * 1024);
+    int t = t0;
+    uint32_t ao = aoff[t0];
+    if constexpr (A64) {
+      // select between the two values, not their addresses (a select of
+      // addresses would index aoff at run time and move it to memory)
+      uint32_t ao_hi = aoff[t0 + A_HPW < A_PW ? t0 + A_HPW : 0];
+      asm("" : "+v"(ao), "+v"(ao_hi));
+      if (hi) {
+        t = t0 + A_HPW;
+        ao = ao_hi;
       }
-    } else {
-      const int t = idx - A_PW;
-      const int q = wave + NW * t;
-      const int m = q / (B_MAT / 1024);  // wave-uniform
-      const uint32_t o = boff[t] == kOob ? kOob : boff[t] + (uint32_t)kt * b_stage_bytes;
-      i32x4_t rb = rsrc_b[0];
-      if constexpr (NB > 1) {
-        if (m == 1) rb = rsrc_b[1];
-      }
-      dma16<SGPR_FROM_VALU, B_STREAM>(rb, o, base + A_LDS + q * 1024);
     }
+    const int q = wave + NW * t;
+    if (q < A_INSTR) {  // wave-uniform
+      const int64_t k0 = (int64_t)ka * A_BK;
+      const int lane = threadIdx.x & 63;
+      const int r = q * (1024 / A_ROWB) + lane / ACH;
+      const int c = (lane % ACH) ^ aswz(r);
+      const uint32_t o = (ao != kOob && k0 + c * 8 < K_) ? ao + (uint32_t)ka * a_stage_bytes : kOob;
+      dma16<SGPR_FROM_VALU>(rsrc_a, o, abuf + q * 1024);
+    }
+  }
+  // This wave's B load t (0 <= t < B_PW) of B stage kt into the B buffer bbuf.
+  template <bool SGPR_FROM_VALU = VALU_SGPR>
+  __device__ __forceinline__ void issue_b(char* bbuf, int kt, int t) {
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int q = wave + NW * t;
+    const int m = q / (B_MAT / 1024);  // wave-uniform
+    const uint32_t o = boff[t] == kOob ? kOob : boff[t] + (uint32_t)kt * b_stage_bytes;
+    i32x4_t rb = rsrc_b[0];
+    if constexpr (NB > 1) {
+      if (m == 1) rb = rsrc_b[1];
+    }
+    dma16<SGPR_FROM_VALU, B_STREAM>(rb, o, bbuf + q * 1024);
+  }
+  template <bool SGPR_FROM_VALU = VALU_SGPR>
+  __device__ __forceinline__ void issue_piece(char* base, int kt, int idx) {
+    if (idx < A_PW)
+      issue_a<SGPR_FROM_VALU>(base, kt, idx);
+    else
+      issue_b<SGPR_FROM_VALU>(base + A_LDS, kt, idx - A_PW);
+  }
+  // A64: load idx (0 <= idx < NPIECE) of 32-K step kt's share: half kt & 1 of
+  // A stage kt / 2 + NSTAGE - 1 into anext, then B stage kt + NSTAGE - 1 into
+  // bnext (both stage slots).
+  __device__ __forceinline__ void issue_piece64(char* anext, char* bnext, int kt, int idx) {
+    const int d = NSTAGE - 1;
+    if (idx < A_HPW)
+      issue_a(anext, (kt >> 1) + d, idx, kt & 1);
+    else
+      issue_b(bnext + A_LDS, kt + d, idx - A_HPW);
   }
 
   // All LDS-direct loads of K stage kt into the stage buffer `base`.
@@ -350,12 +393,14 @@ struct TileGemmDirect {
       }
   }
 
-  __device__ __forceinline__ uint4 read_a(const char* base, int ks, int i) const {
+  // A fragment of row block i at K step ks of the A stage at base, plus ak
+  // chunks (A64: 4 for the second 32-K half of an A stage).
+  __device__ __forceinline__ uint4 read_a(const char* base, int ks, int i, int ak = 0) const {
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int wm0 = (wave / WN) * (BM / WM);
     const int r = MF == 32 ? wm0 + i * 32 + (lane & 31) : wm0 + i * 16 + (lane & 15);
-    const int c = MF == 32 ? ks * 2 + (lane >> 5) : ks * 4 + (lane >> 4);
+    const int c = (MF == 32 ? ks * 2 + (lane >> 5) : ks * 4 + (lane >> 4)) + ak;
     return *reinterpret_cast<const uint4*>(base + r * A_ROWB + ((c ^ aswz(r)) << 4));
   }
 
@@ -383,8 +428,11 @@ struct TileGemmDirect {
   // the first ADIST A fragments, then alternates the MFMAs of block i with
   // the read of block i + ADIST: ADIST LDS reads stay in flight behind the
   // matrix work.
+  // A64: the A fragments come from abase at chunk offset ak instead of base.
   template <int LO, int HI, bool READ_B, typename Between>
-  __device__ __forceinline__ void compute_range(const char* base, Between between) {
+  __device__ __forceinline__ void compute_range(const char* base, Between between,
+                                                const char* abase = nullptr, int ak = 0) {
+    const char* ab = A64 ? abase : base;
     if constexpr (HI > LO) {
       constexpr int NBLK = HI - LO;
       constexpr int D = ADIST < NBLK ? ADIST : NBLK;
@@ -393,11 +441,11 @@ struct TileGemmDirect {
         if constexpr (READ_B) read_frags_b(base, ks, fb_[ks]);
         uint4 a[NBLK];
 #pragma unroll
-        for (int i = 0; i < D; ++i) a[i] = read_a(base, ks, LO + i);
+        for (int i = 0; i < D; ++i) a[i] = read_a(ab, ks, LO + i, ak);
         __builtin_amdgcn_sched_group_barrier(0x100, (READ_B ? 2 * NB * NI : 0) + D, 0);
 #pragma unroll
         for (int i = 0; i < NBLK; ++i) {
-          if (i + D < NBLK) a[i + D] = read_a(base, ks, LO + i + D);
+          if (i + D < NBLK) a[i + D] = read_a(ab, ks, LO + i + D, ak);
           mfma_row(LO + i, a[i], fb_[ks].b);
           __builtin_amdgcn_sched_group_barrier(0x008, NB * NI, 0);
           if (i + D < NBLK) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
@@ -470,6 +518,39 @@ struct TileGemmDirect {
     }
   }
 
+  // A64 K loop: 32-K step kt reads B stage kt (slot kt % NSTAGE) and half
+  // kt & 1 of A stage kt / 2 (slot (kt / 2) % NSTAGE). At the top of step kt
+  // every load issued up to step kt - NSTAGE + 1 must have landed: B stage kt
+  // was issued in step kt - NSTAGE + 1 and the second half of A stage kt / 2
+  // in step 2 (kt / 2) - 2 NSTAGE + 3 at the latest, both no later. A stage
+  // kt / 2 + NSTAGE - 1 goes into the slot of A stage kt / 2 - 1, whose last
+  // reader was step kt - 1 at the latest (done at this step's barrier), and B
+  // stage kt + NSTAGE - 1 into the slot of B stage kt - 1.
+  template <int NA>
+  __device__ __forceinline__ void kloop64(char* lds, int nk) {
+    int bslot = 0, bnext = NSTAGE - 1;
+    int aslot = 0, anext = NSTAGE - 1;
+    for (int kt = 0; kt < nk; ++kt) {
+      wait_vmcnt<(NSTAGE - 2) * MIN_PW>();
+      __syncthreads();
+      char* an = lds + anext * STAGE;
+      char* bn = lds + bnext * STAGE;
+      compute_range<0, NA, true>(
+          lds + bslot * STAGE, [&](int i) {
+            if (i < NPIECE) issue_piece64(an, bn, kt, i);
+          },
+          lds + aslot * STAGE, (kt & 1) * (BK / 8));
+#pragma unroll
+      for (int i = NA * KSTEPS; i < NPIECE; ++i) issue_piece64(an, bn, kt, i);
+      bslot = bslot + 1 == NSTAGE ? 0 : bslot + 1;
+      bnext = bnext + 1 == NSTAGE ? 0 : bnext + 1;
+      if (kt & 1) {
+        aslot = aslot + 1 == NSTAGE ? 0 : aslot + 1;
+        anext = anext + 1 == NSTAGE ? 0 : anext + 1;
+      }
+    }
+  }
+
   // ---- ping-pong schedule (two waves per SIMD alternate roles)
   // Waves 0 .. NW/2-1 form group 0, waves NW/2 .. NW-1 group 1; waves are
   // placed on SIMDs round-robin, so each SIMD holds one wave of each group.
@@ -493,7 +574,7 @@ struct TileGemmDirect {
   //  - the slot of stage s is read by G0 in phase 2s-1 and by G1 in phase
   //    2s; its next stage (s+NSTAGE) is loaded from phase 2s+1 on;
   //  - every wave passes the same barriers (no barrier depends on the group).
-  static constexpr bool PP_OK = MOE_PINGPONG && NW == 8 && MI >= 2 && NSTAGE >= 3;
+  static constexpr bool PP_OK = MOE_PINGPONG && NW == 8 && MI >= 2 && NSTAGE >= 3 && !A64;
   uint4 fa_[PP_OK ? KSTEPS : 1][PP_OK ? MI : 1];  // A fragments of one stage
 
   template <int NA>
@@ -568,12 +649,16 @@ struct TileGemmDirect {
   template <int NA = MI>
   __device__ __forceinline__ void kloop_n(char* lds, int nk, int nact) {
     if constexpr (NA == 0) {
-      if constexpr (PP_OK)
+      if constexpr (A64)
+        kloop64<0>(lds, nk);
+      else if constexpr (PP_OK)
         kloop_pp<0>(lds, nk);
       else
         kloop<0>(lds, nk);
     } else if (nact >= NA) {
-      if constexpr (PP_OK)
+      if constexpr (A64)
+        kloop64<NA>(lds, nk);
+      else if constexpr (PP_OK)
         kloop_pp<NA>(lds, nk);
       else
         kloop<NA>(lds, nk);
@@ -597,8 +682,24 @@ struct TileGemmDirect {
     // latency overlaps the first stages' loads (measured: up/gate -1% at
     // prefill sizes).
     __syncthreads();  // every wave is done with the ring
+    if constexpr (A64) {
+      // the loads steps -2 (NSTAGE - 1) .. -1 would have issued, in order: A
+      // stages 0 .. NSTAGE - 2 and B stages 0 .. NSTAGE - 2
 #pragma unroll
-    for (int s = 0; s + 1 < NSTAGE; ++s) issue_stage(lds + s * STAGE, s);
+      for (int v = -2 * (NSTAGE - 1); v < 0; ++v) {
+        const int ka = (v >> 1) + NSTAGE - 1;  // arithmetic shift: floor(v / 2)
+        const int kb = v + NSTAGE - 1;
+        if (ka >= 0)
+#pragma unroll
+          for (int t = 0; t < A_HPW; ++t) issue_a(lds + ka * STAGE, ka, t, v & 1);
+        if (kb >= 0)
+#pragma unroll
+          for (int t = 0; t < B_PW; ++t) issue_b(lds + kb * STAGE + A_LDS, kb, t);
+      }
+    } else {
+#pragma unroll
+      for (int s = 0; s + 1 < NSTAGE; ++s) issue_stage(lds + s * STAGE, s);
+    }
     kloop_n(lds, nk, nact);
     wait_vmcnt<0>();
   }

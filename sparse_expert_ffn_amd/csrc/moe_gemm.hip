@@ -53,9 +53,21 @@ template <int BM>
 constexpr int mfma_shape() {
   return MOE_MFMA32 && BM >= 128 ? 32 : 16;
 }
+// A in 64-K stages (whole 128-byte lines of the gathered token rows) for the
+// up/gate tiles of 256 rows (STAGING 2 marks the up/gate GEMM): 1 for the
+// tiles that stream their weights (measured faster there, slower where the
+// weights stay in the caches), 2 for every such tile, 0 for none.
+#ifndef MOE_A64
+#define MOE_A64 1
+#endif
+template <int BM, int NB, int STAGING, bool BS>
+constexpr bool a64_tile() {
+  return STAGING == 2 && BM >= 256 && stage_k<BM>() == 32 && (MOE_A64 == 2 || (MOE_A64 == 1 && BS));
+}
 template <int BM, int NB, int STAGING, bool BS>
 struct TileSel<bf16_t, BM, NB, STAGING, BS> {
-  using type = TileGemmDirect<BM, NB, 8, stage_k<BM>(), 144 * 1024, BS, false, mfma_shape<BM>()>;
+  using type = TileGemmDirect<BM, NB, 8, stage_k<BM>(), 144 * 1024, BS, false, mfma_shape<BM>(),
+                              a64_tile<BM, NB, STAGING, BS>()>;
 };
 
 template <typename TG>

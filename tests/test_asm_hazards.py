@@ -181,12 +181,12 @@ def test_scanner_follows_branches_and_back_edges():
 @pytest.mark.skipif(shutil.which(os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")) is None,
                     reason="hipcc not available")
 @pytest.mark.parametrize("source,variant", [("moe_gemm.hip", "plain"), ("moe_gemm.hip", "trace"),
-                                            ("moe_gemm.hip", "mfma32"), ("moe_mx.hip", "plain"),
-                                            ("moe_mx.hip", "trace")])
+                                            ("moe_gemm.hip", "mfma32"), ("moe_gemm.hip", "a64"),
+                                            ("moe_mx.hip", "plain"), ("moe_mx.hip", "trace")])
 def test_gemm_kernels_have_no_valu_sgpr_hazard(tmp_path, variant, source):
     """Every source with LDS-direct loads, in both library builds (the plain
     one and the one with timing records), and the GEMMs with the 32x32x16
-    MFMA core option."""
+    MFMA core option and with 64-K A stages on every 256-row up/gate tile."""
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
     src = os.path.join(buildlib.PKG, "csrc", source)
     out = tmp_path / "kernels.s"
@@ -195,6 +195,8 @@ def test_gemm_kernels_have_no_valu_sgpr_hazard(tmp_path, variant, source):
         flags += buildlib.TRACE_FLAGS
     elif variant == "mfma32":
         flags += ["-DMOE_MFMA32=1"]
+    elif variant == "a64":
+        flags += ["-DMOE_A64=2"]
     cmd = [hipcc, *flags, "-I", os.path.join(buildlib.ROOT, "include"), "-I",
            os.path.join(buildlib.PKG, "csrc"), "-S", "--cuda-device-only", src, "-o", str(out)]
     r = subprocess.run(cmd, capture_output=True, text=True)
