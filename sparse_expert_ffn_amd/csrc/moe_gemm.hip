@@ -1244,8 +1244,9 @@ static bool down_stream_ok(const ForwardParams& p) {
 // order then runs each m-block's n-tiles back to back and no task reuses
 // another's weight strip, so the weight loads take the non-temporal hint
 // (measured: decode -9% per step, dsv3 -1%; with several m-blocks per expert
-// sharing each strip in L2, prefill, the hint cost 1-2%). A cache hint only:
-// the results are the same either way.
+// sharing each strip in L2, prefill, the hint cost 1-2%). The 256-row up/gate
+// tiles then also load A in 64-K stages (a64_tile). Cache hint and load
+// shape only: the results are the same either way.
 static bool weights_streamed(const ForwardParams& p, int BM) {
   return p.E > 0 && 2 * ((p.F + p.E - 1) / p.E) <= BM;
 }
