@@ -517,6 +517,9 @@ __device__ __forceinline__ int64_t upgate_task(const ForwardParams& p, const Tas
       decode_task(t, ts.nb_r, ts.nn_r, ts.gb_r, b, j);
     else
       decode_task(t - ts.t_r, ts.nb_s, ts.nn_s, kGroupBlocks, b, j);
+    // the block's expert, loaded before the row barrier so that its latency
+    // overlaps the sorted ids' (it does not depend on them)
+    const int64_t e_blk = shared ? -1 : (int64_t)__builtin_amdgcn_readfirstlane(p.expert_ids[b]);
     if (threadIdx.x < BM) {
       const int r = threadIdx.x;
       int tok;
@@ -537,8 +540,7 @@ __device__ __forceinline__ int64_t upgate_task(const ForwardParams& p, const Tas
     const int64_t n0 = j * BN;
     const char* Bm[2];
     if (!shared) {
-      const int64_t e = __builtin_amdgcn_readfirstlane(p.expert_ids[b]);
-      const size_t off = (size_t)e * p.H * p.D * sizeof(T);
+      const size_t off = (size_t)e_blk * p.H * p.D * sizeof(T);
       Bm[0] = reinterpret_cast<const char*>(p.Wu) + off;
       Bm[1] = reinterpret_cast<const char*>(p.Wg) + off;
     } else {
@@ -732,6 +734,10 @@ __device__ __forceinline__ void down_task(const ForwardParams& p, const TaskSpac
     __shared__ int s_gave_up;
     const bool gave_up = before_rows(shared ? ts.nb_r + b : b, shared);
     if (WAITS && threadIdx.x == 0) s_gave_up = gave_up ? 1 : 0;
+    // the block's expert, loaded before the row barrier (its latency overlaps
+    // the sorted ids'); the router weights only where the epilogue applies
+    // them (atomic combine: the slot rows are unweighted)
+    const int64_t e_blk = shared ? -1 : (int64_t)__builtin_amdgcn_readfirstlane(p.expert_ids[b]);
     if (threadIdx.x < BM) {
       const int r = threadIdx.x;
       if (!shared) {
@@ -739,7 +745,7 @@ __device__ __forceinline__ void down_task(const ForwardParams& p, const TaskSpac
         if (f < p.F) {
           s_tok[r] = (int)(f / p.k);
           s_f[r] = f;
-          s_w[r] = p.topk_w[f];
+          s_w[r] = p.atomic_combine ? p.topk_w[f] : 0.f;
         } else {
           s_tok[r] = -1;
           s_f[r] = -1;
@@ -757,8 +763,7 @@ __device__ __forceinline__ void down_task(const ForwardParams& p, const TaskSpac
     const int64_t n0 = j * NT;
     const char* Wb;
     if (!shared) {
-      const int64_t e = __builtin_amdgcn_readfirstlane(p.expert_ids[b]);
-      Wb = reinterpret_cast<const char*>(p.Wd) + (size_t)e * p.D * p.H * sizeof(T);
+      Wb = reinterpret_cast<const char*>(p.Wd) + (size_t)e_blk * p.D * p.H * sizeof(T);
     } else {
       Wb = reinterpret_cast<const char*>(p.Wsd);
     }
