@@ -49,6 +49,8 @@ def parse():
     ap.add_argument("--combine", choices=("pass", "fused"), default="pass",
                     help="the router-weighted combine as a pass of its own after the down "
                          "GEMM (default) or inside its epilogue (last arrival per token)")
+    ap.add_argument("--split-tail", action="store_true",
+                    help="long-tail splitting: each up/gate queue's last tasks as two row halves")
     ap.add_argument("--launch", choices=("two", "one"), default="two",
                     help="the expert GEMMs as two persistent launches (up/gate, then down) "
                          "or as one (down tasks wait per m-block for its up/gate tasks)")
@@ -246,7 +248,8 @@ def setup_workload(wl, args, torch, moe, dev="cuda"):
                      wl.renormalize, dtype, sched_quota=args.sched == "quota",
                      fused_launch=args.launch == "one", device=dev,
                      extra_flags=(moe.MOE_SCHED_BATCH if args.sched == "batch" else 0) |
-                     (moe.MOE_COMBINE_FUSED if args.combine == "fused" else 0))
+                     (moe.MOE_COMBINE_FUSED if args.combine == "fused" else 0) |
+                     (moe.MOE_SPLIT_TAIL if args.split_tail else 0))
     stream = torch.cuda.current_stream()
     n_step = [0]
 
@@ -353,6 +356,7 @@ def measure(wl, args, steps, warmup, torch, moe, full=True):
     config = {"workload": wl.name, "S": wl.S, "H": wl.H, "D": wl.D, "E": wl.E, "k": wl.k,
               "D_shared": wl.D_shared, "capacity": wl.capacity, "block_size": bm,
               "scheduler": args.sched, "launch": args.launch, "combine": args.combine,
+              "split_tail": bool(args.split_tail),
               "weight_copies": n_copies,
               "parallelism": "single GPU"}
     if wl.mxfp8:

@@ -143,6 +143,16 @@ typedef struct {
  * no shared expert get a zero row from a small kernel. The down GEMM then
  * runs on the task queues at every size. */
 #define MOE_COMBINE_FUSED 64
+/* flags: long-tail splitting in the up/gate GEMM (the Weave review's tail
+ * handling, section 5.2, pitfall 2). Each task queue's last n mod R tasks (n
+ * tasks on a queue served by R workgroups) run as two row halves, each on the
+ * half-row tile core with the whole workgroup, so the last round of tasks is
+ * half as long. bf16 tiles of 64 rows or more; elsewhere, and with
+ * MOE_SCHED_QUOTA or MOE_FUSED_LAUNCH, it has no effect. Same results, bit
+ * for bit. Off by default: the half-tile core in the kernel costs the whole
+ * tiles about 2% where no task is split (balanced routing), and saves 2-4%
+ * of the up/gate GEMM under a skewed routing. */
+#define MOE_SPLIT_TAIL 128
 
 /* The call's status word: an int32 at this byte offset of the moe_forward
  * workspace. Every moe_forward call sets it to 0 before its GEMMs run; once

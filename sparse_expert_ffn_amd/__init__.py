@@ -24,7 +24,7 @@ __all__ = ["MOE_F32", "MOE_BF16", "MOE_MXFP8", "moe_mxfp8_weight_bytes", "moe_pa
            "build",
            "LIB_PATH", "STATUS", "MOE_FORWARD_STATUS_OFFSET", "MOE_STATUS_READY_TIMEOUT",
            "MOE_STATUS_TASKS_LOST", "MOE_STATUS_QUEUE_COUNT", "MOE_SCHED_BATCH",
-           "MOE_TEST_SKIP_QUEUE_RESET", "MOE_COMBINE_FUSED"]
+           "MOE_TEST_SKIP_QUEUE_RESET", "MOE_COMBINE_FUSED", "MOE_SPLIT_TAIL"]
 
 # SPARSE_EXPERT_FFN_LIB: load the library from another path (e.g. a build
 # with different compile-time tile settings)
@@ -41,6 +41,7 @@ MOE_FUSED_LAUNCH = 8  # up/gate and down GEMMs in one persistent launch (bf16)
 MOE_SCHED_BATCH = 16  # batched claims: 4 tasks per queue atomic
 MOE_TEST_SKIP_QUEUE_RESET = 32  # testing the status word: keep the previous call's queue counters
 MOE_COMBINE_FUSED = 64  # the deterministic combine inside the down GEMM's epilogue
+MOE_SPLIT_TAIL = 128  # long-tail splitting: the up/gate queues' last tasks as two row halves
 # byte offset of the int32 status word in the moe_forward workspace, and its bits
 MOE_FORWARD_STATUS_OFFSET = 128
 MOE_STATUS_READY_TIMEOUT = 1

@@ -24,7 +24,8 @@ bool fits_buffer(int64_t bytes) { return bytes >= 0 && bytes < ((int64_t)1 << 31
 moe_status check_routing_dims(const moe_shape* s) {
   if (s == nullptr) return MOE_ERR_INVALID_ARGUMENT;
   if ((s->flags & ~(MOE_OUTPUT_F32 | MOE_COMBINE_ATOMIC | MOE_SCHED_QUOTA | MOE_FUSED_LAUNCH |
-                    MOE_SCHED_BATCH | MOE_TEST_SKIP_QUEUE_RESET | MOE_COMBINE_FUSED)) != 0)
+                    MOE_SCHED_BATCH | MOE_TEST_SKIP_QUEUE_RESET | MOE_COMBINE_FUSED |
+                    MOE_SPLIT_TAIL)) != 0)
     return MOE_ERR_INVALID_ARGUMENT;
   if (s->dtype != MOE_F32 && s->dtype != MOE_BF16 && s->dtype != MOE_MXFP8)
     return MOE_ERR_INVALID_ARGUMENT;
@@ -302,6 +303,7 @@ moe_status forward_impl(const moe_shape* shape, const void* A, const void* W_up,
   p.arrivals = reinterpret_cast<int*>(ws + L.arr);
   p.arr_tiles = arrival_tiles(shape);
   p.claim_batch = (shape->flags & MOE_SCHED_BATCH) ? kClaimBatch : 1;
+  p.split_tail = (shape->flags & MOE_SPLIT_TAIL) ? 1 : 0;
   p.keep_counters = (shape->flags & MOE_TEST_SKIP_QUEUE_RESET) ? 1 : 0;
   // Slot rows far larger than the 256 MB MALL (DeepSeek-V3 sizes: 0.94 GB)
   // go to HBM and come back from it anyway: the down kernel stores them and

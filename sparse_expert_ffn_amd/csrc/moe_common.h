@@ -135,6 +135,7 @@ struct ForwardParams {
   int* arrivals;          // fused combine: [S][arr_tiles] rows arrived per token and tile
   int64_t arr_tiles;      // 256-column tiles of H
   int claim_batch;        // task parts claimed per queue atomic (1, or kClaimBatch)
+  int split_tail;         // 1: the up/gate queues' last tasks run as two row halves
   int keep_counters;      // testing: the setup kernel leaves the queue counters as they are
   void* a_blk;            // MXFP8: stage-blocked quantised rows of the routed m-blocks
   void* as_blk;           // MXFP8: the same for the shared expert's m-blocks

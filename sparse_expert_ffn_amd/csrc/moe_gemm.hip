@@ -570,7 +570,10 @@ __device__ __forceinline__ int64_t upgate_task(const ForwardParams& p, const Tas
   }
 }
 
-template <typename T, int BM, int BN, bool BS>
+// HALVES: the instance with the half-row core, for the long-tail split
+// (p.split_tail); the other holds whole tiles only (the second core costs the
+// whole tiles about 2% where nothing is split).
+template <typename T, int BM, int BN, bool BS, bool HALVES>
 __global__ __launch_bounds__((tile_threads<T, BM, 2, 2>()), 1) void upgate_kernel(ForwardParams p) {
   using TG = typename TileSel<T, BM, 2, 2, BS>::type;
   extern __shared__ __align__(16) char smem[];
@@ -580,7 +583,7 @@ __global__ __launch_bounds__((tile_threads<T, BM, 2, 2>()), 1) void upgate_kerne
   Claimer cs(blockIdx.x % kXcds);
   QuotaState qs = quota_init(p.E);
   using TH = typename HalfSel<T, BM, 2, 2, BS>::type;
-  constexpr bool kHalves = !std::is_void<TH>::value;
+  constexpr bool kHalves = HALVES && !std::is_void<TH>::value;
   const bool split = kHalves && !p.sched_quota;
   TG g;
   for (;;) {
@@ -1256,16 +1259,25 @@ static bool weights_streamed(const ForwardParams& p, int BM) {
   return p.E > 0 && 2 * ((p.F + p.E - 1) / p.E) <= BM;
 }
 
-template <typename T, int BM>
-static hipError_t launch_upgate_t(const ForwardParams& p, hipStream_t st) {
+template <typename T, int BM, bool BS>
+static hipError_t launch_upgate_bs(const ForwardParams& p, hipStream_t st) {
   constexpr int BN = upgate_bn<BM>();
-  if constexpr (sizeof(T) == 2) {
-    if (weights_streamed(p, BM))
-      return launch_persistent(upgate_kernel<T, BM, BN, true>, lds_bytes<T, BM, 2, 2>(),
+  constexpr bool kHas = !std::is_void<typename HalfSel<T, BM, 2, 2, BS>::type>::value;
+  if constexpr (kHas) {
+    if (p.split_tail && !p.sched_quota)
+      return launch_persistent(upgate_kernel<T, BM, BN, BS, true>, lds_bytes<T, BM, 2, 2>(),
                                tile_threads<T, BM, 2, 2>(), p, st);
   }
-  return launch_persistent(upgate_kernel<T, BM, BN, false>, lds_bytes<T, BM, 2, 2>(),
+  return launch_persistent(upgate_kernel<T, BM, BN, BS, false>, lds_bytes<T, BM, 2, 2>(),
                            tile_threads<T, BM, 2, 2>(), p, st);
+}
+
+template <typename T, int BM>
+static hipError_t launch_upgate_t(const ForwardParams& p, hipStream_t st) {
+  if constexpr (sizeof(T) == 2) {
+    if (weights_streamed(p, BM)) return launch_upgate_bs<T, BM, true>(p, st);
+  }
+  return launch_upgate_bs<T, BM, false>(p, st);
 }
 
 template <typename T, int BM>

@@ -87,7 +87,7 @@ def test_gate_topk_validation(lib):
     assert gate(lib, dec, ws=FAKE, wsn=need - 1) == 3   # too small
     assert gate(lib, dec, ws=FAKE + 4, wsn=need) == 2   # misaligned
     s = shape()
-    s.flags = 128                                       # undefined flag bit
+    s.flags = 256                                       # undefined flag bit
     assert gate(lib, s) == 1
 
 
@@ -155,7 +155,7 @@ def test_forward_validation(lib):
     assert fwd(lib, shape(dtype=moe.MOE_F32, fused_launch=True)) == 2
     assert fwd(lib, shape(fused_launch=True, sched_quota=True)) == 2
     s = shape()
-    s.flags = 128                                       # undefined flag bit
+    s.flags = 256                                       # undefined flag bit
     assert fwd(lib, s) == 1
     # the fused combine: not with the atomic combine, one launch, or MXFP8
     assert fwd(lib, shape(atomic_combine=True, extra_flags=moe.MOE_COMBINE_FUSED)) == 2
@@ -169,6 +169,11 @@ def test_forward_validation(lib):
     for f in (moe.MOE_SCHED_BATCH, moe.MOE_TEST_SKIP_QUEUE_RESET):
         assert fwd(lib, shape(fused_launch=True, extra_flags=f)) == 2
         assert fwd(lib, shape(sched_quota=True, extra_flags=f)) == 2
+    # long-tail splitting: a kernel choice, with or without the other options
+    assert (moe.moe_forward_workspace_bytes(shape(extra_flags=moe.MOE_SPLIT_TAIL))
+            == moe.moe_forward_workspace_bytes(shape()) > 0)
+    assert moe.moe_forward_workspace_bytes(shape(sched_quota=True,
+                                                 extra_flags=moe.MOE_SPLIT_TAIL)) > 0
     assert moe.moe_forward_workspace_bytes(shape(dtype=moe.MOE_F32, fused_launch=True)) == 0
     # readiness counters: one per routed and per shared m-block, more workspace
     assert (moe.moe_forward_workspace_bytes(shape(D_shared=64, fused_launch=True))

@@ -30,11 +30,12 @@ BATCH_CASES = [("prefill_skew", 300, 128), ("prefill_skew", 300, 256), ("dsv3", 
                ("decode", 64, 16), ("tiny_fp32", 64, 16), ("prefill_bal_mxfp8", 300, 128)]
 
 
+@pytest.mark.parametrize("split", [0, moe.MOE_SPLIT_TAIL])
 @pytest.mark.parametrize("name,S,bm", BATCH_CASES)
-def test_batched_claims_same_output(orc, name, S, bm):
-    """Four tasks per queue atomic: the same tiles (half tiles at the queues'
-    ends included, prefill_skew) as one task per atomic, so the output is the
-    same bit for bit, and the queue check passes."""
+def test_batched_claims_same_output(orc, name, S, bm, split):
+    """Four tasks per queue atomic: the same tiles (with MOE_SPLIT_TAIL, half
+    tiles at the queues' ends included) as one task per atomic, so the output
+    is the same bit for bit, and the queue check passes."""
     wl = wk.WORKLOADS[name].with_tokens(S)
     li = wk.draw_layer(wl)
     L = DeviceLayer(wl, li)
@@ -42,7 +43,7 @@ def test_batched_claims_same_output(orc, name, S, bm):
     outs = []
     for flags in (0, moe.MOE_SCHED_BATCH):
         buf = buffers(wl, bm, out_f32=True)
-        buf.shape.flags |= flags
+        buf.shape.flags |= flags | split
         buf.forward_ws.fill_(0xFF)
         O, st = _run(L, buf, G)
         assert st == 0, f"status {st} with flags {flags}"
@@ -79,3 +80,31 @@ def test_queue_check_reports_lost_tasks(orc, name, S, bm):
                         Ws_gate=li.Ws_gate, Ws_down=li.Ws_down, logits=G)
         err, tol = parity(wl, again, ref["O"])
         assert err <= tol
+
+
+SPLIT_CASES = [("prefill_skew", 300, 128), ("prefill_skew", 700, 256), ("prefill_bal", 700, 128),
+               ("prefill_bal", 3000, 256), ("dsv3", 100, 256), ("decode", 64, 16),
+               ("tiny_fp32", 64, 16), ("prefill_bal_mxfp8", 300, 128)]
+
+
+@pytest.mark.parametrize("name,S,bm", SPLIT_CASES)
+def test_split_tail_same_output(orc, name, S, bm):
+    """Long-tail splitting (MOE_SPLIT_TAIL): each up/gate queue's last tasks
+    run as two row halves on the half-row core, which adds the same K chunks
+    in the same order: the output equals the whole-tile run's bit for bit, and
+    the queue check (which counts the half parts) passes. Where the flag has
+    no effect (16-row tiles, fp32, MXFP8) the outputs are equal too."""
+    wl = wk.WORKLOADS[name].with_tokens(S)
+    li = wk.draw_layer(wl)
+    L = DeviceLayer(wl, li)
+    G = orc.gate_logits(li.A, li.Wr, li.bias)
+    outs = []
+    for flags in (0, moe.MOE_SPLIT_TAIL):
+        buf = buffers(wl, bm, out_f32=True)
+        buf.shape.flags |= flags
+        buf.forward_ws.fill_(0xFF)
+        O, st = _run(L, buf, G)
+        assert st == 0, f"status {st} with flags {flags}"
+        outs.append(O)
+    assert np.all(np.isfinite(outs[1]))
+    assert np.array_equal(outs[0], outs[1])
