@@ -857,9 +857,18 @@ struct DownTile<T, BM, BS, true, true> {
   using type = TileGemmDirect<BM, 2, 8, stage_k<BM>(), 144 * 1024, BS, true, mfma_shape<BM>()>;
 };
 
-template <typename T, int BM, int BN, bool BS, bool FC = false>
+// LEAN: the instance for the default options (task queues, slot combine),
+// with the quota scheduler's claims and the atomic epilogue compiled out
+// (measured: down -1 to -2.5% at prefill sizes; the code the kernel carries
+// changes how its main loop is built).
+template <typename T, int BM, int BN, bool BS, bool FC = false, bool LEAN = false>
 __global__ __launch_bounds__((tile_threads<T, BM, kDownStrips, 1>()), 1) void down_kernel(
-    ForwardParams p) {
+    ForwardParams pk) {
+  ForwardParams p = pk;
+  if constexpr (LEAN) {
+    p.sched_quota = 0;
+    p.atomic_combine = 0;
+  }
   static_assert(kDownStrips == 2, "two strips per down task");
   using TG = typename DownTile<T, BM, BS, FC>::type;
   extern __shared__ __align__(16) char smem[];
@@ -1293,19 +1302,26 @@ static hipError_t launch_down_t(const ForwardParams& p, hipStream_t st) {
     return launch_persistent(down_kernel<T, BM, BN, false, true>, lds_bytes<T, BM, kDownStrips, 1>(),
                              tile_threads<T, BM, kDownStrips, 1>(), p, st);
   }
+  const bool lean = !p.sched_quota && !p.atomic_combine;
+  constexpr int BN = down_bn<BM>();
   if constexpr (sizeof(T) == 2) {
     const bool bs = weights_streamed(p, BM);
     if (down_stream_ok<BM>(p))
       return bs ? launch_persistent(down_stream_kernel<BM, true>, 0, 512, p, st)
                 : launch_persistent(down_stream_kernel<BM, false>, 0, 512, p, st);
     if (bs)
-      return launch_persistent(down_kernel<T, BM, down_bn<BM>(), true>,
-                               lds_bytes<T, BM, kDownStrips, 1>(),
-                               tile_threads<T, BM, kDownStrips, 1>(), p, st);
+      return lean ? launch_persistent(down_kernel<T, BM, BN, true, false, true>,
+                                      lds_bytes<T, BM, kDownStrips, 1>(),
+                                      tile_threads<T, BM, kDownStrips, 1>(), p, st)
+                  : launch_persistent(down_kernel<T, BM, BN, true>,
+                                      lds_bytes<T, BM, kDownStrips, 1>(),
+                                      tile_threads<T, BM, kDownStrips, 1>(), p, st);
   }
-  constexpr int BN = down_bn<BM>();
-  return launch_persistent(down_kernel<T, BM, BN, false>, lds_bytes<T, BM, kDownStrips, 1>(),
-                           tile_threads<T, BM, kDownStrips, 1>(), p, st);
+  return lean ? launch_persistent(down_kernel<T, BM, BN, false, false, true>,
+                                  lds_bytes<T, BM, kDownStrips, 1>(),
+                                  tile_threads<T, BM, kDownStrips, 1>(), p, st)
+              : launch_persistent(down_kernel<T, BM, BN, false>, lds_bytes<T, BM, kDownStrips, 1>(),
+                                  tile_threads<T, BM, kDownStrips, 1>(), p, st);
 }
 
 template <typename T>
